@@ -1,0 +1,205 @@
+/*
+ * paged_attn.h - C ABI of the gfx950 (MI355X) paged grouped-query attention
+ * library (libpaged_attn.so).
+ *
+ * Three operations, each defined by scaled dot-product attention over a
+ * paged K/V cache with FP32 accumulation and FP32 softmax state:
+ *
+ *   attn_paged_decode        decode / speculative verify: 1-8 query rows per
+ *                            sequence, K/V split into partitions and merged
+ *                            with a log-sum-exp merge (Geramy/LSE releases,
+ *                            v0.4.19 "Long-context split attention" and v0.4.20
+ *                            "automatic split attention"; K/V reads shared by
+ *                            the query heads and rows of a group, v0.4.21
+ *                            "joint decode attention").
+ *   attn_prefill             causal prefill with optional per-head attention
+ *                            sinks (TokenSpeed-Kernel-AMD page, "Attention":
+ *                            full causal attention with attention sinks).
+ *   attn_prefill_blocksparse causal prefill restricted to the key blocks a
+ *                            caller-supplied block mask keeps (Geramy/LSE
+ *                            README, FlashPrefill V2 paragraph: attention runs
+ *                            on selected blocks only; the selection rule is
+ *                            the caller's).
+ *
+ * Semantics (identical for all three).  For sequence b with L = seq_lens[b]
+ * keys and n = q_rows query rows, row i sits at absolute position
+ * p = L - n + i and attends to keys j with j <= p (and, for the block-sparse
+ * call, mask[b][mh][p / mask_block][j / mask_block] != 0).  Query head h reads
+ * KV head h / (num_q_heads / num_kv_heads).  With s_j = softmax_scale * q.k_j
+ * (k_j, v_j dequantised: value * k_scale, value * v_scale):
+ *     m = max(max_j s_j, sink_h),  Z = sum_j e^{s_j - m} + e^{sink_h - m},
+ *     o = sum_j e^{s_j - m} v_j / Z,  lse = m + ln Z.
+ * No sink means sink_h = -inf.  A row with no allowed key gets o = 0 and
+ * lse = sink_h (-inf without sinks).
+ *
+ * Memory layout (all device memory, element strides):
+ *   K pool   tile (page, kv_head) at k_pages + page*k_stride_page +
+ *            head*k_stride_head, laid out [page_size][head_dim] (token-major).
+ *   V pool   tile at v_pages + page*v_stride_page + head*v_stride_head, laid
+ *            out [head_dim][page_size] (token-minor), so the tokens of one
+ *            value component are contiguous.
+ *   page_table  int32 [batch][page_table_stride]; entry k of row b is the page
+ *            holding tokens 16k..16k+15 of sequence b.  Entries at or past
+ *            ceil(seq_lens[b]/16) are never read.
+ *   seq_lens int32 [batch]; keys in the cache for each sequence, including the
+ *            rows of this call.  Values above page_table_stride*page_size are
+ *            clamped to it.
+ *   Q, O     [batch][q_rows][num_q_heads][head_dim] through the given strides,
+ *            head_dim contiguous.
+ *   lse      optional float [batch][num_q_heads][q_rows] (natural log).
+ *   block_mask  uint8 [batch][mask_heads][mask_q_blocks][mask_k_blocks];
+ *            entries outside that extent count as 0.
+ *
+ * Ownership and threading: the caller owns every buffer.  The library never
+ * allocates or frees device memory and never synchronises: each call only
+ * enqueues work on `hip_stream` (NULL = the null stream) and returns; buffers
+ * must stay valid until the stream reaches that point.  A decode workspace
+ * must not be shared by calls in flight at the same time.  An attn_ctx is
+ * immutable after attn_open and may be used from several host threads.
+ *
+ * Errors: every call returns an attn_status.  On failure, if `err` is not
+ * NULL, *err receives a message the caller releases with attn_free().
+ *   ATTN_ERR_INVALID_ARGUMENT  null pointers, inconsistent shapes or strides,
+ *                              num_q_heads % num_kv_heads != 0, misaligned
+ *                              base pointers or strides (16 bytes), q_rows
+ *                              outside [1, 8] for decode, a block mask passed
+ *                              to a call that does not take one (or missing
+ *                              where required), bad mask geometry.
+ *   ATTN_ERR_UNSUPPORTED       a well-formed request this build does not
+ *                              implement (head_dim not 64 or 128, page_size
+ *                              not 16, unsupported dtype combination).
+ *   ATTN_ERR_WORKSPACE_TOO_SMALL  decode workspace below the queried size.
+ *   ATTN_ERR_DEVICE            no usable gfx950 device, or a HIP error while
+ *                              enqueuing (its text in *err).
+ * Device-side data (page ids, seq_lens, mask bytes) is trusted: page ids must
+ * lie in [0, num_pages).
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARGUMENT = 1,
+  ATTN_ERR_UNSUPPORTED = 2,
+  ATTN_ERR_WORKSPACE_TOO_SMALL = 3,
+  ATTN_ERR_DEVICE = 4
+} attn_status;
+
+/* Storage / compute types.  FP8 is OCP e4m3fn (bias 7, max 448, no inf). */
+typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2, ATTN_FP8_E4M3 = 3 } attn_dtype;
+
+typedef struct attn_ctx attn_ctx;
+
+/* Paged K/V cache of one layer. */
+typedef struct {
+  const void *k_pages;          /* K tiles [page_size][head_dim] */
+  const void *v_pages;          /* V tiles [head_dim][page_size] */
+  int32_t dtype;                /* attn_dtype of K and V */
+  int32_t num_pages;            /* pages in the pool */
+  int32_t page_size;            /* tokens per page; must be 16 */
+  int32_t num_kv_heads;
+  int32_t head_dim;             /* 64 or 128 */
+  int32_t pad0;
+  int64_t k_stride_page, k_stride_head;   /* elements */
+  int64_t v_stride_page, v_stride_head;   /* elements */
+  float k_scale, v_scale;       /* dequantisation multipliers (1.0 unless FP8) */
+  const int32_t *page_table;    /* [batch][page_table_stride] */
+  int32_t page_table_stride;
+  int32_t pad1;
+  const int32_t *seq_lens;      /* [batch] */
+} attn_kv;
+
+/* Queries and outputs. */
+typedef struct {
+  const void *q;
+  int32_t q_dtype;              /* F32, F16 or BF16 (see each call) */
+  int32_t batch;
+  int32_t q_rows;               /* decode: 1..8 rows; prefill: rows per sequence */
+  int32_t num_q_heads;
+  int64_t q_stride_b, q_stride_row, q_stride_head;   /* elements */
+  void *o;
+  int32_t o_dtype;              /* F32, F16 or BF16 */
+  int32_t pad0;
+  int64_t o_stride_b, o_stride_row, o_stride_head;   /* elements */
+  float *lse;                   /* nullable [batch][num_q_heads][q_rows] */
+} attn_io;
+
+typedef struct {
+  float softmax_scale;          /* <= 0 selects 1/sqrt(head_dim) */
+  int32_t num_splits;           /* decode: 0 = plan from capacity and LDS; > 0 forces it */
+  const float *sinks;           /* nullable [num_q_heads], finite or -inf */
+  const uint8_t *block_mask;    /* attn_prefill_blocksparse only, else NULL */
+  int32_t mask_heads;           /* 1 (shared) or num_kv_heads */
+  int32_t mask_block;           /* tokens per mask block: a multiple of 64 */
+  int32_t mask_q_blocks, mask_k_blocks;
+} attn_opts;
+
+/* ABI version of the loaded library (ATTN_ABI_VERSION). */
+int attn_abi_version(void);
+
+/* Open device `hip_device` (must be gfx950).  Caches CU count and LDS size. */
+attn_status attn_open(int hip_device, attn_ctx **ctx, char **err);
+
+/* A context for planning and argument checking only, describing a device
+ * with `num_cus` compute units: every call validates and plans as usual and
+ * then returns ATTN_ERR_DEVICE instead of enqueuing work. */
+attn_status attn_open_host_only(int num_cus, attn_ctx **ctx, char **err);
+
+void attn_close(attn_ctx *ctx);
+
+/* Release a string returned through an `err` argument. */
+void attn_free(void *p);
+
+/* Decode plan: number of KV partitions, tokens per partition and the
+ * workspace bytes attn_paged_decode needs for these arguments.  The
+ * partition count follows the page table's capacity (page_table_stride *
+ * page_size), the rows that share each K/V read and the device's CU count
+ * (Geramy/LSE releases, v0.4.20: partitions from K/V table capacity, with an
+ * LDS check). */
+attn_status attn_paged_decode_plan(const attn_ctx *ctx, const attn_io *io, const attn_kv *kv,
+                                   const attn_opts *opts, int32_t *num_splits,
+                                   int32_t *tokens_per_split, size_t *workspace_bytes,
+                                   char **err);
+
+/* Workspace bytes for attn_paged_decode (0 if the arguments are invalid). */
+size_t attn_paged_decode_workspace_bytes(const attn_ctx *ctx, const attn_io *io,
+                                         const attn_kv *kv, const attn_opts *opts);
+
+/* Decode / verify: q_rows in [1, 8].  Q dtype: F32/F16/BF16 with F32 K/V,
+ * equal to the K/V dtype for F16/BF16 K/V, F16 or BF16 with FP8 K/V.
+ * `workspace` is device memory of at least the queried size (16-byte
+ * aligned).  block_mask must be NULL. */
+attn_status attn_paged_decode(attn_ctx *ctx, const attn_io *io, const attn_kv *kv,
+                              const attn_opts *opts, void *workspace, size_t workspace_bytes,
+                              void *hip_stream, char **err);
+
+/* Causal prefill (q_rows rows at the end of each sequence, q_rows <= seq_len
+ * expected).  K/V F16, BF16 or FP8; Q F16/BF16 (equal to K/V for 16-bit K/V).
+ * block_mask must be NULL. */
+attn_status attn_prefill(attn_ctx *ctx, const attn_io *io, const attn_kv *kv,
+                         const attn_opts *opts, void *hip_stream, char **err);
+
+/* Block-sparse causal prefill: as attn_prefill, with block_mask required. */
+attn_status attn_prefill_blocksparse(attn_ctx *ctx, const attn_io *io, const attn_kv *kv,
+                                     const attn_opts *opts, void *hip_stream, char **err);
+
+/* Test hook: gather sequence b's K and V through the page table and
+ * dequantise them exactly as the attention kernels do, into FP32 arrays
+ * k_out, v_out of [num_kv_heads][seq_len][head_dim] (device memory). */
+attn_status attn_debug_gather_kv(attn_ctx *ctx, const attn_kv *kv, int32_t b, int32_t seq_len,
+                                 float *k_out, float *v_out, void *hip_stream, char **err);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

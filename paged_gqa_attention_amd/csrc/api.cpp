@@ -1,0 +1,398 @@
+// C ABI of the paged attention library: argument validation, split planning,
+// workspace sizing and kernel launches.  The library never allocates device
+// memory and never synchronises; every call only enqueues on the given stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/paged_attn.h"
+#include "attn_internal.h"
+
+struct attn_ctx {
+  int device;
+  int num_cus;
+  size_t lds_per_block;
+  bool host_only;
+  char arch[64];
+};
+
+namespace {
+
+using pa::DecodeArgs;
+using pa::PrefillArgs;
+
+constexpr int kPage = 16;
+
+int elt_bytes(int dt) {
+  switch (dt) {
+    case ATTN_F32: return 4;
+    case ATTN_F16: return 2;
+    case ATTN_BF16: return 2;
+    case ATTN_FP8_E4M3: return 1;
+  }
+  return 0;
+}
+
+attn_status fail(char **err, attn_status st, const char *fmt, ...) {
+  if (err) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    *err = strdup(buf);
+  }
+  return st;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+// ---- shared validation --------------------------------------------------------
+
+attn_status check_kv(const attn_kv *kv, char **err) {
+  if (!kv) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "kv is NULL");
+  if (!kv->k_pages || !kv->v_pages) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "K/V pages are NULL");
+  if (!kv->page_table || !kv->seq_lens)
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "page_table / seq_lens is NULL");
+  if (elt_bytes(kv->dtype) == 0) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "bad K/V dtype %d", kv->dtype);
+  if (kv->num_pages < 1 || kv->num_kv_heads < 1 || kv->page_table_stride < 1)
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "num_pages, num_kv_heads and page_table_stride must be >= 1");
+  if (kv->head_dim < 1 || kv->page_size < 1)
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "head_dim and page_size must be >= 1");
+  if (kv->page_size != kPage) return fail(err, ATTN_ERR_UNSUPPORTED, "page_size %d (only 16)", kv->page_size);
+  if (kv->head_dim != 64 && kv->head_dim != 128)
+    return fail(err, ATTN_ERR_UNSUPPORTED, "head_dim %d (only 64 or 128)", kv->head_dim);
+  if (!aligned16(kv->k_pages) || !aligned16(kv->v_pages))
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "K/V pages must be 16-byte aligned");
+  const int64_t tile = (int64_t)kPage * kv->head_dim;
+  const int eb = elt_bytes(kv->dtype);
+  const int64_t s[4] = {kv->k_stride_page, kv->k_stride_head, kv->v_stride_page, kv->v_stride_head};
+  for (int i = 0; i < 4; ++i) {
+    if (s[i] < tile) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "K/V strides must be >= one page tile (%lld elements)", (long long)tile);
+    if ((s[i] * eb) % 16) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "K/V strides must be multiples of 16 bytes");
+  }
+  if (!(kv->k_scale > 0.f) || !(kv->v_scale > 0.f) || !std::isfinite(kv->k_scale) || !std::isfinite(kv->v_scale))
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "k_scale and v_scale must be finite and > 0");
+  return ATTN_OK;
+}
+
+attn_status check_io(const attn_io *io, const attn_kv *kv, char **err) {
+  if (!io) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "io is NULL");
+  if (!io->q || !io->o) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "q / o is NULL");
+  if (io->batch < 1 || io->q_rows < 1 || io->num_q_heads < 1)
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "batch, q_rows and num_q_heads must be >= 1");
+  if (io->num_q_heads % kv->num_kv_heads)
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "num_q_heads %d is not a multiple of num_kv_heads %d", io->num_q_heads, kv->num_kv_heads);
+  if (io->q_dtype != ATTN_F32 && io->q_dtype != ATTN_F16 && io->q_dtype != ATTN_BF16)
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "q_dtype must be F32, F16 or BF16");
+  if (io->o_dtype != ATTN_F32 && io->o_dtype != ATTN_F16 && io->o_dtype != ATTN_BF16)
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "o_dtype must be F32, F16 or BF16");
+  if (!aligned16(io->q) || !aligned16(io->o)) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "q and o must be 16-byte aligned");
+  if (io->lse && (reinterpret_cast<uintptr_t>(io->lse) & 3u)) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "lse must be 4-byte aligned");
+  const int qb = elt_bytes(io->q_dtype), ob = elt_bytes(io->o_dtype);
+  const int64_t qs[3] = {io->q_stride_b, io->q_stride_row, io->q_stride_head};
+  const int64_t os[3] = {io->o_stride_b, io->o_stride_row, io->o_stride_head};
+  for (int i = 0; i < 3; ++i) {
+    if (qs[i] < 0 || os[i] < 0) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "negative q/o stride");
+    if ((qs[i] * qb) % 16 || (os[i] * ob) % 16) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "q/o strides must be multiples of 16 bytes");
+  }
+  if (io->q_stride_head < kv->head_dim || io->o_stride_head < kv->head_dim)
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "q/o head stride below head_dim");
+  return ATTN_OK;
+}
+
+attn_status check_ctx(const attn_ctx *ctx, char **err) {
+  if (!ctx) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "ctx is NULL");
+  return ATTN_OK;
+}
+
+// ---- decode planning ------------------------------------------------------------
+
+struct DecodePlan {
+  bool mfma;
+  int rows, rb, row_blocks, P, T;
+  size_t ws_bytes, ws_o_bytes;
+};
+
+constexpr int kTGran = 128;   // partition granularity (tokens)
+
+attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *kv, const attn_opts *opts,
+                        DecodePlan *pl, char **err) {
+  attn_status st;
+  if ((st = check_ctx(ctx, err)) != ATTN_OK) return st;
+  if ((st = check_kv(kv, err)) != ATTN_OK) return st;
+  if ((st = check_io(io, kv, err)) != ATTN_OK) return st;
+  if (!opts) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "opts is NULL");
+  if (opts->block_mask) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "attn_paged_decode takes no block mask");
+  if (opts->num_splits < 0) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "num_splits must be >= 0");
+  if (io->q_rows > 8) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "decode q_rows %d outside [1, 8]", io->q_rows);
+  const int G = io->num_q_heads / kv->num_kv_heads;
+  const int rows = G * io->q_rows;
+  const int D = kv->head_dim;
+  pl->rows = rows;
+  pl->mfma = kv->dtype != ATTN_F32 && rows > 8;
+  if (pl->mfma) {
+    if (!pa::decode_mfma_supported(kv->dtype, io->q_dtype, D, rows))
+      return fail(err, ATTN_ERR_UNSUPPORTED, "decode: K/V dtype %d with Q dtype %d and %d rows per KV head is not supported", kv->dtype, io->q_dtype, rows);
+    pl->rb = rows;
+    pl->row_blocks = 1;
+  } else {
+    if (!pa::decode_valu_supported(kv->dtype, io->q_dtype, D))
+      return fail(err, ATTN_ERR_UNSUPPORTED, "decode: K/V dtype %d with Q dtype %d is not supported", kv->dtype, io->q_dtype);
+    pl->rb = rows <= 4 ? 4 : 8;
+    pl->row_blocks = (int)ceil_div(rows, pl->rb);
+  }
+  // LDS the partial kernel needs for its rows (merge buffer + softmax state)
+  const size_t lds = pl->mfma ? (size_t)round_up(rows, 16) * (D + 4) * 4 + 2 * 4 * 64 * 4
+                              : (size_t)pl->rb * D * 4 + 4 * 16 * pl->rb * 4 + 3 * 4 * pl->rb * 4;
+  if (lds > ctx->lds_per_block)
+    return fail(err, ATTN_ERR_UNSUPPORTED, "decode needs %zu bytes of LDS, the device has %zu", lds, ctx->lds_per_block);
+
+  const int64_t cap = (int64_t)kv->page_table_stride * kPage;
+  const int rows_per_wg = pl->mfma ? rows : pl->rb;
+  const int64_t tmin = round_up(std::max<int64_t>(256, 64 * (int64_t)rows_per_wg), kTGran);
+  int64_t T;
+  if (opts->num_splits > 0) {
+    T = round_up(ceil_div(cap, opts->num_splits), kTGran);
+  } else {
+    const int64_t groups = (int64_t)io->batch * kv->num_kv_heads * pl->row_blocks;
+    const int64_t target = std::max<int64_t>(1, ceil_div(4 * (int64_t)ctx->num_cus, groups));
+    T = std::max(tmin, round_up(ceil_div(cap, target), kTGran));
+  }
+  const int64_t P = ceil_div(cap, T);
+  if (P > 65535) return fail(err, ATTN_ERR_UNSUPPORTED, "too many partitions (%lld)", (long long)P);
+  pl->P = (int)P;
+  pl->T = (int)T;
+  const int64_t slots = (int64_t)io->batch * kv->num_kv_heads * rows * P;
+  pl->ws_o_bytes = (size_t)round_up(slots * D * 4, 256);
+  pl->ws_bytes = pl->ws_o_bytes + (size_t)round_up(slots * 2 * 4, 256);
+  return ATTN_OK;
+}
+
+float score_scale(const attn_opts *opts, const attn_kv *kv) {
+  const float s = opts->softmax_scale > 0.f ? opts->softmax_scale : 1.0f / std::sqrt((float)kv->head_dim);
+  return s * kv->k_scale * 1.4426950408889634f;
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) { ok = false; return; }
+    if (prev != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+  }
+  ~DeviceGuard() {
+    int cur;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+attn_status launched(hipError_t e, char **err, const char *what) {
+  if (e != hipSuccess) return fail(err, ATTN_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+// ---- prefill ------------------------------------------------------------------------
+
+attn_status prefill_common(attn_ctx *ctx, const attn_io *io, const attn_kv *kv, const attn_opts *opts,
+                           bool sparse, void *stream, char **err) {
+  attn_status st;
+  if ((st = check_ctx(ctx, err)) != ATTN_OK) return st;
+  if ((st = check_kv(kv, err)) != ATTN_OK) return st;
+  if ((st = check_io(io, kv, err)) != ATTN_OK) return st;
+  if (!opts) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "opts is NULL");
+  if (!sparse && opts->block_mask) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "attn_prefill takes no block mask (use attn_prefill_blocksparse)");
+  if (sparse) {
+    if (!opts->block_mask) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "attn_prefill_blocksparse needs a block mask");
+    if (opts->mask_block < 64 || opts->mask_block % 64)
+      return fail(err, ATTN_ERR_INVALID_ARGUMENT, "mask_block %d must be a positive multiple of 64", opts->mask_block);
+    if (opts->mask_heads != 1 && opts->mask_heads != kv->num_kv_heads)
+      return fail(err, ATTN_ERR_INVALID_ARGUMENT, "mask_heads must be 1 or num_kv_heads");
+    if (opts->mask_q_blocks < 1 || opts->mask_k_blocks < 1)
+      return fail(err, ATTN_ERR_INVALID_ARGUMENT, "mask_q_blocks and mask_k_blocks must be >= 1");
+  }
+  const int G = io->num_q_heads / kv->num_kv_heads;
+  if (!pa::prefill_supported(kv->dtype, io->q_dtype, kv->head_dim))
+    return fail(err, ATTN_ERR_UNSUPPORTED, "prefill: K/V dtype %d with Q dtype %d is not supported", kv->dtype, io->q_dtype);
+  PrefillArgs a{};
+  a.q = io->q;
+  a.q_sb = io->q_stride_b; a.q_sr = io->q_stride_row; a.q_sh = io->q_stride_head;
+  a.k = kv->k_pages; a.v = kv->v_pages;
+  a.k_sp = kv->k_stride_page; a.k_sh = kv->k_stride_head;
+  a.v_sp = kv->v_stride_page; a.v_sh = kv->v_stride_head;
+  a.page_table = kv->page_table;
+  a.pt_stride = kv->page_table_stride;
+  a.capacity = (int32_t)std::min<int64_t>((int64_t)kv->page_table_stride * kPage, INT32_MAX);
+  a.lens = kv->seq_lens;
+  a.B = io->batch; a.n_q = io->q_rows; a.Hq = io->num_q_heads; a.Hkv = kv->num_kv_heads;
+  a.G = G; a.D = kv->head_dim;
+  a.kv_dtype = kv->dtype; a.q_dtype = io->q_dtype; a.o_dtype = io->o_dtype;
+  a.score_scale = score_scale(opts, kv);
+  a.v_scale = kv->v_scale;
+  a.sinks = opts->sinks;
+  a.o = io->o;
+  a.o_sb = io->o_stride_b; a.o_sr = io->o_stride_row; a.o_sh = io->o_stride_head;
+  a.lse = io->lse;
+  a.mask = sparse ? opts->block_mask : nullptr;
+  a.mask_heads = opts->mask_heads; a.mask_block = opts->mask_block;
+  a.mask_nqb = opts->mask_q_blocks; a.mask_nkb = opts->mask_k_blocks;
+  a.q_tiles = (int)ceil_div(io->q_rows, 128);
+  a.heads_per_wg = (G % 2 == 0) ? 2 : 1;
+  const int64_t ntask = (int64_t)a.q_tiles * a.B * a.Hkv;
+  const int64_t nwg = round_up(ntask, 8) * (G / a.heads_per_wg);
+  if (nwg > INT32_MAX) return fail(err, ATTN_ERR_UNSUPPORTED, "prefill grid too large");
+  a.num_wg = (int)nwg;
+  if (ctx->host_only) return fail(err, ATTN_ERR_DEVICE, "host-only context: nothing enqueued");
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return fail(err, ATTN_ERR_DEVICE, "cannot select device %d", ctx->device);
+  return launched(pa::launch_prefill(a, (hipStream_t)stream), err, "prefill launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+void attn_free(void *p) { free(p); }
+
+attn_status attn_open(int hip_device, attn_ctx **ctx, char **err) {
+  if (!ctx) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "ctx is NULL");
+  *ctx = nullptr;
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess || n == 0) return fail(err, ATTN_ERR_DEVICE, "no HIP device visible (%s)", hipGetErrorString(e));
+  if (hip_device < 0 || hip_device >= n) return fail(err, ATTN_ERR_DEVICE, "device %d out of range (%d visible)", hip_device, n);
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, hip_device);
+  if (e != hipSuccess) return fail(err, ATTN_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(err, ATTN_ERR_DEVICE, "device %d is %s; this library is built for gfx950", hip_device, prop.gcnArchName);
+  attn_ctx *c = (attn_ctx *)calloc(1, sizeof(attn_ctx));
+  if (!c) return fail(err, ATTN_ERR_DEVICE, "out of host memory");
+  c->device = hip_device;
+  c->num_cus = prop.multiProcessorCount;
+  c->lds_per_block = prop.sharedMemPerBlock;
+  c->host_only = false;
+  snprintf(c->arch, sizeof c->arch, "%s", prop.gcnArchName);
+  *ctx = c;
+  return ATTN_OK;
+}
+
+attn_status attn_open_host_only(int num_cus, attn_ctx **ctx, char **err) {
+  if (!ctx) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "ctx is NULL");
+  *ctx = nullptr;
+  if (num_cus < 1) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "num_cus must be >= 1");
+  attn_ctx *c = (attn_ctx *)calloc(1, sizeof(attn_ctx));
+  if (!c) return fail(err, ATTN_ERR_DEVICE, "out of host memory");
+  c->device = -1;
+  c->num_cus = num_cus;
+  c->lds_per_block = 160 * 1024;
+  c->host_only = true;
+  snprintf(c->arch, sizeof c->arch, "gfx950 (host-only)");
+  *ctx = c;
+  return ATTN_OK;
+}
+
+void attn_close(attn_ctx *ctx) { free(ctx); }
+
+attn_status attn_paged_decode_plan(const attn_ctx *ctx, const attn_io *io, const attn_kv *kv,
+                                   const attn_opts *opts, int32_t *num_splits,
+                                   int32_t *tokens_per_split, size_t *workspace_bytes, char **err) {
+  DecodePlan pl;
+  attn_status st = plan_decode(ctx, io, kv, opts, &pl, err);
+  if (st != ATTN_OK) return st;
+  if (num_splits) *num_splits = pl.P;
+  if (tokens_per_split) *tokens_per_split = pl.T;
+  if (workspace_bytes) *workspace_bytes = pl.ws_bytes;
+  return ATTN_OK;
+}
+
+size_t attn_paged_decode_workspace_bytes(const attn_ctx *ctx, const attn_io *io, const attn_kv *kv,
+                                         const attn_opts *opts) {
+  DecodePlan pl;
+  if (plan_decode(ctx, io, kv, opts, &pl, nullptr) != ATTN_OK) return 0;
+  return pl.ws_bytes;
+}
+
+attn_status attn_paged_decode(attn_ctx *ctx, const attn_io *io, const attn_kv *kv, const attn_opts *opts,
+                              void *workspace, size_t workspace_bytes, void *hip_stream, char **err) {
+  DecodePlan pl;
+  attn_status st = plan_decode(ctx, io, kv, opts, &pl, err);
+  if (st != ATTN_OK) return st;
+  if (!workspace) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  if (workspace_bytes < pl.ws_bytes)
+    return fail(err, ATTN_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, pl.ws_bytes);
+  DecodeArgs a{};
+  a.q = io->q;
+  a.q_sb = io->q_stride_b; a.q_sr = io->q_stride_row; a.q_sh = io->q_stride_head;
+  a.k = kv->k_pages; a.v = kv->v_pages;
+  a.k_sp = kv->k_stride_page; a.k_sh = kv->k_stride_head;
+  a.v_sp = kv->v_stride_page; a.v_sh = kv->v_stride_head;
+  a.page_table = kv->page_table;
+  a.pt_stride = kv->page_table_stride;
+  a.capacity = (int32_t)std::min<int64_t>((int64_t)kv->page_table_stride * kPage, INT32_MAX);
+  a.lens = kv->seq_lens;
+  a.B = io->batch; a.R = io->q_rows; a.Hq = io->num_q_heads; a.Hkv = kv->num_kv_heads;
+  a.G = io->num_q_heads / kv->num_kv_heads; a.D = kv->head_dim;
+  a.rows = pl.rows;
+  a.kv_dtype = kv->dtype; a.q_dtype = io->q_dtype; a.o_dtype = io->o_dtype;
+  a.score_scale = score_scale(opts, kv);
+  a.v_scale = kv->v_scale;
+  a.sinks = opts->sinks;
+  a.o = io->o;
+  a.o_sb = io->o_stride_b; a.o_sr = io->o_stride_row; a.o_sh = io->o_stride_head;
+  a.lse = io->lse;
+  a.P = pl.P; a.T = pl.T;
+  a.row_blocks = pl.row_blocks;
+  a.ws_o = reinterpret_cast<float *>(workspace);
+  a.ws_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + pl.ws_o_bytes);
+  if (ctx->host_only) return fail(err, ATTN_ERR_DEVICE, "host-only context: nothing enqueued");
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return fail(err, ATTN_ERR_DEVICE, "cannot select device %d", ctx->device);
+  hipStream_t s = (hipStream_t)hip_stream;
+  st = launched(pl.mfma ? pa::launch_decode_mfma(a, s) : pa::launch_decode_valu(a, s), err, "decode partial launch");
+  if (st != ATTN_OK) return st;
+  return launched(pa::launch_decode_merge(a, s), err, "decode merge launch");
+}
+
+attn_status attn_prefill(attn_ctx *ctx, const attn_io *io, const attn_kv *kv, const attn_opts *opts,
+                         void *hip_stream, char **err) {
+  return prefill_common(ctx, io, kv, opts, false, hip_stream, err);
+}
+
+attn_status attn_prefill_blocksparse(attn_ctx *ctx, const attn_io *io, const attn_kv *kv,
+                                     const attn_opts *opts, void *hip_stream, char **err) {
+  return prefill_common(ctx, io, kv, opts, true, hip_stream, err);
+}
+
+attn_status attn_debug_gather_kv(attn_ctx *ctx, const attn_kv *kv, int32_t b, int32_t seq_len,
+                                 float *k_out, float *v_out, void *hip_stream, char **err) {
+  attn_status st;
+  if ((st = check_ctx(ctx, err)) != ATTN_OK) return st;
+  if ((st = check_kv(kv, err)) != ATTN_OK) return st;
+  if (!k_out || !v_out) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "k_out / v_out is NULL");
+  if (b < 0 || seq_len < 0) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "negative b or seq_len");
+  if ((int64_t)seq_len > (int64_t)kv->page_table_stride * kPage)
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "seq_len beyond the page-table capacity");
+  if (ctx->host_only) return fail(err, ATTN_ERR_DEVICE, "host-only context: nothing enqueued");
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return fail(err, ATTN_ERR_DEVICE, "cannot select device %d", ctx->device);
+  return launched(pa::launch_debug_gather(kv->k_pages, kv->v_pages, kv->k_stride_page, kv->k_stride_head,
+                                          kv->v_stride_page, kv->v_stride_head, kv->dtype,
+                                          kv->num_kv_heads, kv->head_dim, kv->k_scale, kv->v_scale,
+                                          kv->page_table + (int64_t)b * kv->page_table_stride, seq_len,
+                                          k_out, v_out, (hipStream_t)hip_stream),
+                  err, "debug gather launch");
+}
+
+}  // extern "C"

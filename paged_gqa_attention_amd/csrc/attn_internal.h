@@ -1,0 +1,73 @@
+// Kernel argument blocks and launcher declarations (host <-> kernel files).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Everything a decode launch needs; all pointers are device pointers.
+struct DecodeArgs {
+  const void *q;
+  int64_t q_sb, q_sr, q_sh;
+  const void *k, *v;
+  int64_t k_sp, k_sh, v_sp, v_sh;
+  const int32_t *page_table;
+  int32_t pt_stride;
+  int32_t capacity;       // pt_stride * 16
+  const int32_t *lens;
+  int32_t B, R, Hq, Hkv, G, D;
+  int32_t rows;           // G * R rows share each K/V read
+  int32_t kv_dtype, q_dtype, o_dtype;
+  float score_scale;      // softmax_scale * k_scale * log2(e): scores in log2 units
+  float v_scale;
+  const float *sinks;     // nullable [Hq]
+  void *o;
+  int64_t o_sb, o_sr, o_sh;
+  float *lse;             // nullable [B][Hq][R]
+  int32_t P;              // partitions per sequence
+  int32_t T;              // tokens per partition (multiple of 128)
+  int32_t row_blocks;     // VALU path: ceil(rows / rows_per_block)
+  float *ws_o;            // [B][Hkv][rows][P][D]   unnormalised partial outputs
+  float *ws_ml;           // [B][Hkv][rows][P][2]   partial max (log2 units) and sum
+};
+
+struct PrefillArgs {
+  const void *q;
+  int64_t q_sb, q_sr, q_sh;
+  const void *k, *v;
+  int64_t k_sp, k_sh, v_sp, v_sh;
+  const int32_t *page_table;
+  int32_t pt_stride;
+  int32_t capacity;
+  const int32_t *lens;
+  int32_t B, n_q, Hq, Hkv, G, D;
+  int32_t kv_dtype, q_dtype, o_dtype;
+  float score_scale;      // softmax_scale * k_scale * log2(e)
+  float v_scale;
+  const float *sinks;
+  void *o;
+  int64_t o_sb, o_sr, o_sh;
+  float *lse;             // nullable [B][Hq][n_q]
+  const uint8_t *mask;    // nullable
+  int32_t mask_heads, mask_block, mask_nqb, mask_nkb;
+  int32_t q_tiles;        // ceil(n_q / 128)
+  int32_t heads_per_wg;   // 1 or 2 query heads of one group per workgroup
+  int32_t num_wg;         // total workgroups
+};
+
+hipError_t launch_decode_valu(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t s);
+bool decode_mfma_supported(int kv_dtype, int q_dtype, int D, int rows);
+bool decode_valu_supported(int kv_dtype, int q_dtype, int D);
+
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
+bool prefill_supported(int kv_dtype, int q_dtype, int D);
+
+hipError_t launch_debug_gather(const void *k, const void *v, int64_t k_sp, int64_t k_sh,
+                               int64_t v_sp, int64_t v_sh, int kv_dtype, int Hkv, int D,
+                               float k_scale, float v_scale, const int32_t *pt_row, int seq_len,
+                               float *k_out, float *v_out, hipStream_t s);
+
+}  // namespace pa

@@ -1,0 +1,152 @@
+// Device helpers shared by the gfx950 attention kernels: storage-dtype
+// conversions, cross-lane reductions and MFMA fragment types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3 };
+
+template <int DT> struct DtInfo;
+template <> struct DtInfo<DT_F32>  { static constexpr int bytes = 4; };
+template <> struct DtInfo<DT_F16>  { static constexpr int bytes = 2; };
+template <> struct DtInfo<DT_BF16> { static constexpr int bytes = 2; };
+template <> struct DtInfo<DT_FP8>  { static constexpr int bytes = 1; };
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kPage = 16;
+
+// ---- 16-byte global loads ------------------------------------------------------
+
+__device__ __forceinline__ u32x4 ld16(const void *p) {
+  return *reinterpret_cast<const u32x4 *>(p);
+}
+__device__ __forceinline__ u32x2 ld8(const void *p) {
+  return *reinterpret_cast<const u32x2 *>(p);
+}
+
+// ---- storage -> FP32 -------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2, w)[0];
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2, w)[1];
+}
+// two e4m3fn codes (bytes 0,1 if !HI, else 2,3 of w) to FP32, exact
+template <bool HI>
+__device__ __forceinline__ f32x2 fp8x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+}
+// two e4m3fn codes to a packed bf16 / f16 pair, exact (scale 1.0)
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+// to the 16-bit MFMA/dot operand type (f16 if F16 else bf16)
+template <bool F16, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_16(uint32_t w) {
+  if constexpr (F16) return fp8x2_to_f16x2<HI>(w);
+  else return fp8x2_to_bf16x2<HI>(w);
+}
+
+// element e of a 16-byte chunk of dtype DT, to FP32
+template <int DT>
+__device__ __forceinline__ float chunk_elem(const u32x4 &c, int e) {
+  if constexpr (DT == DT_F32) {
+    return __uint_as_float(c[e]);
+  } else if constexpr (DT == DT_BF16) {
+    uint32_t w = c[e >> 1];
+    return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+  } else if constexpr (DT == DT_F16) {
+    uint32_t w = c[e >> 1];
+    return (e & 1) ? f16_hi(w) : f16_lo(w);
+  } else {
+    uint32_t w = c[e >> 2];
+    f32x2 v = (e & 2) ? fp8x2_to_f32<true>(w) : fp8x2_to_f32<false>(w);
+    return (e & 1) ? v[1] : v[0];
+  }
+}
+
+// ---- FP32 -> storage ---------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 r;
+  r[0] = (__bf16)a;  // RNE
+  r[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  f16x2 r;
+  r[0] = (_Float16)a;
+  r[1] = (_Float16)b;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+template <int DT>
+__device__ __forceinline__ void store_out(void *base, int64_t idx, float v) {
+  if constexpr (DT == DT_F32) {
+    reinterpret_cast<float *>(base)[idx] = v;
+  } else if constexpr (DT == DT_BF16) {
+    reinterpret_cast<__bf16 *>(base)[idx] = (__bf16)v;
+  } else {
+    reinterpret_cast<_Float16 *>(base)[idx] = (_Float16)v;
+  }
+}
+
+// ---- 2-element dot products with FP32 accumulation --------------------------------
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c,
+                                false);
+}
+
+// ---- cross-lane -----------------------------------------------------------------------
+
+// DPP controls (GFX9 encoding)
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), CTRL, 0xF, 0xF,
+                                                     false));
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int m) {
+  int lane = __lane_id();
+  return __uint_as_float(__builtin_amdgcn_ds_bpermute((lane ^ m) << 2, __float_as_uint(v)));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  return __builtin_fmaxf(a, __builtin_fmaxf(b, c));
+}
+
+}  // namespace pa

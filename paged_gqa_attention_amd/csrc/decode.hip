@@ -1,0 +1,851 @@
+// Paged decode / speculative-verify attention for gfx950.
+//
+// One workgroup (4 waves) owns one KV partition of one (sequence, KV head)
+// and all the query rows that read that KV head: the G query heads of the
+// group times the R verify rows (Geramy/LSE releases, v0.4.21: K/V reads
+// shared across query heads and token rows).  Each wave walks pages of the
+// partition, keeps an online-softmax state per row in FP32, the four waves
+// are merged in LDS, and the partition's unnormalised output, running max and
+// sum go to the workspace.  A second kernel merges the partitions with a
+// log-sum-exp merge and adds the sink (Geramy/LSE releases, v0.4.19: one
+// partial family and one merge family; v0.4.20: partitions from K/V table
+// capacity, empty partitions skipped).
+//
+// Two partial kernels:
+//   decode_valu  FP32 VALU arithmetic, up to 8 rows per workgroup.  Used for
+//                single-row decode (HBM-bound, no matrix cores needed) and for
+//                FP32 K/V.  Four lanes share a token for Q.K; lanes own value
+//                components for P.V.
+//   decode_mfma  bf16/f16 MFMA 16x16x32 for 16..64 rows (multi-row verify):
+//                S^T = K.Q^T and O^T += V^T.P^T, so every lane's softmax row
+//                matches its accumulator row and V tiles (token-minor pages)
+//                load straight into MFMA operands.
+#include "attn_internal.h"
+#include "common.h"
+
+namespace pa {
+
+constexpr int kWaves = 4;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------------------------
+// Intra-workgroup merge of the four waves' softmax states, then the partial
+// write.  `m_w`/`l_w` are [kWaves][NR] in LDS, `acc` is [NR][D] in LDS.
+// Each wave calls add_wave() in turn (deterministic order).
+// ---------------------------------------------------------------------------------
+template <int NR>
+__device__ __forceinline__ void wave_scales(const float (*m_w)[NR], int wave, int r, float &M,
+                                            float &f) {
+  M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = __builtin_fmaxf(M, m_w[w][r]);
+  float Mu = (M == kNegInf) ? 0.f : M;
+  f = fast_exp2(m_w[wave][r] - Mu);
+}
+
+// ==================================================================================
+// VALU partial kernel
+// ==================================================================================
+//
+// Lane layout per page (16 tokens):
+//   K: lane = 4*n + qq handles token n; its 16-byte chunks are (4c + qq) of the
+//      token row, c < NL.  A quad holds one token; partial dot products are
+//      summed over the quad with DPP.
+//   V: the page's V tile [D][16] is read as 64-lane x 16-byte chunks
+//      g = 64c + lane; chunk g is value row g / CPR, tokens (g % CPR) * EPC + e.
+//   After the quad sum every lane knows all rows' scores of its token and
+//   handles the softmax of rows r = qq + 4k.
+template <int KVDT, int QDT, int D, int RB>
+__global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
+  constexpr int ELT = DtInfo<KVDT>::bytes;
+  constexpr int NL = D * ELT / 64;   // 16-byte chunks per lane per page, for K and for V
+  constexpr int EPC = 16 / ELT;      // elements per chunk
+  constexpr int CPR = ELT;           // V chunks per value row (16 tokens * ELT bytes)
+  constexpr int MR = RB / 4;         // softmax rows per lane
+  constexpr int QW = (KVDT == DT_F32) ? 4 : (KVDT == DT_FP8 ? 8 : 4);  // Q words per K chunk
+
+  __shared__ float p_lds[kWaves][16][RB];
+  __shared__ float alpha_lds[kWaves][RB];
+  __shared__ float m_w[kWaves][RB];
+  __shared__ float l_w[kWaves][RB];
+  __shared__ float acc_lds[RB][D];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform_int(threadIdx.x >> 6);
+  const int p = blockIdx.x, b = blockIdx.z;
+  const int kvh = blockIdx.y / a.row_blocks, rb = blockIdx.y % a.row_blocks;
+  const int L = min(a.lens[b], a.capacity);
+  const int t0 = p * a.T;
+  if (t0 >= L) return;  // empty partition: the merge never reads it
+  const int t1 = min(L, t0 + a.T);
+  const int n = lane >> 2, qq = lane & 3;
+  const int tg = lane % CPR;
+
+  // ---- query rows of this block ----
+  int pos[RB];
+  uint32_t q[RB][NL][QW];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const int rr = rb * RB + r;
+    const bool ok = rr < a.rows;
+    const int h = kvh * a.G + (ok ? rr / a.R : 0);
+    const int i = ok ? rr % a.R : 0;
+    pos[r] = ok ? L - a.R + i : -1;
+    const char *qrow = reinterpret_cast<const char *>(a.q) +
+                       ((int64_t)b * a.q_sb + (int64_t)i * a.q_sr + (int64_t)h * a.q_sh) *
+                           (QDT == DT_F32 ? 4 : 2);
+#pragma unroll
+    for (int c = 0; c < NL; ++c) {
+      const int e0 = (4 * c + qq) * EPC;  // first element of this lane's chunk
+      if constexpr (KVDT == DT_F32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v;
+          if constexpr (QDT == DT_F32) v = reinterpret_cast<const float *>(qrow)[e0 + e];
+          else if constexpr (QDT == DT_BF16)
+            v = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(qrow)[e0 + e] << 16);
+          else v = (float)reinterpret_cast<const _Float16 *>(qrow)[e0 + e];
+          q[r][c][e] = ok ? __float_as_uint(v) : 0u;
+        }
+      } else {
+        // 16-bit Q words, EPC elements
+#pragma unroll
+        for (int w = 0; w < QW; w += 4) {
+          u32x4 v = ld16(qrow + (e0 + 2 * w) * 2);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) q[r][c][w + e] = ok ? v[e] : 0u;
+        }
+      }
+    }
+  }
+  int pos_mine[MR];
+#pragma unroll
+  for (int k = 0; k < MR; ++k) {
+    int v = pos[4 * k];
+    v = qq == 1 ? pos[4 * k + 1] : v;
+    v = qq == 2 ? pos[4 * k + 2] : v;
+    v = qq == 3 ? pos[4 * k + 3] : v;
+    pos_mine[k] = v;
+  }
+
+  float m_run[MR], l_run[MR];
+  float o[RB][NL];
+#pragma unroll
+  for (int k = 0; k < MR; ++k) { m_run[k] = kNegInf; l_run[k] = 0.f; }
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int c = 0; c < NL; ++c) o[r][c] = 0.f;
+
+  const char *kbase = reinterpret_cast<const char *>(a.k) + (int64_t)kvh * a.k_sh * ELT;
+  const char *vbase = reinterpret_cast<const char *>(a.v) + (int64_t)kvh * a.v_sh * ELT;
+  const int32_t *pt = a.page_table + (int64_t)b * a.pt_stride;
+  const int pg_end = (t1 + 15) >> 4;
+  int pg = (t0 >> 4) + wave;
+
+  u32x4 kc[NL], vc[NL];
+  auto load_page = [&](int page_idx, u32x4 *kd, u32x4 *vd) {
+    const int64_t pid = pt[page_idx];
+    const char *kp = kbase + pid * a.k_sp * ELT + n * (D * ELT) + qq * 16;
+    const char *vp = vbase + pid * a.v_sp * ELT + lane * 16;
+#pragma unroll
+    for (int c = 0; c < NL; ++c) {
+      kd[c] = ld16(kp + c * 64);
+      vd[c] = ld16(vp + c * 1024);
+    }
+  };
+  if (pg < pg_end) load_page(pg, kc, vc);
+
+  for (; pg < pg_end; pg += kWaves) {
+    u32x4 kn[NL], vn[NL];
+    const int pgn = pg + kWaves;
+    if (pgn < pg_end) load_page(pgn, kn, vn);
+
+    // ---- scores of this lane's token for all rows ----
+    float s[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < NL; ++c) {
+        if constexpr (KVDT == DT_F32) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(__uint_as_float(q[r][c][e]),
+                                                           __uint_as_float(kc[c][e]), acc);
+        } else if constexpr (KVDT == DT_BF16) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc = dot2_bf16(q[r][c][e], kc[c][e], acc);
+        } else if constexpr (KVDT == DT_F16) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc = dot2_f16(q[r][c][e], kc[c][e], acc);
+        } else {  // FP8 K -> 16-bit pairs of Q's type
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            uint32_t lo = fp8x2_to_16<QDT != DT_BF16, false>(kc[c][e]);
+            uint32_t hi = fp8x2_to_16<QDT != DT_BF16, true>(kc[c][e]);
+            if constexpr (QDT == DT_BF16) {
+              acc = dot2_bf16(q[r][c][2 * e], lo, acc);
+              acc = dot2_bf16(q[r][c][2 * e + 1], hi, acc);
+            } else {
+              acc = dot2_f16(q[r][c][2 * e], lo, acc);
+              acc = dot2_f16(q[r][c][2 * e + 1], hi, acc);
+            }
+          }
+        }
+      }
+      acc += dpp<kDppQuadXor1>(acc);
+      acc += dpp<kDppQuadXor2>(acc);
+      s[r] = acc;
+    }
+
+    // ---- online softmax for this lane's rows ----
+    const int tok = pg * 16 + n;
+    const bool page_full = (pg * 16 + 16 <= t1);
+#pragma unroll
+    for (int k = 0; k < MR; ++k) {
+      float v = s[4 * k];
+      v = qq == 1 ? s[4 * k + 1] : v;
+      v = qq == 2 ? s[4 * k + 2] : v;
+      v = qq == 3 ? s[4 * k + 3] : v;
+      const bool valid = tok < t1 && tok <= pos_mine[k];
+      const float x = valid ? v * a.score_scale : kNegInf;
+      float mx = x;
+      mx = __builtin_fmaxf(mx, dpp<kDppRowRor4>(mx));
+      mx = __builtin_fmaxf(mx, dpp<kDppRowRor8>(mx));
+      mx = __builtin_fmaxf(mx, shfl_xor(mx, 16));
+      mx = __builtin_fmaxf(mx, shfl_xor(mx, 32));
+      const float m_new = __builtin_fmaxf(m_run[k], mx);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[k] - m_use);
+      const float pv = fast_exp2(x - m_use);
+      l_run[k] = l_run[k] * alpha + pv;
+      m_run[k] = m_new;
+      p_lds[wave][n][qq + 4 * k] = pv;
+      if (n == 0) alpha_lds[wave][qq + 4 * k] = alpha;
+    }
+    wave_lds_sync();
+
+    // ---- O += P V for this lane's value rows and token group ----
+    float al[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) al[r] = alpha_lds[wave][r];
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int c = 0; c < NL; ++c) o[r][c] *= al[r];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      const int t = tg * EPC + e;
+      float pr[RB];
+#pragma unroll
+      for (int r = 0; r < RB; ++r) pr[r] = p_lds[wave][t][r];
+      const bool tvalid = page_full || (pg * 16 + t < t1);
+#pragma unroll
+      for (int c = 0; c < NL; ++c) {
+        float vv = chunk_elem<KVDT>(vc[c], e);
+        vv = tvalid ? vv : 0.f;  // slots past the end may hold anything, NaN included
+#pragma unroll
+        for (int r = 0; r < RB; ++r) o[r][c] = __builtin_fmaf(pr[r], vv, o[r][c]);
+      }
+    }
+    wave_lds_sync();
+
+#pragma unroll
+    for (int c = 0; c < NL; ++c) { kc[c] = kn[c]; vc[c] = vn[c]; }
+  }
+
+  // ---- wave totals: l over the 16 token lanes of a row, o over the token groups ----
+#pragma unroll
+  for (int k = 0; k < MR; ++k) {
+    float l = l_run[k];
+    l += dpp<kDppRowRor4>(l);
+    l += dpp<kDppRowRor8>(l);
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+    l_run[k] = l;
+  }
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int c = 0; c < NL; ++c) {
+      float v = o[r][c];
+      if constexpr (CPR >= 2) v += dpp<kDppQuadXor1>(v);
+      if constexpr (CPR >= 4) v += dpp<kDppQuadXor2>(v);
+      o[r][c] = v;
+    }
+  if (n == 0) {
+#pragma unroll
+    for (int k = 0; k < MR; ++k) {
+      m_w[wave][qq + 4 * k] = m_run[k];
+      l_w[wave][qq + 4 * k] = l_run[k];
+    }
+  }
+  __syncthreads();
+
+  float f[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    float M;
+    wave_scales<RB>(m_w, wave, r, M, f[r]);
+  }
+  for (int w = 0; w < kWaves; ++w) {
+    if (wave == w && tg == 0) {
+#pragma unroll
+      for (int c = 0; c < NL; ++c) {
+        const int dv = (64 * c + lane) / CPR;
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          const float v = f[r] * o[r][c];
+          acc_lds[r][dv] = (w == 0) ? v : acc_lds[r][dv] + v;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- partial write: rows of this block ----
+  const int64_t P = a.P;
+  for (int idx = threadIdx.x; idx < RB * D; idx += 256) {
+    const int r = idx / D, d = idx % D;
+    const int rr = rb * RB + r;
+    if (rr < a.rows) {
+      const int64_t slot = (((int64_t)b * a.Hkv + kvh) * a.rows + rr) * P + p;
+      a.ws_o[slot * D + d] = acc_lds[r][d];
+    }
+  }
+  if (threadIdx.x < RB) {
+    const int r = threadIdx.x;
+    const int rr = rb * RB + r;
+    if (rr < a.rows) {
+      float M = kNegInf;
+      for (int w = 0; w < kWaves; ++w) M = __builtin_fmaxf(M, m_w[w][r]);
+      const float Mu = (M == kNegInf) ? 0.f : M;
+      float l = 0.f;
+      for (int w = 0; w < kWaves; ++w) l += fast_exp2(m_w[w][r] - Mu) * l_w[w][r];
+      const int64_t slot = (((int64_t)b * a.Hkv + kvh) * a.rows + rr) * P + p;
+      a.ws_ml[slot * 2 + 0] = M;
+      a.ws_ml[slot * 2 + 1] = l;
+    }
+  }
+}
+
+// ==================================================================================
+// MFMA partial kernel (16..64 rows)
+// ==================================================================================
+//
+// Per wave step: a page pair (32 tokens).  QK^T uses two 16x16x32 MFMAs per
+// 32-element d chunk, `a` = 0, 1, whose A rows m = 4j + i take tokens
+// 8j + 4a + i, so that after both the lane (n = row, j) holds the scores of
+// the 8 consecutive tokens 8j..8j+7 - exactly the 8 key slots it supplies as
+// the B operand (P^T) of the PV MFMA, whose A operand (V^T) is then a single
+// 16-byte read of a token-minor V page.
+template <int KVDT, int QDT>
+struct MfmaT {
+  static constexpr bool f16 = (KVDT == DT_F16) || (KVDT == DT_FP8 && QDT == DT_F16);
+};
+
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// d offset of the 8 elements lane group j supplies for 32-wide d chunk kc
+template <int KVDT>
+__device__ __forceinline__ int dchunk(int kc, int j) {
+  if constexpr (KVDT == DT_FP8) return 64 * (kc >> 1) + 16 * j + 8 * (kc & 1);
+  else return 32 * kc + 8 * j;
+}
+
+template <int KVDT, int QDT, int D, int NB>
+__global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
+  constexpr int ELT = DtInfo<KVDT>::bytes;
+  constexpr bool F16 = MfmaT<KVDT, QDT>::f16;
+  constexpr int KC = D / 32;           // 32-wide d chunks
+  constexpr int MB = D / 16;           // 16-row value blocks
+  constexpr int NR = 16 * NB;          // padded rows
+  constexpr int KL = (KVDT == DT_FP8) ? KC / 2 : KC;  // 16-byte K loads per `a`
+
+  __shared__ float m_w[kWaves][NR];
+  __shared__ float l_w[kWaves][NR];
+  __shared__ float acc_lds[NR][D + 4];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform_int(threadIdx.x >> 6);
+  const int p = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int L = min(a.lens[b], a.capacity);
+  const int t0 = p * a.T;
+  if (t0 >= L) return;
+  const int t1 = min(L, t0 + a.T);
+  const int n = lane & 15, j = lane >> 4;
+
+  // ---- Q^T fragments: B[k = d][n = row] ----
+  u32x4 qf[NB][KC];
+  int pos[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int rr = 16 * nb + n;
+    const bool ok = rr < a.rows;
+    const int h = kvh * a.G + (ok ? rr / a.R : 0);
+    const int i = ok ? rr % a.R : 0;
+    pos[nb] = ok ? L - a.R + i : -1;
+    const char *qrow = reinterpret_cast<const char *>(a.q) +
+                       ((int64_t)b * a.q_sb + (int64_t)i * a.q_sr + (int64_t)h * a.q_sh) * 2;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      u32x4 v = ld16(qrow + dchunk<KVDT>(kc, j) * 2);
+      qf[nb][kc] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  f32x4 oacc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) oacc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[NB], l_run[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) { m_run[nb] = kNegInf; l_run[nb] = 0.f; }
+
+  const char *kbase = reinterpret_cast<const char *>(a.k) + (int64_t)kvh * a.k_sh * ELT;
+  const char *vbase = reinterpret_cast<const char *>(a.v) + (int64_t)kvh * a.v_sh * ELT;
+  const int32_t *pt = a.page_table + (int64_t)b * a.pt_stride;
+  const int pg_end = (t1 + 15) >> 4;
+  const int pp_end = (t1 + 31) >> 5;
+  int pp = (t0 >> 5) + wave;
+
+  // K rows: A row m = n of MFMA `a` holds token 8*(n/4) + 4a + n%4 (page-pair local)
+  // V rows: value row 16*mb + n, tokens 8*j .. 8*j+7 (page j/2, offset 8*(j&1))
+  u32x4 kf[2][KL];
+  u32x2 vf8[MB];   // FP8 V: 8 bytes per fragment
+  u32x4 vf16[MB];
+  auto load_pair = [&](int ppi, u32x4 (*kd)[KL], u32x4 *vd16, u32x2 *vd8) {
+    const int pg0 = 2 * ppi;
+    const bool has1 = (pg0 + 1) < pg_end;
+    const int64_t pid0 = pt[pg0];
+    const int64_t pid1 = has1 ? pt[pg0 + 1] : pid0;
+#pragma unroll
+    for (int aa = 0; aa < 2; ++aa) {
+      const int tok = 8 * (n >> 2) + 4 * aa + (n & 3);
+      const int64_t pid = tok < 16 ? pid0 : pid1;
+      const char *kp = kbase + pid * a.k_sp * ELT + (tok & 15) * (D * ELT);
+#pragma unroll
+      for (int u = 0; u < KL; ++u) {
+        const int d0 = (KVDT == DT_FP8) ? 64 * u + 16 * j : dchunk<KVDT>(u, j);
+        kd[aa][u] = ld16(kp + d0 * ELT);
+      }
+    }
+    const int64_t pidv = (j >> 1) ? pid1 : pid0;
+    const char *vp = vbase + pidv * a.v_sp * ELT + (8 * (j & 1)) * ELT;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const char *row = vp + (int64_t)(16 * mb + n) * 16 * ELT;
+      if constexpr (KVDT == DT_FP8) vd8[mb] = ld8(row);
+      else vd16[mb] = ld16(row);
+    }
+  };
+  if (pp < pp_end) load_pair(pp, kf, vf16, vf8);
+
+  for (; pp < pp_end; pp += kWaves) {
+    u32x4 kn[2][KL];
+    u32x2 vn8[MB];
+    u32x4 vn16[MB];
+    const int ppn = pp + kWaves;
+    if (ppn < pp_end) load_pair(ppn, kn, vn16, vn8);
+
+    // ---- S^T = K Q^T ----
+    f32x4 s[NB][2];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int aa = 0; aa < 2; ++aa) s[nb][aa] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int aa = 0; aa < 2; ++aa) {
+#pragma unroll
+      for (int u = 0; u < KL; ++u) {
+        if constexpr (KVDT == DT_FP8) {
+          // 16 FP8 codes -> two 8-element 16-bit fragments (chunks kc = 2u, 2u+1)
+          u32x4 lo, hi;
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            const uint32_t x = kf[aa][u][w];
+            const uint32_t y = kf[aa][u][w + 2];
+            lo[2 * w] = fp8x2_to_16<F16, false>(x);
+            lo[2 * w + 1] = fp8x2_to_16<F16, true>(x);
+            hi[2 * w] = fp8x2_to_16<F16, false>(y);
+            hi[2 * w + 1] = fp8x2_to_16<F16, true>(y);
+          }
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            s[nb][aa] = mfma16<F16>(lo, qf[nb][2 * u], s[nb][aa]);
+            s[nb][aa] = mfma16<F16>(hi, qf[nb][2 * u + 1], s[nb][aa]);
+          }
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) s[nb][aa] = mfma16<F16>(kf[aa][u], qf[nb][u], s[nb][aa]);
+        }
+      }
+    }
+
+    // ---- online softmax: lane row 16*nb + n, tokens 8j .. 8j+7 ----
+    const int tokb = pp * 32 + 8 * j;
+    u32x4 pf[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float x[8];
+#pragma unroll
+      for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = tokb + 4 * aa + i;
+          const bool valid = tok < t1 && tok <= pos[nb];
+          x[4 * aa + i] = valid ? s[nb][aa][i] * a.score_scale : kNegInf;
+        }
+      float mx = max3(x[0], x[1], x[2]);
+      mx = max3(mx, x[3], x[4]);
+      mx = max3(mx, x[5], x[6]);
+      mx = __builtin_fmaxf(mx, x[7]);
+      mx = __builtin_fmaxf(mx, shfl_xor(mx, 16));
+      mx = __builtin_fmaxf(mx, shfl_xor(mx, 32));
+      const float m_new = __builtin_fmaxf(m_run[nb], mx);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[nb] - m_use);
+      m_run[nb] = m_new;
+      float pv[8], ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pv[e] = fast_exp2(x[e] - m_use);
+        ps += pv[e];
+      }
+      l_run[nb] = l_run[nb] * alpha + ps;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) oacc[mb][nb] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        pf[nb][e] = F16 ? pack_f16x2(pv[2 * e], pv[2 * e + 1]) : pack_bf16x2(pv[2 * e], pv[2 * e + 1]);
+    }
+
+    // ---- O^T += V^T P^T ----
+    const bool tail = (pp * 32 + 32 > t1);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      u32x4 vfr;
+      if constexpr (KVDT == DT_FP8) {
+        vfr[0] = fp8x2_to_16<F16, false>(vf8[mb][0]);
+        vfr[1] = fp8x2_to_16<F16, true>(vf8[mb][0]);
+        vfr[2] = fp8x2_to_16<F16, false>(vf8[mb][1]);
+        vfr[3] = fp8x2_to_16<F16, true>(vf8[mb][1]);
+      } else {
+        vfr = vf16[mb];
+      }
+      if (tail) {  // value slots at or past the end may hold anything: zero them
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int tk = tokb + 2 * e;
+          uint32_t w = vfr[e];
+          if (tk >= t1) w &= 0xffff0000u;
+          if (tk + 1 >= t1) w &= 0x0000ffffu;
+          vfr[e] = w;
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) oacc[mb][nb] = mfma16<F16>(vfr, pf[nb], oacc[mb][nb]);
+    }
+
+#pragma unroll
+    for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+      for (int u = 0; u < KL; ++u) kf[aa][u] = kn[aa][u];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) { vf16[mb] = vn16[mb]; vf8[mb] = vn8[mb]; }
+  }
+
+  // ---- wave totals ----
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    float l = l_run[nb];
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+    l_run[nb] = l;
+  }
+  if (j == 0) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      m_w[wave][16 * nb + n] = m_run[nb];
+      l_w[wave][16 * nb + n] = l_run[nb];
+    }
+  }
+  __syncthreads();
+  float f[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    float M;
+    wave_scales<NR>(m_w, wave, 16 * nb + n, M, f[nb]);
+  }
+  for (int w = 0; w < kWaves; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int d = 16 * mb + 4 * j + i, r = 16 * nb + n;
+            const float v = f[nb] * oacc[mb][nb][i];
+            acc_lds[r][d] = (w == 0) ? v : acc_lds[r][d] + v;
+          }
+    }
+    __syncthreads();
+  }
+
+  const int64_t P = a.P;
+  for (int idx = threadIdx.x; idx < NR * D; idx += 256) {
+    const int r = idx / D, d = idx % D;
+    if (r < a.rows) {
+      const int64_t slot = (((int64_t)b * a.Hkv + kvh) * a.rows + r) * P + p;
+      a.ws_o[slot * D + d] = acc_lds[r][d];
+    }
+  }
+  for (int r = threadIdx.x; r < NR; r += 256) {
+    if (r < a.rows) {
+      float M = kNegInf;
+      for (int w = 0; w < kWaves; ++w) M = __builtin_fmaxf(M, m_w[w][r]);
+      const float Mu = (M == kNegInf) ? 0.f : M;
+      float l = 0.f;
+      for (int w = 0; w < kWaves; ++w) l += fast_exp2(m_w[w][r] - Mu) * l_w[w][r];
+      const int64_t slot = (((int64_t)b * a.Hkv + kvh) * a.rows + r) * P + p;
+      a.ws_ml[slot * 2 + 0] = M;
+      a.ws_ml[slot * 2 + 1] = l;
+    }
+  }
+}
+
+// ==================================================================================
+// Log-sum-exp merge of the partitions + sink, one wave per output row
+// ==================================================================================
+template <int ODT, int D>
+__global__ __launch_bounds__(64) void decode_merge(DecodeArgs a) {
+  constexpr int DPL = D / 64;
+  const int lane = threadIdx.x;
+  const int rr = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int L = min(a.lens[b], a.capacity);
+  const int Pl = (L + a.T - 1) / a.T;  // live partitions
+  const int h = kvh * a.G + rr / a.R, i = rr % a.R;
+  const int64_t base = (((int64_t)b * a.Hkv + kvh) * a.rows + rr) * a.P;
+  const float sink = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
+
+  float M = sink;
+  for (int p = lane; p < Pl; p += 64) M = __builtin_fmaxf(M, a.ws_ml[(base + p) * 2]);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) M = __builtin_fmaxf(M, shfl_xor(M, m));
+
+  float o[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
+  float Z = 0.f;
+  if (M != kNegInf) {
+    Z = fast_exp2(sink - M);
+    for (int p0 = 0; p0 < Pl; p0 += 64) {
+      const int pm = p0 + lane;
+      float w = 0.f;
+      if (pm < Pl) {
+        const float mp = a.ws_ml[(base + pm) * 2];
+        const float lp = a.ws_ml[(base + pm) * 2 + 1];
+        w = (mp == kNegInf) ? 0.f : fast_exp2(mp - M);
+        Z += w * lp;
+      }
+      const int cnt = min(64, Pl - p0);
+      for (int q = 0; q < cnt; ++q) {
+        const float wq = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(w), q));
+        const float *op = a.ws_o + (base + p0 + q) * D;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[e] = __builtin_fmaf(wq, op[lane + 64 * e], o[e]);
+      }
+    }
+    // Z: the sink term counted once (lane 0), partition terms summed over lanes
+    float zs = Z - (lane == 0 ? 0.f : fast_exp2(sink - M));
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) zs += shfl_xor(zs, m);
+    Z = zs;
+  }
+  const float inv = (M == kNegInf) ? 0.f : a.v_scale / Z;
+  char *orow = reinterpret_cast<char *>(a.o);
+  const int64_t obase = (int64_t)b * a.o_sb + (int64_t)i * a.o_sr + (int64_t)h * a.o_sh;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) store_out<ODT>(orow, obase + lane + 64 * e, o[e] * inv);
+  if (a.lse && lane == 0) {
+    const float lse = (M == kNegInf) ? kNegInf : (M + __builtin_log2f(Z)) * kLn2;
+    a.lse[((int64_t)b * a.Hq + h) * a.R + i] = lse;
+  }
+}
+
+// ==================================================================================
+// Debug gather: K/V of one sequence through the page table, dequantised the
+// way the kernels do it (FP8 through both the FP32 and the 16-bit routes;
+// a disagreement between the two is reported as NaN).
+// ==================================================================================
+template <int KVDT>
+__global__ void debug_gather(const void *k, const void *v, int64_t k_sp, int64_t k_sh,
+                             int64_t v_sp, int64_t v_sh, int Hkv, int D, float k_scale,
+                             float v_scale, const int32_t *pt, int seq_len, float *k_out,
+                             float *v_out) {
+  const int64_t total = (int64_t)Hkv * seq_len * D;
+  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int d = idx % D;
+    const int t = (idx / D) % seq_len;
+    const int g = idx / ((int64_t)D * seq_len);
+    const int64_t pid = pt[t >> 4];
+    const int64_t ki = pid * k_sp + g * k_sh + (t & 15) * D + d;
+    const int64_t vi = pid * v_sp + g * v_sh + (int64_t)d * 16 + (t & 15);
+    float kv[2];
+    const int64_t src[2] = {ki, vi};
+    const void *base[2] = {k, v};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int64_t e = src[s];
+      if constexpr (KVDT == DT_F32) {
+        kv[s] = reinterpret_cast<const float *>(base[s])[e];
+      } else if constexpr (KVDT == DT_BF16) {
+        kv[s] = bf16_lo(reinterpret_cast<const uint16_t *>(base[s])[e]);
+      } else if constexpr (KVDT == DT_F16) {
+        kv[s] = f16_lo(reinterpret_cast<const uint16_t *>(base[s])[e]);
+      } else {
+        const uint32_t code = reinterpret_cast<const uint8_t *>(base[s])[e];
+        const float a32 = fp8x2_to_f32<false>(code)[0];
+        const float b16 = bf16_lo(fp8x2_to_bf16x2<false>(code));
+        const float h16 = f16_lo(fp8x2_to_f16x2<false>(code));
+        const bool agree = (__float_as_uint(a32) == __float_as_uint(b16)) &&
+                           (__float_as_uint(a32) == __float_as_uint(h16));
+        kv[s] = (agree || a32 != a32) ? a32 : __builtin_nanf("");
+      }
+    }
+    k_out[idx] = kv[0] * k_scale;
+    v_out[idx] = kv[1] * v_scale;
+  }
+}
+
+// ==================================================================================
+// launchers
+// ==================================================================================
+
+bool decode_valu_supported(int kv, int qd, int D) {
+  if (D != 64 && D != 128) return false;
+  if (kv == DT_F32) return qd == DT_F32 || qd == DT_F16 || qd == DT_BF16;
+  if (kv == DT_BF16) return qd == DT_BF16;
+  if (kv == DT_F16) return qd == DT_F16;
+  if (kv == DT_FP8) return qd == DT_BF16 || qd == DT_F16;
+  return false;
+}
+
+bool decode_mfma_supported(int kv, int qd, int D, int rows) {
+  if (D != 64 && D != 128) return false;
+  if (rows > 64) return false;
+  if (kv == DT_BF16) return qd == DT_BF16;
+  if (kv == DT_F16) return qd == DT_F16;
+  if (kv == DT_FP8) return qd == DT_BF16 || qd == DT_F16;
+  return false;
+}
+
+template <int KV, int QD, int D>
+static hipError_t valu_rb(const DecodeArgs &a, hipStream_t s) {
+  dim3 grid(a.P, a.Hkv * a.row_blocks, a.B);
+  const int rb = (a.rows + a.row_blocks - 1) / a.row_blocks;
+  if (rb <= 4) hipLaunchKernelGGL((decode_valu<KV, QD, D, 4>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((decode_valu<KV, QD, D, 8>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int KV, int QD>
+static hipError_t valu_d(const DecodeArgs &a, hipStream_t s) {
+  return a.D == 64 ? valu_rb<KV, QD, 64>(a, s) : valu_rb<KV, QD, 128>(a, s);
+}
+
+hipError_t launch_decode_valu(const DecodeArgs &a, hipStream_t s) {
+  switch (a.kv_dtype) {
+    case DT_F32:
+      if (a.q_dtype == DT_F32) return valu_d<DT_F32, DT_F32>(a, s);
+      if (a.q_dtype == DT_BF16) return valu_d<DT_F32, DT_BF16>(a, s);
+      return valu_d<DT_F32, DT_F16>(a, s);
+    case DT_BF16: return valu_d<DT_BF16, DT_BF16>(a, s);
+    case DT_F16: return valu_d<DT_F16, DT_F16>(a, s);
+    default:
+      if (a.q_dtype == DT_BF16) return valu_d<DT_FP8, DT_BF16>(a, s);
+      return valu_d<DT_FP8, DT_F16>(a, s);
+  }
+}
+
+template <int KV, int QD, int D>
+static hipError_t mfma_nb(const DecodeArgs &a, hipStream_t s) {
+  dim3 grid(a.P, a.Hkv, a.B);
+  const int nb = (a.rows + 15) / 16;
+  switch (nb) {
+    case 1: hipLaunchKernelGGL((decode_mfma<KV, QD, D, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_mfma<KV, QD, D, 2>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((decode_mfma<KV, QD, D, 4>), grid, dim3(256), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+template <int KV, int QD>
+static hipError_t mfma_d(const DecodeArgs &a, hipStream_t s) {
+  return a.D == 64 ? mfma_nb<KV, QD, 64>(a, s) : mfma_nb<KV, QD, 128>(a, s);
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s) {
+  switch (a.kv_dtype) {
+    case DT_BF16: return mfma_d<DT_BF16, DT_BF16>(a, s);
+    case DT_F16: return mfma_d<DT_F16, DT_F16>(a, s);
+    default:
+      if (a.q_dtype == DT_BF16) return mfma_d<DT_FP8, DT_BF16>(a, s);
+      return mfma_d<DT_FP8, DT_F16>(a, s);
+  }
+}
+
+template <int ODT>
+static hipError_t merge_o(const DecodeArgs &a, hipStream_t s) {
+  dim3 grid(a.rows, a.Hkv, a.B);
+  if (a.D == 64) hipLaunchKernelGGL((decode_merge<ODT, 64>), grid, dim3(64), 0, s, a);
+  else hipLaunchKernelGGL((decode_merge<ODT, 128>), grid, dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t s) {
+  if (a.o_dtype == DT_F32) return merge_o<DT_F32>(a, s);
+  if (a.o_dtype == DT_BF16) return merge_o<DT_BF16>(a, s);
+  return merge_o<DT_F16>(a, s);
+}
+
+hipError_t launch_debug_gather(const void *k, const void *v, int64_t k_sp, int64_t k_sh,
+                               int64_t v_sp, int64_t v_sh, int kv_dtype, int Hkv, int D,
+                               float k_scale, float v_scale, const int32_t *pt_row, int seq_len,
+                               float *k_out, float *v_out, hipStream_t s) {
+  const int64_t total = (int64_t)Hkv * seq_len * D;
+  if (total == 0) return hipSuccess;
+  const int blocks = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
+#define PA_GATHER(DT)                                                                     \
+  hipLaunchKernelGGL((debug_gather<DT>), dim3(blocks), dim3(256), 0, s, k, v, k_sp, k_sh, \
+                     v_sp, v_sh, Hkv, D, k_scale, v_scale, pt_row, seq_len, k_out, v_out)
+  switch (kv_dtype) {
+    case DT_F32: PA_GATHER(DT_F32); break;
+    case DT_F16: PA_GATHER(DT_F16); break;
+    case DT_BF16: PA_GATHER(DT_BF16); break;
+    default: PA_GATHER(DT_FP8); break;
+  }
+#undef PA_GATHER
+  return hipGetLastError();
+}
+
+}  // namespace pa

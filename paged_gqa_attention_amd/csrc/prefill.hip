@@ -1,0 +1,501 @@
+// Causal prefill attention (with optional per-head sinks and an optional
+// block mask) over a paged K/V cache, for gfx950.
+//
+// A workgroup owns a 128-row query tile of HPW (1 or 2) query heads of one
+// KV group; each wave owns 64 rows of one head.  64-key K/V tiles are
+// gathered through the page table into LDS (double buffered) and shared by
+// all waves.  Per wave and tile:
+//     S^T = K Q^T        (32x32x16 MFMA, FP32 accumulators)
+//     online softmax     (FP32, one row per lane column, lazy rescaling)
+//     O^T += V^T P^T     (P rounded to the MFMA operand type)
+// The K rows of each 32-key block are stored in LDS in the order that makes
+// every lane's 16 scores of a row exactly the 16 keys it then supplies to
+// the P.V products, and V pages are token-minor, so no transposes are needed.
+//
+// Tiles wholly above a wave's diagonal are skipped (Geramy/LSE releases,
+// v0.4.14: fully masked key windows skipped, the rest keep their arithmetic);
+// with a block mask only tiles some row keeps are visited (FlashPrefill V2
+// paragraph of the Geramy/LSE README).  Sinks are added to the softmax
+// denominator at the end (TokenSpeed-Kernel-AMD page, "Attention").
+//
+// Workgroup order: tasks (query tile, sequence, KV head) are ordered
+// heaviest-first and dealt round-robin to the 8 XCDs; the G/HPW workgroups of
+// one task land on the same XCD back to back so their K/V tiles come from
+// that XCD's L2.
+#include "attn_internal.h"
+#include "common.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kXcds = 8;
+constexpr int kTileK = 64;     // keys per tile
+constexpr int kTileQ = 128;    // query rows per workgroup
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLazy = 8.0f;  // rescale only when the max grows by more than 2^8
+
+__device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f32x16 &c,
+                                         bool f16) {
+  if (f16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// LDS row of key k within a 32-key block: swap bits 2 and 3 (an involution)
+__device__ __forceinline__ int kperm(int k) {
+  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+template <int KVDT, int QDT>
+struct Cfg {
+  static constexpr bool f16 = (KVDT == DT_F16) || (KVDT == DT_FP8 && QDT == DT_F16);
+};
+
+}  // namespace
+
+template <int KVDT, int QDT, int D, int HPW, bool MASK>
+__global__ __launch_bounds__(HPW * 128) void prefill_mfma(PrefillArgs a) {
+  constexpr int ELT = DtInfo<KVDT>::bytes;
+  constexpr bool F16 = Cfg<KVDT, QDT>::f16;
+  constexpr int NT = HPW * 128;         // threads
+  constexpr int KS = D / 16;            // 16-wide d steps of QK^T
+  constexpr int DB = D / 32;            // 32-row value blocks of PV
+  constexpr int KSTR = D + 8;           // K LDS row stride (16-bit elements)
+  constexpr int VSTR = kTileK + 8;      // V^T LDS row stride
+  constexpr int KBUF = kTileK * KSTR;
+  constexpr int VBUF = D * VSTR;
+  // global chunks (16 bytes of stored dtype) per tile, and per thread
+  constexpr int KCH = kTileK * D * ELT / 16;
+  constexpr int VCH = KCH;
+  constexpr int KPT = (KCH + NT - 1) / NT;
+  constexpr int VPT = (VCH + NT - 1) / NT;
+  constexpr int EPC = 16 / ELT;         // stored elements per chunk
+  constexpr int LIST = 1024;            // tiles per mask window
+
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KBUF];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][VBUF];
+  __shared__ int tile_list[MASK ? LIST : 1];
+  __shared__ int list_count[MASK ? NT / 64 + 1 : 1];
+
+  // ---- task of this workgroup ----
+  const int wpt = a.G / HPW;  // workgroups per task
+  const int x = blockIdx.x;
+  const int xcd = x % kXcds, slot = x / kXcds;
+  const int task = (slot / wpt) * kXcds + xcd;
+  const int hp = slot % wpt;
+  const int ntask = a.q_tiles * a.B * a.Hkv;
+  if (task >= ntask) return;
+  const int kvh = task % a.Hkv;
+  const int b = (task / a.Hkv) % a.B;
+  const int qt = a.q_tiles - 1 - task / (a.Hkv * a.B);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = kvh * a.G + hp * HPW + (wave >> 1);
+  const int q0 = qt * kTileQ + (wave & 1) * 64;  // first row of this wave
+  const int L = min(a.lens[b], a.capacity);
+  const int off = L - a.n_q;                      // position of row i is off + i
+  const int nl = lane & 31, hh = lane >> 5;
+
+  // rows of the whole tile and of this wave
+  const int tile_last = min(qt * kTileQ + kTileQ, a.n_q) - 1;
+  const int wave_last = min(q0 + 64, a.n_q) - 1;
+  const bool wave_has_rows = q0 < a.n_q;
+  const int key_end = min(L, off + tile_last + 1);  // keys the tile can see
+  // key_end <= 0: no key is visible to any row, the rows are empty (o = 0, lse = sink)
+  const int nt = key_end > 0 ? (key_end + kTileK - 1) / kTileK : 0;
+  const int wave_key_end = wave_has_rows ? min(L, off + wave_last + 1) : 0;
+  const int wave_first_pos = off + q0;
+
+  // ---- Q^T fragments: B[k = d][n = row], lane (row nl (+32 nb), k half hh) ----
+  u32x4 qf[2][KS];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int i = q0 + 32 * nb + nl;
+    const bool ok = i < a.n_q;
+    const char *qrow = reinterpret_cast<const char *>(a.q) +
+                       ((int64_t)b * a.q_sb + (int64_t)(ok ? i : 0) * a.q_sr +
+                        (int64_t)h * a.q_sh) * 2;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = ld16(qrow + (16 * ks + 8 * hh) * 2);
+      qf[nb][ks] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  f32x16 oacc[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][nb][i] = 0.f;
+  float m_run[2] = {kNegInf, kNegInf};
+  float l_run[2] = {0.f, 0.f};
+  int pos_row[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int i = q0 + 32 * nb + nl;
+    pos_row[nb] = i < a.n_q ? off + i : -1;
+  }
+
+  const int32_t *pt = a.page_table + (int64_t)b * a.pt_stride;
+  const char *kbase = reinterpret_cast<const char *>(a.k) + (int64_t)kvh * a.k_sh * ELT;
+  const char *vbase = reinterpret_cast<const char *>(a.v) + (int64_t)kvh * a.v_sh * ELT;
+  const int mh = (MASK && a.mask_heads != 1) ? kvh : 0;
+  const uint8_t *mrow = MASK ? a.mask + ((int64_t)b * a.mask_heads + mh) *
+                                          (int64_t)a.mask_nqb * a.mask_nkb
+                             : nullptr;
+
+  // ---- staging: global -> registers -> LDS ----
+  u32x4 kreg[KPT], vreg[VPT];
+  auto gload = [&](int t) {
+    const int kbase_tok = t * kTileK;
+#pragma unroll
+    for (int c = 0; c < KPT; ++c) {
+      const int ch = tid + c * NT;
+      if (ch < KCH) {
+        const int key = ch / (D * ELT / 16);
+        const int part = ch % (D * ELT / 16);
+        const int tok = kbase_tok + key;
+        const int64_t pid = pt[min(tok, L - 1) >> 4];  // keys past the end: masked later
+        kreg[c] = ld16(kbase + (pid * a.k_sp + (tok & 15) * D + part * EPC) * ELT);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < VPT; ++c) {
+      const int ch = tid + c * NT;
+      if (ch < VCH) {
+        const int pg = ch / (D * ELT);
+        const int cc = ch % (D * ELT);
+        const int tok0 = kbase_tok + 16 * pg;
+        const int64_t pid = pt[min(tok0, L - 1) >> 4];
+        vreg[c] = ld16(vbase + (pid * a.v_sp + (int64_t)cc * EPC) * ELT);
+      }
+    }
+  };
+  auto lstore = [&](int t, int buf) {
+    const int kbase_tok = t * kTileK;
+#pragma unroll
+    for (int c = 0; c < KPT; ++c) {
+      const int ch = tid + c * NT;
+      if (ch < KCH) {
+        const int key = ch / (D * ELT / 16);
+        const int part = ch % (D * ELT / 16);
+        const int row = (key & ~31) | kperm(key & 31);
+        uint16_t *dst = &k_lds[buf][row * KSTR + part * EPC];
+        if constexpr (KVDT == DT_FP8) {
+          u32x4 lo, hi;
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            lo[2 * w] = fp8x2_to_16<F16, false>(kreg[c][w]);
+            lo[2 * w + 1] = fp8x2_to_16<F16, true>(kreg[c][w]);
+            hi[2 * w] = fp8x2_to_16<F16, false>(kreg[c][w + 2]);
+            hi[2 * w + 1] = fp8x2_to_16<F16, true>(kreg[c][w + 2]);
+          }
+          *reinterpret_cast<u32x4 *>(dst) = lo;
+          *reinterpret_cast<u32x4 *>(dst + 8) = hi;
+        } else {
+          *reinterpret_cast<u32x4 *>(dst) = kreg[c];
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < VPT; ++c) {
+      const int ch = tid + c * NT;
+      if (ch < VCH) {
+        const int pg = ch / (D * ELT);
+        const int cc = ch % (D * ELT);
+        const int d = cc / ELT;               // value row
+        const int tg = cc % ELT;              // token group within the page row
+        const int tok0 = kbase_tok + 16 * pg + tg * EPC;
+        uint16_t *dst = &v_lds[buf][d * VSTR + 16 * pg + tg * EPC];
+        u32x4 w16[EPC / 8];
+        if constexpr (KVDT == DT_FP8) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            w16[w >> 1][2 * (w & 1)] = fp8x2_to_16<F16, false>(vreg[c][w]);
+            w16[w >> 1][2 * (w & 1) + 1] = fp8x2_to_16<F16, true>(vreg[c][w]);
+          }
+        } else {
+          w16[0] = vreg[c];
+        }
+        // zero slots at or past the end of the sequence (they may hold NaN)
+        if (tok0 + EPC > L) {
+#pragma unroll
+          for (int q = 0; q < EPC / 8; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int tk = tok0 + 8 * q + 2 * e;
+              uint32_t wv = w16[q][e];
+              if (tk >= L) wv &= 0xffff0000u;
+              if (tk + 1 >= L) wv &= 0x0000ffffu;
+              w16[q][e] = wv;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < EPC / 8; ++q) *reinterpret_cast<u32x4 *>(dst + 8 * q) = w16[q];
+      }
+    }
+  };
+
+  // ---- per-tile work of one wave ----
+  const float sc = a.score_scale;
+  auto compute = [&](int t, int buf) {
+    const int kt0 = t * kTileK;
+    if (!wave_has_rows || kt0 >= wave_key_end) return;
+    bool keep_row[2] = {true, true};
+    if constexpr (MASK) {
+      const int kb = kt0 / a.mask_block;
+      bool any = false;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int pr = pos_row[nb];
+        bool k = false;
+        if (pr >= 0) {
+          const int qb = pr / a.mask_block;
+          k = qb < a.mask_nqb && kb < a.mask_nkb && mrow[(int64_t)qb * a.mask_nkb + kb] != 0;
+        }
+        keep_row[nb] = k;
+        any |= k;
+      }
+      if (!__builtin_amdgcn_ballot_w64(any)) return;
+    }
+    const bool diag = (kt0 + kTileK - 1 > wave_first_pos) || (kt0 + kTileK > L);
+    const uint16_t *kl = k_lds[buf];
+    const uint16_t *vl = v_lds[buf];
+
+    // S^T[mb][nb]: keys 32mb + kperm(m), rows 32nb + nl
+    f32x16 s[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[mb][nb][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const u32x4 ka = *reinterpret_cast<const u32x4 *>(kl + (32 * mb + nl) * KSTR + 16 * ks + 8 * hh);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) s[mb][nb] = mfma32(ka, qf[nb][ks], s[mb][nb], F16);
+      }
+    }
+
+    // softmax, rows 32nb + nl; lane half hh holds keys 32mb + 16g' + 8hh + 4(g&1) + i'
+    u32x4 pf[2][2][2];  // [mb][kk][nb]: P^T fragment, keys 32mb + 16kk + 8hh .. +8
+    float alpha[2];
+    bool need_rescale = false;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      float x[32];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float v = s[mb][nb][i] * sc;
+          if (diag || MASK) {
+            const int key = kt0 + 32 * mb + 16 * (i >> 3) + 8 * hh + 4 * ((i >> 2) & 1) + (i & 3);
+            const bool ok = key <= pos_row[nb] && key < L && keep_row[nb];
+            v = ok ? v : kNegInf;
+          }
+          x[16 * mb + i] = v;
+        }
+      float mx = x[0];
+#pragma unroll
+      for (int e = 1; e + 1 < 32; e += 2) mx = max3(mx, x[e], x[e + 1]);
+      mx = __builtin_fmaxf(mx, x[31]);
+      mx = __builtin_fmaxf(mx, shfl_xor(mx, 32));
+      const float m_old = m_run[nb];
+      const bool grow = mx > m_old + kLazy;
+      const float m_new = grow ? mx : m_old;
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      alpha[nb] = grow ? fast_exp2(m_old - m_use) : 1.0f;
+      need_rescale |= grow;
+      m_run[nb] = m_new;
+      float lsum = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          u32x4 f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = fast_exp2(x[16 * mb + 8 * kk + 2 * e] - m_use);
+            const float p1 = fast_exp2(x[16 * mb + 8 * kk + 2 * e + 1] - m_use);
+            const uint32_t w = F16 ? pack_f16x2(p0, p1) : pack_bf16x2(p0, p1);
+            f[e] = w;
+            lsum = F16 ? dot2_f16(w, 0x3C003C00u, lsum) : dot2_bf16(w, 0x3F803F80u, lsum);
+          }
+          pf[mb][kk][nb] = f;
+        }
+      l_run[nb] = l_run[nb] * alpha[nb] + lsum;
+    }
+    if (__builtin_amdgcn_ballot_w64(need_rescale)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) oacc[db][nb] *= alpha[nb];
+    }
+
+    // O^T[db][nb] += V^T[32 rows, 16 keys] P^T[16 keys, 32 rows]
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const u32x4 va = *reinterpret_cast<const u32x4 *>(vl + (32 * db + nl) * VSTR + 32 * mb + 16 * kk + 8 * hh);
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) oacc[db][nb] = mfma32(va, pf[mb][kk][nb], oacc[db][nb], F16);
+        }
+  };
+
+  // ---- tile loop ----
+  if (nt > 0) {
+    if constexpr (!MASK) {
+      gload(0);
+      lstore(0, 0);
+      __syncthreads();
+      for (int t = 0; t < nt; ++t) {
+        const int buf = t & 1;
+        if (t + 1 < nt) gload(t + 1);
+        compute(t, buf);
+        if (t + 1 < nt) lstore(t + 1, buf ^ 1);
+        __syncthreads();
+      }
+    } else {
+      // rows of the tile span query blocks [qb_lo, qb_hi]
+      const int first_row = qt * kTileQ;
+      const int qb_lo = max(0, off + first_row) / a.mask_block;
+      const int qb_hi = max(0, off + tile_last) / a.mask_block;
+      for (int w0 = 0; w0 < nt; w0 += LIST) {
+        const int wn = min(LIST, nt - w0);
+        // compact list of tiles in [w0, w0 + wn) that some row of the tile keeps
+        int base = 0;
+        for (int c0 = 0; c0 < wn; c0 += NT) {
+          const int t = w0 + c0 + tid;
+          bool keep = false;
+          if (c0 + tid < wn) {
+            const int kb = (t * kTileK) / a.mask_block;
+            for (int qb = qb_lo; qb <= qb_hi && !keep; ++qb)
+              keep = qb < a.mask_nqb && kb < a.mask_nkb && kb <= qb &&
+                     mrow[(int64_t)qb * a.mask_nkb + kb] != 0;
+          }
+          const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+          const int below = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+          if (lane == 0) list_count[wave] = __builtin_popcountll(bal);
+          __syncthreads();
+          int wbase = base;
+          for (int w = 0; w < wave; ++w) wbase += list_count[w];
+          if (keep) tile_list[wbase + below] = t;
+          int tot = 0;
+          for (int w = 0; w < NT / 64; ++w) tot += list_count[w];
+          __syncthreads();
+          base += tot;
+        }
+        const int cnt = base;
+        if (cnt == 0) continue;
+        gload(tile_list[0]);
+        lstore(tile_list[0], 0);
+        __syncthreads();
+        for (int idx = 0; idx < cnt; ++idx) {
+          const int buf = idx & 1;
+          const int t = tile_list[idx];
+          const bool more = idx + 1 < cnt;
+          const int tn = more ? tile_list[idx + 1] : 0;
+          if (more) gload(tn);
+          compute(t, buf);
+          if (more) lstore(tn, buf ^ 1);
+          __syncthreads();
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: sink, normalisation, output ----
+  if (!wave_has_rows) return;
+  const float sink = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
+  char *obase = reinterpret_cast<char *>(a.o);
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const float l = l_run[nb] + shfl_xor(l_run[nb], 32);
+    const float m = m_run[nb];
+    const float M = __builtin_fmaxf(m, sink);
+    float scale_o = 0.f, lse = kNegInf;
+    if (M != kNegInf) {
+      const float em = fast_exp2(m - M);
+      const float Z = l * em + fast_exp2(sink - M);
+      scale_o = em * a.v_scale / Z;
+      lse = (M + __builtin_log2f(Z)) * kLn2;
+    }
+    const int i = q0 + 32 * nb + nl;
+    if (i < a.n_q) {
+      const int64_t orow = (int64_t)b * a.o_sb + (int64_t)i * a.o_sr + (int64_t)h * a.o_sh;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * db + 8 * g + 4 * hh;
+          const float v0 = oacc[db][nb][4 * g + 0] * scale_o;
+          const float v1 = oacc[db][nb][4 * g + 1] * scale_o;
+          const float v2 = oacc[db][nb][4 * g + 2] * scale_o;
+          const float v3 = oacc[db][nb][4 * g + 3] * scale_o;
+          if (a.o_dtype == DT_BF16) {
+            u32x2 w = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+            *reinterpret_cast<u32x2 *>(obase + (orow + d0) * 2) = w;
+          } else if (a.o_dtype == DT_F16) {
+            u32x2 w = {pack_f16x2(v0, v1), pack_f16x2(v2, v3)};
+            *reinterpret_cast<u32x2 *>(obase + (orow + d0) * 2) = w;
+          } else {
+            *reinterpret_cast<f32x4 *>(obase + (orow + d0) * 4) = f32x4{v0, v1, v2, v3};
+          }
+        }
+      if (a.lse && hh == 0) a.lse[((int64_t)b * a.Hq + h) * a.n_q + i] = lse;
+    }
+  }
+}
+
+bool prefill_supported(int kv, int qd, int D) {
+  if (D != 64 && D != 128) return false;
+  if (kv == DT_BF16) return qd == DT_BF16;
+  if (kv == DT_F16) return qd == DT_F16;
+  if (kv == DT_FP8) return qd == DT_BF16 || qd == DT_F16;
+  return false;
+}
+
+template <int KV, int QD, int D, int HPW>
+static hipError_t prefill_m(const PrefillArgs &a, hipStream_t s) {
+  if (a.mask)
+    hipLaunchKernelGGL((prefill_mfma<KV, QD, D, HPW, true>), dim3(a.num_wg), dim3(HPW * 128), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_mfma<KV, QD, D, HPW, false>), dim3(a.num_wg), dim3(HPW * 128), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int KV, int QD, int D>
+static hipError_t prefill_h(const PrefillArgs &a, hipStream_t s) {
+  return a.heads_per_wg == 2 ? prefill_m<KV, QD, D, 2>(a, s) : prefill_m<KV, QD, D, 1>(a, s);
+}
+
+template <int KV, int QD>
+static hipError_t prefill_d(const PrefillArgs &a, hipStream_t s) {
+  return a.D == 64 ? prefill_h<KV, QD, 64>(a, s) : prefill_h<KV, QD, 128>(a, s);
+}
+
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {
+  switch (a.kv_dtype) {
+    case DT_BF16: return prefill_d<DT_BF16, DT_BF16>(a, s);
+    case DT_F16: return prefill_d<DT_F16, DT_F16>(a, s);
+    default:
+      if (a.q_dtype == DT_BF16) return prefill_d<DT_FP8, DT_BF16>(a, s);
+      return prefill_d<DT_FP8, DT_F16>(a, s);
+  }
+}
+
+}  // namespace pa

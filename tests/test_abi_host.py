@@ -1,0 +1,187 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+symbol the header declares, and its argument checking and split planning
+behave as documented.  Planning-only contexts never enqueue work."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import paged_gqa_attention_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_attn.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:attn_status|size_t|int|void)\s+\**(attn_\w+)\s*\(",
+                                 src, re.M)))
+
+
+def test_header_declares_the_binding_names():
+    assert _declared() == sorted(pa.EXPORTED)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pa.LIB_PATH):
+        pytest.skip("library not built")
+    return pa.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert lib.attn_abi_version() == 1
+
+
+def test_open_without_a_gpu_is_a_device_error(lib):
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(pa.AttnError) as e:
+        pa.attn_open(0)
+    assert e.value.status == pa.ATTN_ERR_DEVICE
+
+
+class FakeTensor:
+    """Shape/stride/pointer stand-in so argument checks can run without device memory."""
+
+    def __init__(self, shape, dtype, ptr=0x10000, strides=None):
+        self.shape = tuple(shape)
+        self.dtype = dtype
+        self._ptr = ptr
+        if strides is None:
+            strides, acc = [], 1
+            for s in reversed(shape):
+                strides.append(acc)
+                acc *= s
+            strides = list(reversed(strides))
+        self._strides = tuple(strides)
+
+    def data_ptr(self):
+        return self._ptr
+
+    def stride(self, i=None):
+        return self._strides if i is None else self._strides[i]
+
+    def dim(self):
+        return len(self.shape)
+
+    def is_contiguous(self):
+        return True
+
+    def numel(self):
+        n = 1
+        for s in self.shape:
+            n *= s
+        return n
+
+    def element_size(self):
+        return torch.empty((), dtype=self.dtype).element_size()
+
+
+def _decode_args(B=2, R=1, Hq=8, Hkv=2, d=128, stride=64, dtype=torch.bfloat16, pages=100):
+    k = FakeTensor((pages, Hkv, 16, d), dtype, 0x100000)
+    v = FakeTensor((pages, Hkv, d, 16), dtype, 0x200000)
+    pt = FakeTensor((B, stride), torch.int32, 0x300000)
+    lens = FakeTensor((B,), torch.int32, 0x400000)
+    q = FakeTensor((B, R, Hq, d), torch.bfloat16 if dtype == torch.float8_e4m3fn else dtype, 0x500000)
+    o = FakeTensor((B, R, Hq, d), q.dtype, 0x600000)
+    return pa.make_io(q, o), pa.make_kv(k, v, pt, lens), pa.make_opts()
+
+
+@pytest.fixture(scope="module")
+def hctx(lib):
+    return pa.attn_open_host_only(256)
+
+
+def test_plan_headline_decode(hctx):
+    io, kv, op = _decode_args(B=16, R=1, Hq=32, Hkv=8, d=128, stride=1024)
+    P, T, W = pa.attn_paged_decode_plan(hctx, io, kv, op)
+    assert P * T >= 1024 * 16 and T % 128 == 0
+    assert 16 * 8 * P >= 4 * 256 or T == 256
+    assert W >= 16 * 8 * 4 * P * (128 + 2) * 4
+
+
+def test_plan_forced_splits(hctx):
+    io, kv, op = _decode_args(stride=64)
+    op.num_splits = 3
+    P, T, W = pa.attn_paged_decode_plan(hctx, io, kv, op)
+    assert P == 3 and T * 3 >= 64 * 16
+
+
+def test_plan_fp8_long_context(hctx):
+    io, kv, op = _decode_args(B=4, R=4, Hq=32, Hkv=8, d=128, stride=4096, dtype=torch.float8_e4m3fn)
+    P, T, W = pa.attn_paged_decode_plan(hctx, io, kv, op)
+    assert 4 * 8 * P >= 256 and P * T >= 65536
+
+
+def _status(fn):
+    try:
+        fn()
+    except pa.AttnError as e:
+        return e.status
+    return pa.ATTN_OK
+
+
+def test_host_only_context_never_enqueues(hctx):
+    io, kv, op = _decode_args()
+    ws = FakeTensor((1 << 24,), torch.uint8, 0x700000)
+    assert _status(lambda: pa.attn_paged_decode(hctx, io, kv, op, ws, stream=0)) == pa.ATTN_ERR_DEVICE
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda io, kv, op: setattr(io, "q_rows", 9), pa.ATTN_ERR_INVALID_ARGUMENT),
+    (lambda io, kv, op: setattr(io, "q_rows", 0), pa.ATTN_ERR_INVALID_ARGUMENT),
+    (lambda io, kv, op: setattr(io, "num_q_heads", 7), pa.ATTN_ERR_INVALID_ARGUMENT),
+    (lambda io, kv, op: setattr(io, "q", None), pa.ATTN_ERR_INVALID_ARGUMENT),
+    (lambda io, kv, op: setattr(io, "q", 0x500008), pa.ATTN_ERR_INVALID_ARGUMENT),
+    (lambda io, kv, op: setattr(kv, "k_pages", 0x100004), pa.ATTN_ERR_INVALID_ARGUMENT),
+    (lambda io, kv, op: setattr(kv, "page_table", None), pa.ATTN_ERR_INVALID_ARGUMENT),
+    (lambda io, kv, op: setattr(kv, "k_scale", 0.0), pa.ATTN_ERR_INVALID_ARGUMENT),
+    (lambda io, kv, op: setattr(kv, "k_stride_head", 100), pa.ATTN_ERR_INVALID_ARGUMENT),
+    (lambda io, kv, op: setattr(kv, "page_size", 32), pa.ATTN_ERR_UNSUPPORTED),
+    (lambda io, kv, op: setattr(kv, "head_dim", 96), pa.ATTN_ERR_UNSUPPORTED),
+    (lambda io, kv, op: setattr(io, "q_dtype", pa.ATTN_F16), pa.ATTN_ERR_UNSUPPORTED),
+    (lambda io, kv, op: setattr(op, "block_mask", 0x800000), pa.ATTN_ERR_INVALID_ARGUMENT),
+    (lambda io, kv, op: setattr(op, "num_splits", -1), pa.ATTN_ERR_INVALID_ARGUMENT),
+])
+def test_decode_validation(hctx, mutate, status):
+    io, kv, op = _decode_args()
+    mutate(io, kv, op)
+    ws = FakeTensor((1 << 24,), torch.uint8, 0x700000)
+    assert _status(lambda: pa.attn_paged_decode(hctx, io, kv, op, ws, stream=0)) == status
+
+
+def test_workspace_too_small(hctx):
+    io, kv, op = _decode_args()
+    _, _, need = pa.attn_paged_decode_plan(hctx, io, kv, op)
+    ws = FakeTensor((need - 16,), torch.uint8, 0x700000)
+    assert _status(lambda: pa.attn_paged_decode(hctx, io, kv, op, ws, stream=0)) == \
+        pa.ATTN_ERR_WORKSPACE_TOO_SMALL
+
+
+def _prefill_args(S=256, Hq=8, Hkv=2, d=64, dtype=torch.bfloat16, mask=False):
+    io, kv, _ = _decode_args(B=1, R=S, Hq=Hq, Hkv=Hkv, d=d, stride=(S + 15) // 16, dtype=dtype)
+    m = FakeTensor((1, 1, 2, 2), torch.uint8, 0x900000) if mask else None
+    return io, kv, pa.make_opts(block_mask=m)
+
+
+def test_prefill_validation(hctx):
+    io, kv, op = _prefill_args()
+    assert _status(lambda: pa.attn_prefill(hctx, io, kv, op, stream=0)) == pa.ATTN_ERR_DEVICE
+    # a mask on the dense call, none on the sparse call
+    io, kv, op = _prefill_args(mask=True)
+    assert _status(lambda: pa.attn_prefill(hctx, io, kv, op, stream=0)) == pa.ATTN_ERR_INVALID_ARGUMENT
+    assert _status(lambda: pa.attn_prefill_blocksparse(hctx, io, kv, op, stream=0)) == pa.ATTN_ERR_DEVICE
+    op.mask_block = 100
+    assert _status(lambda: pa.attn_prefill_blocksparse(hctx, io, kv, op, stream=0)) == pa.ATTN_ERR_INVALID_ARGUMENT
+    op.mask_block, op.mask_heads = 128, 3
+    assert _status(lambda: pa.attn_prefill_blocksparse(hctx, io, kv, op, stream=0)) == pa.ATTN_ERR_INVALID_ARGUMENT
+    io, kv, op = _prefill_args()
+    assert _status(lambda: pa.attn_prefill_blocksparse(hctx, io, kv, op, stream=0)) == pa.ATTN_ERR_INVALID_ARGUMENT
+    # FP32 K/V prefill is not implemented
+    io, kv, op = _prefill_args(dtype=torch.float32)
+    assert _status(lambda: pa.attn_prefill(hctx, io, kv, op, stream=0)) == pa.ATTN_ERR_UNSUPPORTED

@@ -1,0 +1,326 @@
+"""GPU parity: the HIP path through the C ABI against the FP64 oracle, element
+by element, at sizes that span several tiles/partitions and ragged tails,
+plus the invariants the pages state (page permutation, split + merge,
+all-ones mask, sink = -inf, replay determinism)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_gqa_attention_amd as pa
+import synth
+from synth import DT_BF16, DT_F16, DT_F32, DT_FP8
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from helpers import Dev, check_full, ctx, run  # noqa: E402
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------------ gather / codecs
+
+@pytest.mark.parametrize("dtype", [DT_F32, DT_F16, DT_BF16, DT_FP8])
+def test_debug_gather_bit_exact(dtype):
+    _say("gather", dtype)
+    p = synth.make_decode(61, 2, 4, 2, 64, [70, 33], 1, kv_dtype=dtype, stride=8, extra_pages=3)
+    d = Dev(p)
+    for b in range(2):
+        L = int(p.seq_lens[b])
+        ko = torch.empty((2, L, 64), dtype=torch.float32, device="cuda")
+        vo = torch.empty_like(ko)
+        kv = pa.make_kv(d.k, d.v, d.pt, d.lens, p.k_scale, p.v_scale)
+        pa.attn_debug_gather_kv(ctx(), kv, b, L, ko, vo)
+        torch.cuda.synchronize()
+        for g in range(2):
+            k, v = oracle.gather(p, b, g)
+            # FP32 products of exact codes and FP32 scales are exact in FP64
+            assert np.array_equal(ko[g].double().cpu().numpy(), k.astype(np.float32).astype(np.float64)) or \
+                np.array_equal(ko[g].double().cpu().numpy(), k)
+            assert np.array_equal(vo[g].double().cpu().numpy(), v.astype(np.float32).astype(np.float64)) or \
+                np.array_equal(vo[g].double().cpu().numpy(), v)
+
+
+def test_fp8_every_code_decodes_exactly():
+    """All 256 e4m3fn codes through the kernels' FP32 and 16-bit conversions."""
+    _say("fp8 codes")
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    k = codes.view(1, 1, 16, 16).repeat(1, 1, 1, 4).contiguous()   # 1 page, d=64
+    k = k.view(torch.float8_e4m3fn)
+    v = k.transpose(2, 3).contiguous()
+    pt = torch.zeros((1, 1), dtype=torch.int32)
+    lens = torch.tensor([16], dtype=torch.int32)
+    kd, vd, ptd, ld = k.cuda(), v.cuda(), pt.cuda(), lens.cuda()
+    kv = pa.make_kv(kd, vd, ptd, ld)
+    ko = torch.empty((1, 16, 64), dtype=torch.float32, device="cuda")
+    vo = torch.empty_like(ko)
+    pa.attn_debug_gather_kv(ctx(), kv, 0, 16, ko, vo)
+    torch.cuda.synchronize()
+    ref = oracle.decode_codes(DT_FP8, k.view(torch.uint8).numpy().reshape(-1)).reshape(16, 64)
+    got = ko[0].double().cpu().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+# ------------------------------------------------------------------ decode
+
+DECODE_CASES = [
+    # (name, kwargs)
+    ("cfg1", dict(fn="config1")),
+    ("bf16_r1_g4", dict(B=3, Hq=32, Hkv=8, d=128, lens=[1000, 37, 2100], R=1, dt=DT_BF16)),
+    ("bf16_r4_g4", dict(B=3, Hq=32, Hkv=8, d=128, lens=[1000, 37, 2100], R=4, dt=DT_BF16)),
+    ("bf16_r8_g4", dict(B=3, Hq=32, Hkv=8, d=128, lens=[1000, 37, 2100], R=8, dt=DT_BF16)),
+    ("bf16_r2_g4_sink", dict(B=2, Hq=8, Hkv=2, d=128, lens=[515, 1700], R=2, dt=DT_BF16, sinks=True)),
+    ("f16_r1_d64", dict(B=2, Hq=8, Hkv=2, d=64, lens=[300, 1029], R=1, dt=DT_F16)),
+    ("f16_r8_d64", dict(B=2, Hq=8, Hkv=2, d=64, lens=[300, 1029], R=8, dt=DT_F16, sinks=True)),
+    ("fp8_r4", dict(B=2, Hq=32, Hkv=8, d=128, lens=[1500, 777], R=4, dt=DT_FP8)),
+    ("fp8_r1", dict(B=2, Hq=32, Hkv=8, d=128, lens=[1500, 777], R=1, dt=DT_FP8, sinks=True)),
+    ("fp8_r8_d64_f16q", dict(B=2, Hq=16, Hkv=2, d=64, lens=[600, 90], R=8, dt=DT_FP8, q=DT_F16)),
+    ("f32_r1_d128", dict(B=2, Hq=8, Hkv=2, d=128, lens=[300, 700], R=1, dt=DT_F32, o=DT_F32)),
+    ("f32_r4_g4", dict(B=2, Hq=8, Hkv=2, d=64, lens=[300, 700], R=4, dt=DT_F32, o=DT_F32, sinks=True)),
+    ("f32_q_bf16", dict(B=1, Hq=4, Hkv=1, d=64, lens=[500], R=3, dt=DT_F32, q=DT_BF16, o=DT_F32)),
+    ("mha_r8", dict(B=2, Hq=4, Hkv=4, d=128, lens=[200, 400], R=8, dt=DT_BF16)),
+    ("g8_r8_64rows", dict(B=1, Hq=16, Hkv=2, d=128, lens=[1100], R=8, dt=DT_BF16)),
+    ("g3_r5_odd", dict(B=2, Hq=6, Hkv=2, d=64, lens=[77, 130], R=5, dt=DT_BF16, sinks=True)),
+    ("empty_and_short", dict(B=3, Hq=8, Hkv=2, d=128, lens=[0, 3, 50], R=4, dt=DT_BF16, sinks=True)),
+    ("empty_no_sink", dict(B=2, Hq=8, Hkv=2, d=64, lens=[0, 20], R=1, dt=DT_BF16)),
+    ("fp32_out_bf16_kv", dict(B=2, Hq=8, Hkv=2, d=128, lens=[400, 90], R=4, dt=DT_BF16, o=DT_F32)),
+]
+
+
+def _decode_problem(kw, seed=0):
+    if kw.get("fn") == "config1":
+        return synth.config1()
+    return synth.make_decode(seed or 71, kw["B"], kw["Hq"], kw["Hkv"], kw["d"], kw["lens"], kw["R"],
+                             kv_dtype=kw["dt"], q_dtype=kw.get("q"), o_dtype=kw.get("o"),
+                             sinks=kw.get("sinks", False), stride=kw.get("stride"))
+
+
+@pytest.mark.parametrize("name,kw", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_parity(name, kw):
+    _say("decode", name)
+    p = _decode_problem(kw)
+    d = Dev(p)
+    o, l = run(d)
+    check_full(p, o, l, label=name)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5, 64])
+def test_decode_forced_splits(splits):
+    """Any partition count gives the unsplit result within FP32 rounding
+    (Geramy/LSE releases, v0.4.20: split and unsplit responses identical)."""
+    _say("splits", splits)
+    p = synth.make_decode(72, 2, 8, 2, 128, [2000, 513], 4, kv_dtype=DT_BF16, o_dtype=DT_F32,
+                          sinks=True)
+    d = Dev(p)
+    o, l = run(d, num_splits=splits)
+    check_full(p, o, l, tol=2e-3, label=f"splits={splits}")
+
+
+def test_decode_page_permutation_bit_identical():
+    _say("decode permutation")
+    p = synth.make_decode(73, 2, 32, 8, 128, [900, 1333], 4, kv_dtype=DT_BF16, extra_pages=7)
+    o0, l0 = run(Dev(p))
+    perm = synth.permutation(73, 9, p.num_pages)
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(p.num_pages)
+    p.k_pool = p.k_pool[inv].contiguous()
+    p.v_pool = p.v_pool[inv].contiguous()
+    p.page_table = perm[p.page_table.long()].to(torch.int32)
+    o1, l1 = run(Dev(p))
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_decode_sink_minus_inf_bit_identical():
+    _say("decode sink -inf")
+    p = synth.make_decode(74, 2, 8, 2, 128, [400, 800], 1, kv_dtype=DT_BF16)
+    o0, l0 = run(Dev(p))
+    p.sinks = torch.full((8,), -math.inf, dtype=torch.float32)
+    o1, l1 = run(Dev(p))
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_decode_replay_deterministic():
+    _say("decode replay")
+    p = synth.make_decode(75, 3, 32, 8, 128, [3000, 100, 2000], 8, kv_dtype=DT_BF16, sinks=True)
+    d = Dev(p)
+    o0, l0 = run(d)
+    o1, l1 = run(d)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_decode_verify_row_matches_single_row_decode():
+    """Verify row r equals an R=1 decode at length L - R + r + 1 (within rounding)."""
+    _say("verify rows")
+    R = 8
+    p = synth.make_decode(76, 1, 32, 8, 128, [1000], R, kv_dtype=DT_BF16, o_dtype=DT_F32)
+    o, _ = run(Dev(p))
+    for r in [0, 3, 7]:
+        q1 = synth.make_decode(76, 1, 32, 8, 128, [1000], 1, kv_dtype=DT_BF16, o_dtype=DT_F32)
+        q1.k_pool, q1.v_pool, q1.page_table = p.k_pool, p.v_pool, p.page_table
+        q1.seq_lens = torch.tensor([1000 - R + r + 1], dtype=torch.int32)
+        q1.q = p.q[:, r:r + 1].clone()
+        o1, _ = run(Dev(q1))
+        assert np.max(np.abs(o1[0, 0] - o[0, r])) <= 2e-3
+
+
+def test_decode_buffers_untouched_outside_outputs():
+    """Guard bands around O stay intact and inputs are not modified."""
+    _say("decode guards")
+    p = synth.make_decode(77, 2, 8, 2, 128, [300, 600], 4, kv_dtype=DT_BF16)
+    d = Dev(p)
+    big = torch.full((3, 2, 4, 8, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    o = big[1]
+    before = [t.clone() for t in (d.q, d.k, d.v, d.pt, d.lens)]
+    pa.paged_decode(ctx(), d.q, d.k, d.v, d.pt, d.lens, out=o)
+    torch.cuda.synchronize()
+    assert torch.all(big[0] == 7.0) and torch.all(big[2] == 7.0)
+    for a, b in zip(before, (d.q, d.k, d.v, d.pt, d.lens)):
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.float8_e4m3fn else a,
+                           b.view(torch.uint8) if b.dtype == torch.float8_e4m3fn else b)
+    check_full(p, o.double().cpu().numpy(), None)
+
+
+def test_decode_strided_q_and_o():
+    """Q and O given through non-packed strides (a slice of a larger buffer)."""
+    _say("decode strides")
+    p = synth.make_decode(78, 2, 8, 2, 64, [300, 129], 2, kv_dtype=DT_BF16)
+    d = Dev(p)
+    qbig = torch.zeros((2, 2, 16, 64), dtype=torch.bfloat16, device="cuda")
+    qbig[:, :, 4:12] = d.q
+    obig = torch.zeros((2, 2, 16, 64), dtype=torch.bfloat16, device="cuda")
+    pa.paged_decode(ctx(), qbig[:, :, 4:12], d.k, d.v, d.pt, d.lens, out=obig[:, :, 4:12])
+    torch.cuda.synchronize()
+    check_full(p, obig[:, :, 4:12].double().cpu().numpy(), None)
+    assert torch.all(obig[:, :, :4] == 0) and torch.all(obig[:, :, 12:] == 0)
+
+
+# ------------------------------------------------------------------ prefill
+
+PREFILL_CASES = [
+    ("d64_g4_sink", dict(B=2, Hq=8, Hkv=2, d=64, S=300, sinks=True)),
+    ("d64_g8_cfg4shape", dict(B=1, Hq=64, Hkv=8, d=64, S=260, sinks=True, scale=0.125)),
+    ("d128_g4", dict(B=2, Hq=8, Hkv=2, d=128, S=200, sinks=False)),
+    ("d64_mha", dict(B=1, Hq=3, Hkv=3, d=64, S=190, sinks=True)),
+    ("d128_g3_odd", dict(B=1, Hq=6, Hkv=2, d=128, S=129, sinks=True)),
+    ("d64_f16", dict(B=1, Hq=4, Hkv=2, d=64, S=257, sinks=True, dt=DT_F16)),
+    ("d128_fp8", dict(B=1, Hq=8, Hkv=2, d=128, S=333, sinks=True, dt=DT_FP8)),
+    ("d64_chunked", dict(B=2, Hq=8, Hkv=2, d=64, S=700, q_rows=150, sinks=True)),
+    ("d64_tiny", dict(B=2, Hq=4, Hkv=2, d=64, S=5, sinks=True)),
+    ("d64_fp32_out", dict(B=1, Hq=4, Hkv=2, d=64, S=150, sinks=True, o=DT_F32)),
+]
+
+
+def _prefill_problem(kw, seed=81):
+    return synth.make_prefill(seed, kw["B"], kw["Hq"], kw["Hkv"], kw["d"], kw["S"],
+                              q_rows=kw.get("q_rows"), kv_dtype=kw.get("dt", DT_BF16),
+                              sinks=kw.get("sinks", True), softmax_scale=kw.get("scale", 0.0),
+                              o_dtype=kw.get("o"))
+
+
+@pytest.mark.parametrize("name,kw", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
+def test_prefill_parity(name, kw):
+    _say("prefill", name)
+    p = _prefill_problem(kw)
+    o, l = run(Dev(p))
+    check_full(p, o, l, label=name)
+
+
+def test_prefill_ragged_batch_lengths():
+    """Sequences of different lengths with fewer query rows than keys."""
+    _say("prefill ragged")
+    p = synth.make_prefill(82, 3, 8, 2, 64, 400, q_rows=100, lens=[400, 250, 100], sinks=True)
+    o, l = run(Dev(p))
+    check_full(p, o, l)
+
+
+def test_prefill_more_rows_than_keys_gives_empty_rows():
+    _say("prefill empty rows")
+    p = synth.make_prefill(83, 2, 4, 2, 64, 50, q_rows=80, lens=[50, 10], sinks=True)
+    o, l = run(Dev(p))
+    check_full(p, o, l)
+
+
+BS_CASES = [
+    ("d128_blk128", dict(S=1000, Hq=8, Hkv=2, d=128, blk=128, mh=1, keep=0.3)),
+    ("d64_blk64_perhead", dict(S=700, Hq=8, Hkv=2, d=64, blk=64, mh=2, keep=0.4, sinks=True)),
+    ("d64_blk256", dict(S=900, Hq=4, Hkv=2, d=64, blk=256, mh=1, keep=0.5)),
+]
+
+
+@pytest.mark.parametrize("name,kw", BS_CASES, ids=[c[0] for c in BS_CASES])
+def test_blocksparse_parity(name, kw):
+    _say("blocksparse", name)
+    p = synth.make_blocksparse(91, 1, kw["Hq"], kw["Hkv"], kw["d"], kw["S"], mask_block=kw["blk"],
+                               mask_heads=kw["mh"], keep_prob=kw["keep"], sinks=kw.get("sinks", False))
+    o, l = run(Dev(p))
+    check_full(p, o, l, label=name)
+
+
+def test_blocksparse_random_mask_with_holes():
+    """Arbitrary masks, including dropped diagonal blocks (empty rows) and
+    entries above the diagonal (ignored)."""
+    _say("blocksparse holes")
+    p = synth.make_blocksparse(92, 2, 4, 2, 64, 500, mask_block=64, mask_heads=1, sinks=True)
+    u = synth.uniform(92, 50, p.mask.numel()).view(p.mask.shape)
+    p.mask = (u < 0.5).to(torch.uint8)
+    o, l = run(Dev(p))
+    check_full(p, o, l)
+
+
+def test_all_ones_mask_bit_identical_to_dense():
+    """Skipping nothing keeps the dense arithmetic bit for bit (Geramy/LSE
+    releases, v0.4.14: contributing windows keep arithmetic and ordering)."""
+    _say("all-ones mask")
+    p = synth.make_blocksparse(93, 2, 8, 2, 128, 600, mask_block=128, sinks=True)
+    p.mask = torch.ones_like(p.mask)
+    o1, l1 = run(Dev(p))
+    p.mask = None
+    p.kind = "prefill"
+    o0, l0 = run(Dev(p))
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_prefill_sink_minus_inf_bit_identical():
+    _say("prefill sink -inf")
+    p = synth.make_prefill(94, 1, 8, 2, 64, 300, sinks=False)
+    o0, l0 = run(Dev(p))
+    p.sinks = torch.full((8,), -math.inf, dtype=torch.float32)
+    o1, l1 = run(Dev(p))
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_prefill_page_permutation_bit_identical():
+    _say("prefill permutation")
+    p = synth.make_prefill(95, 2, 8, 2, 64, 333, sinks=True)
+    o0, l0 = run(Dev(p))
+    perm = synth.permutation(95, 9, p.num_pages)
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(p.num_pages)
+    p.k_pool = p.k_pool[inv].contiguous()
+    p.v_pool = p.v_pool[inv].contiguous()
+    p.page_table = perm[p.page_table.long()].to(torch.int32)
+    o1, l1 = run(Dev(p))
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_prefill_row_matches_decode():
+    """Prefill row i equals a single-row decode at length i + 1 (rounding aside)."""
+    _say("prefill vs decode")
+    p = synth.make_prefill(96, 1, 8, 2, 128, 300, sinks=True, o_dtype=DT_F32)
+    o, _ = run(Dev(p))
+    for i in [0, 63, 64, 200, 299]:
+        q1 = synth.make_decode(96, 1, 8, 2, 128, [300], 1, kv_dtype=DT_BF16, o_dtype=DT_F32, sinks=True)
+        q1.k_pool, q1.v_pool, q1.page_table, q1.sinks = p.k_pool, p.v_pool, p.page_table, p.sinks
+        q1.seq_lens = torch.tensor([i + 1], dtype=torch.int32)
+        q1.q = p.q[:, i:i + 1].clone()
+        o1, _ = run(Dev(q1))
+        assert np.max(np.abs(o1[0, 0] - o[0, i])) <= 1e-2
