@@ -1,0 +1,296 @@
+"""Benchmark of the paged GQA attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--all]
+
+Prints ONE JSON line.  ``value`` is paged decode throughput in GB/s of
+algorithmic HBM bytes (every live K/V element once, plus Q, O and the used
+page-table entries) for the decode workload with every sequence at 16,384
+tokens: 16 sequences, 32 query heads, 8 KV heads, head_dim 128, BF16, one
+query row, page-table stride 1,024 pages.  The prefill half of the metric
+(causal attention with sinks, 16 x 8,192 tokens, 64 query / 8 KV heads,
+head_dim 64, BF16) is reported in the ``prefill`` object in TFLOP/s.
+
+Inputs are generated on the GPU with the seeded counter-based generator and
+are resident in HBM before timing.  Each timed region is K calls on one
+stream, bracketed by synchronisation, timed with HIP events on that stream.
+The FP64 CPU oracle is timed on a bounded sample of rows of the same
+workload (``cpu_baseline``).  ``--all`` also prints the other workloads to
+stderr (not part of the JSON line).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode achieved HBM GB/s @16K; causal prefill attention TFLOP/s (BF16)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 FLOP/clk (dense)
+CPU_THREADS = 16
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def _src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "paged_gqa_attention_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(key: str, src_hash: str, launches_per_call: int = 1):
+    """HBM bytes per call from committed rocprofv3 counter summaries, or None
+    when the kernel source changed since the counters were taken."""
+    path = os.path.join(PROFILES, "hbm_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get(key)
+    if not rec or rec.get("src_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_call")
+
+
+def time_calls(fn, steps: int, warmup: int):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps   # ms per call
+
+
+def decode_setup(ctx, p, dev="cuda", num_splits=0):
+    import torch
+    import paged_gqa_attention_amd as pa
+    q = p.q.to(dev)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    io = pa.make_io(q, o)
+    kv = pa.make_kv(p.k_pool.to(dev), p.v_pool.to(dev), p.page_table.to(dev),
+                    p.seq_lens.to(dev), p.k_scale, p.v_scale)
+    op = pa.make_opts(p.softmax_scale, None if p.sinks is None else p.sinks.to(dev),
+                      None, 128, num_splits)
+    P, T, W = pa.attn_paged_decode_plan(ctx, io, kv, op)
+    ws = torch.empty(max(W, 16), dtype=torch.uint8, device=dev)
+    call = lambda: pa.attn_paged_decode(ctx, io, kv, op, ws)
+    return call, (P, T), (io, kv, op, ws)
+
+
+def prefill_setup(ctx, p, dev="cuda"):
+    import torch
+    import paged_gqa_attention_amd as pa
+    q = p.q.to(dev)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    io = pa.make_io(q, o)
+    kv = pa.make_kv(p.k_pool.to(dev), p.v_pool.to(dev), p.page_table.to(dev),
+                    p.seq_lens.to(dev), p.k_scale, p.v_scale)
+    mask = None if p.mask is None else p.mask.to(dev)
+    op = pa.make_opts(p.softmax_scale, None if p.sinks is None else p.sinks.to(dev), mask,
+                      p.mask_block)
+    fn = pa.attn_prefill if mask is None else pa.attn_prefill_blocksparse
+    return (lambda: fn(ctx, io, kv, op)), (io, kv, op)
+
+
+def cpu_baseline_decode(p, budget_s: float = 12.0):
+    """Oracle on a bounded sample of rows, scaled to GB/s of the same workload."""
+    import numpy as np
+    import oracle
+    from paged_gqa_attention_amd import accounting as acc
+    op = oracle.OracleProblem(p)
+    rows_all = op.all_rows()
+    g = np.random.default_rng(0)
+    # calibrate on a few rows, then size the sample to the time budget
+    n = CPU_THREADS
+    sel = rows_all[g.choice(len(rows_all), n, replace=False)]
+    t0 = time.perf_counter()
+    _, _, used = oracle.attend(op, sel, threads=CPU_THREADS)
+    dt = time.perf_counter() - t0
+    n2 = int(min(len(rows_all), max(n, n * budget_s / max(dt, 1e-3))))
+    sel = rows_all[g.choice(len(rows_all), n2, replace=False)]
+    t0 = time.perf_counter()
+    _, _, used = oracle.attend(op, sel, threads=CPU_THREADS)
+    dt = time.perf_counter() - t0
+    total = acc.decode_bytes(p.seq_lens.tolist(), p.q_rows, p.num_q_heads, p.num_kv_heads,
+                             p.head_dim, p.kv_dtype, p.q_dtype, p.o_dtype)
+    gbs = total * (n2 / len(rows_all)) / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(used), "kind": "oracle",
+            "sample": f"{n2} of {len(rows_all)} output rows (random, seed 0), {dt:.1f} s; "
+                      f"bytes scaled by the sampled fraction of rows"}
+
+
+def cpu_baseline_prefill(p, budget_s: float = 8.0):
+    import numpy as np
+    import oracle
+    from paged_gqa_attention_amd import accounting as acc
+    op = oracle.OracleProblem(p)
+    g = np.random.default_rng(1)
+    B, S, H = p.batch, p.q_rows, p.num_q_heads
+
+    def pick(n):
+        return np.stack([g.integers(0, B, n), g.integers(0, S, n), g.integers(0, H, n)],
+                        axis=1).astype(np.int32)
+
+    sel = pick(CPU_THREADS * 4)
+    t0 = time.perf_counter()
+    oracle.attend(op, sel, threads=CPU_THREADS)
+    dt = time.perf_counter() - t0
+    n2 = int(max(len(sel), len(sel) * budget_s / max(dt, 1e-3)))
+    sel = pick(n2)
+    t0 = time.perf_counter()
+    _, _, used = oracle.attend(op, sel, threads=CPU_THREADS)
+    dt = time.perf_counter() - t0
+    # flops of the sampled rows: row i of a sequence of length L sees L - S + i + 1 keys
+    keys = sum(int(p.seq_lens[b]) - S + int(i) + 1 for b, i, _ in sel)
+    flops = 4 * p.head_dim * keys
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(used),
+            "kind": "oracle", "sample": f"{n2} random output rows, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--all", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path; "
+              "a sharded deployment runs one copy per GPU on its share of the heads.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_gqa_attention_amd as pa
+    import synth
+    from paged_gqa_attention_amd import accounting as acc
+
+    torch.manual_seed(0)
+    dev = "cuda"
+    ctx = pa.attn_open(0)
+
+    # ---------------- decode @16K (the headline) ----------------
+    t_gen = time.perf_counter()
+    p = synth.config2(q_rows=1, lens=[16384] * 16, device=dev)
+    call, (P, T), keep = decode_setup(ctx, p, dev)
+    gen_s = time.perf_counter() - t_gen
+    ms = time_calls(call, args.steps, args.warmup)
+    nbytes = acc.decode_bytes(p.seq_lens.tolist(), 1, 32, 8, 128, synth.DT_BF16,
+                              synth.DT_BF16, synth.DT_BF16)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    dec_hash = _src_hash("decode.hip", "common.h")
+    traffic = _traffic("decode_bf16_16k", dec_hash)
+    roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "decode_valu<bf16,bf16,128,4> + decode_merge (one attn_paged_decode call)",
+            "bytes_per_call": nbytes}
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline_decode(p)   # the oracle copies the inputs to host memory
+    del keep, call, p
+    torch.cuda.empty_cache()
+
+    # ---------------- prefill 8K x 16 ----------------
+    pp = synth.config4(seq_len=8192, batch=16, device=dev)
+    pcall, pkeep = prefill_setup(ctx, pp, dev)
+    psteps = max(3, args.steps // 2)
+    pms = time_calls(pcall, psteps, max(1, args.warmup // 2))
+    flops = acc.attention_flops(acc.causal_pairs(8192, 8192), 64, 64, 16)
+    tfs = flops / (pms * 1e-3) / 1e12
+    pre_hash = _src_hash("prefill.hip", "common.h")
+    prefill = {
+        "metric": "causal prefill attention TFLOP/s (BF16)", "value": round(tfs, 1),
+        "unit": "TFLOP/s", "ms_per_step": round(pms, 4), "steps": psteps,
+        "config": {"workload": "causal prefill + sinks, B=16, S=8192, Hq=64, Hkv=8, d=64, bf16",
+                   "flops_per_call": flops},
+        "roofline": {"bound": "mfma", "achieved": round(tfs, 1), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tfs / BF16_PEAK_TFLOPS, 4),
+                     "traffic": _traffic("prefill_bf16_8k_b16", pre_hash),
+                     "kernel": "prefill_mfma<bf16,bf16,64,2,false>"},
+    }
+    if not args.no_cpu:
+        prefill["cpu_baseline"] = cpu_baseline_prefill(pp)
+    del pkeep, pcall, pp
+    torch.cuda.empty_cache()
+
+    line = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "paged decode, B=16, Hq=32, Hkv=8, d=128, 16,384 tokens each, "
+                               "bf16 K/V, 1 query row, page-table stride 1024",
+                   "num_splits": P, "tokens_per_split": T, "bytes_per_call": nbytes,
+                   "input_gen_s": round(gen_s, 2)},
+        "roofline": roof, "cpu_baseline": cpu, "prefill": prefill,
+    }
+    if args.all:
+        extra(ctx, args)
+    print(json.dumps(line), flush=True)
+
+
+def extra(ctx, args):
+    """The other workloads, printed to stderr as one JSON object per line."""
+    import torch
+    import synth
+    from paged_gqa_attention_amd import accounting as acc
+    dev = "cuda"
+    for R in (1, 4, 8):
+        p = synth.config2(q_rows=R, device=dev)
+        call, (P, T), keep = decode_setup(ctx, p, dev)
+        ms = time_calls(call, args.steps, args.warmup)
+        b = acc.decode_bytes(p.seq_lens.tolist(), R, 32, 8, 128, 2, 2, 2)
+        print(json.dumps({"workload": f"decode/verify B=16 L~U[8K,16K] R={R}", "ms": round(ms, 4),
+                          "GB/s": round(b / ms / 1e6, 1), "splits": P}), file=sys.stderr, flush=True)
+        del keep, call, p
+    p = synth.config3(device=dev)
+    call, (P, T), keep = decode_setup(ctx, p, dev)
+    ms = time_calls(call, args.steps, args.warmup)
+    b = acc.decode_bytes(p.seq_lens.tolist(), 4, 32, 8, 128, 3, 2, 2)
+    print(json.dumps({"workload": "fp8 decode B=4 L=65536 R=4", "ms": round(ms, 4),
+                      "GB/s": round(b / ms / 1e6, 1), "splits": P}), file=sys.stderr, flush=True)
+    del keep, call, p
+    torch.cuda.empty_cache()
+    for S in (1024, 4096, 8192):
+        for B in (1, 4, 16):
+            p = synth.config4(seq_len=S, batch=B, device=dev)
+            call, keep = prefill_setup(ctx, p, dev)
+            ms = time_calls(call, max(3, args.steps // 2), 2)
+            f = acc.attention_flops(acc.causal_pairs(S, S), 64, 64, B)
+            print(json.dumps({"workload": f"prefill+sinks S={S} B={B}", "ms": round(ms, 4),
+                              "TFLOP/s": round(f / ms / 1e9, 1)}), file=sys.stderr, flush=True)
+            del keep, call, p
+            torch.cuda.empty_cache()
+    p = synth.config5(device=dev)
+    call, keep = prefill_setup(ctx, p, dev)
+    ms = time_calls(call, max(3, args.steps // 2), 2)
+    m = p.mask[0, 0].cpu()
+    rows = [m[qb].nonzero().flatten().tolist() for qb in range(m.shape[0])]
+    pairs = acc.mask_pairs(rows, 32768, 128)
+    f = acc.attention_flops(pairs, 32, 128, 1)
+    p.mask = None
+    dcall, dkeep = prefill_setup(ctx, p, dev)
+    dms = time_calls(dcall, 3, 1)
+    print(json.dumps({"workload": "blocksparse prefill S=32768 (kept pairs)", "ms": round(ms, 4),
+                      "TFLOP/s": round(f / ms / 1e9, 1), "dense_ms": round(dms, 4),
+                      "kept_fraction_of_causal": round(pairs / acc.causal_pairs(32768, 32768), 4)}),
+          file=sys.stderr, flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -184,8 +184,8 @@ def test_decode_buffers_untouched_outside_outputs():
     torch.cuda.synchronize()
     assert torch.all(big[0] == 7.0) and torch.all(big[2] == 7.0)
     for a, b in zip(before, (d.q, d.k, d.v, d.pt, d.lens)):
-        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.float8_e4m3fn else a,
-                           b.view(torch.uint8) if b.dtype == torch.float8_e4m3fn else b)
+        # compare bytes: the pools hold NaN in slots past each sequence's end
+        assert torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
     check_full(p, o.double().cpu().numpy(), None)
 
 
