@@ -143,6 +143,26 @@ __device__ __forceinline__ float shfl_xor(float v, int m) {
   return __uint_as_float(__builtin_amdgcn_ds_bpermute((lane ^ m) << 2, __float_as_uint(v)));
 }
 
+// Reductions across the two 32-lane halves / the 16-lane quarters of a wave.
+// v_permlane32_swap(x, x) returns (x[0:32], x[0:32]) and (x[32:64], x[32:64]);
+// combining the two gives the pairwise result in every lane (gfx950).
+__device__ __forceinline__ float max_xor32(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float max3(float a, float b, float c) {

@@ -57,28 +57,27 @@ struct Cfg {
 }  // namespace
 
 template <int KVDT, int QDT, int D, int HPW, bool MASK>
-__global__ __launch_bounds__(HPW * 128) void prefill_mfma(PrefillArgs a) {
+__global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
   constexpr int ELT = DtInfo<KVDT>::bytes;
   constexpr bool F16 = Cfg<KVDT, QDT>::f16;
-  constexpr int NT = HPW * 128;         // threads
+  constexpr int NW = HPW * 4;           // waves: 4 per query head, 32 rows each
+  constexpr int NT = NW * 64;           // threads
   constexpr int KS = D / 16;            // 16-wide d steps of QK^T
   constexpr int DB = D / 32;            // 32-row value blocks of PV
   constexpr int KSTR = D + 8;           // K LDS row stride (16-bit elements)
   constexpr int VSTR = kTileK + 8;      // V^T LDS row stride
   constexpr int KBUF = kTileK * KSTR;
   constexpr int VBUF = D * VSTR;
-  // global chunks (16 bytes of stored dtype) per tile, and per thread
-  constexpr int KCH = kTileK * D * ELT / 16;
-  constexpr int VCH = KCH;
+  constexpr int CPK = D * ELT / 16;     // 16-byte chunks per stored K row
+  constexpr int KCH = kTileK * CPK;     // chunks per K tile (= per V tile)
   constexpr int KPT = (KCH + NT - 1) / NT;
-  constexpr int VPT = (VCH + NT - 1) / NT;
   constexpr int EPC = 16 / ELT;         // stored elements per chunk
   constexpr int LIST = 1024;            // tiles per mask window
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KBUF];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][VBUF];
   __shared__ int tile_list[MASK ? LIST : 1];
-  __shared__ int list_count[MASK ? NT / 64 + 1 : 1];
+  __shared__ int list_count[MASK ? NW : 1];
 
   // ---- task of this workgroup ----
   const int wpt = a.G / HPW;  // workgroups per task
@@ -95,53 +94,43 @@ __global__ __launch_bounds__(HPW * 128) void prefill_mfma(PrefillArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = kvh * a.G + hp * HPW + (wave >> 1);
-  const int q0 = qt * kTileQ + (wave & 1) * 64;  // first row of this wave
+  const int h = kvh * a.G + hp * HPW + (wave >> 2);
+  const int q0 = qt * kTileQ + (wave & 3) * 32;  // first row of this wave
   const int L = min(a.lens[b], a.capacity);
   const int off = L - a.n_q;                      // position of row i is off + i
   const int nl = lane & 31, hh = lane >> 5;
+  const int npages = (L + kPage - 1) / kPage;
 
-  // rows of the whole tile and of this wave
   const int tile_last = min(qt * kTileQ + kTileQ, a.n_q) - 1;
-  const int wave_last = min(q0 + 64, a.n_q) - 1;
+  const int wave_last = min(q0 + 32, a.n_q) - 1;
   const bool wave_has_rows = q0 < a.n_q;
-  const int key_end = min(L, off + tile_last + 1);  // keys the tile can see
-  // key_end <= 0: no key is visible to any row, the rows are empty (o = 0, lse = sink)
+  const int key_end = min(L, off + tile_last + 1);  // keys any row of the tile can see
   const int nt = key_end > 0 ? (key_end + kTileK - 1) / kTileK : 0;
   const int wave_key_end = wave_has_rows ? min(L, off + wave_last + 1) : 0;
   const int wave_first_pos = off + q0;
+  const int row = q0 + nl;
+  const int pos_row = row < a.n_q ? off + row : -1;
 
-  // ---- Q^T fragments: B[k = d][n = row], lane (row nl (+32 nb), k half hh) ----
-  u32x4 qf[2][KS];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int i = q0 + 32 * nb + nl;
-    const bool ok = i < a.n_q;
+  // ---- Q^T fragments: B[k = d][n = row]; lane (row nl, k half hh) ----
+  u32x4 qf[KS];
+  {
+    const bool ok = row < a.n_q;
     const char *qrow = reinterpret_cast<const char *>(a.q) +
-                       ((int64_t)b * a.q_sb + (int64_t)(ok ? i : 0) * a.q_sr +
+                       ((int64_t)b * a.q_sb + (int64_t)(ok ? row : 0) * a.q_sr +
                         (int64_t)h * a.q_sh) * 2;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4 v = ld16(qrow + (16 * ks + 8 * hh) * 2);
-      qf[nb][ks] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 v = ld16(qrow + (16 * ks + 8 * hh) * 2);
+      qf[ks] = ok ? v : u32x4{0u, 0u, 0u, 0u};
     }
   }
 
-  f32x16 oacc[DB][2];
+  f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][nb][i] = 0.f;
-  float m_run[2] = {kNegInf, kNegInf};
-  float l_run[2] = {0.f, 0.f};
-  int pos_row[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int i = q0 + 32 * nb + nl;
-    pos_row[nb] = i < a.n_q ? off + i : -1;
-  }
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m_run = kNegInf, l_run = 0.f;
 
   const int32_t *pt = a.page_table + (int64_t)b * a.pt_stride;
   const char *kbase = reinterpret_cast<const char *>(a.k) + (int64_t)kvh * a.k_sh * ELT;
@@ -151,30 +140,25 @@ __global__ __launch_bounds__(HPW * 128) void prefill_mfma(PrefillArgs a) {
                                           (int64_t)a.mask_nqb * a.mask_nkb
                              : nullptr;
 
-  // ---- staging: global -> registers -> LDS ----
-  u32x4 kreg[KPT], vreg[VPT];
+  // ---- staging: global -> registers -> LDS.  The 4 page ids of a tile are
+  // workgroup-uniform scalar loads; then every thread issues its 16-byte loads.
+  u32x4 kreg[KPT], vreg[KPT];
   auto gload = [&](int t) {
-    const int kbase_tok = t * kTileK;
+    t = __builtin_amdgcn_readfirstlane(t);
+    int64_t pid[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pid[k] = pt[min(4 * t + k, npages - 1)];
 #pragma unroll
     for (int c = 0; c < KPT; ++c) {
       const int ch = tid + c * NT;
-      if (ch < KCH) {
-        const int key = ch / (D * ELT / 16);
-        const int part = ch % (D * ELT / 16);
-        const int tok = kbase_tok + key;
-        const int64_t pid = pt[min(tok, L - 1) >> 4];  // keys past the end: masked later
-        kreg[c] = ld16(kbase + (pid * a.k_sp + (tok & 15) * D + part * EPC) * ELT);
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < VPT; ++c) {
-      const int ch = tid + c * NT;
-      if (ch < VCH) {
-        const int pg = ch / (D * ELT);
-        const int cc = ch % (D * ELT);
-        const int tok0 = kbase_tok + 16 * pg;
-        const int64_t pid = pt[min(tok0, L - 1) >> 4];
-        vreg[c] = ld16(vbase + (pid * a.v_sp + (int64_t)cc * EPC) * ELT);
+      if (KCH % NT == 0 || ch < KCH) {
+        const int key = ch / CPK, part = ch % CPK;
+        const int pg = key >> 4;
+        const int64_t p = pg == 0 ? pid[0] : pg == 1 ? pid[1] : pg == 2 ? pid[2] : pid[3];
+        kreg[c] = ld16(kbase + (p * a.k_sp + (key & 15) * D + part * EPC) * ELT);
+        const int vpg = ch / (D * ELT), cc = ch % (D * ELT);
+        const int64_t pv = vpg == 0 ? pid[0] : vpg == 1 ? pid[1] : vpg == 2 ? pid[2] : pid[3];
+        vreg[c] = ld16(vbase + (pv * a.v_sp + (int64_t)cc * EPC) * ELT);
       }
     }
   };
@@ -183,62 +167,59 @@ __global__ __launch_bounds__(HPW * 128) void prefill_mfma(PrefillArgs a) {
 #pragma unroll
     for (int c = 0; c < KPT; ++c) {
       const int ch = tid + c * NT;
-      if (ch < KCH) {
-        const int key = ch / (D * ELT / 16);
-        const int part = ch % (D * ELT / 16);
-        const int row = (key & ~31) | kperm(key & 31);
-        uint16_t *dst = &k_lds[buf][row * KSTR + part * EPC];
+      if (KCH % NT == 0 || ch < KCH) {
+        const int key = ch / CPK, part = ch % CPK;
+        const int krow = (key & ~31) | kperm(key & 31);
+        uint16_t *kdst = &k_lds[buf][krow * KSTR + part * EPC];
+        const int vpg = ch / (D * ELT), cc = ch % (D * ELT);
+        const int d = cc / ELT, tg = cc % ELT;          // value row, token group
+        const int tok0 = kbase_tok + 16 * vpg + tg * EPC;
+        uint16_t *vdst = &v_lds[buf][d * VSTR + 16 * vpg + tg * EPC];
         if constexpr (KVDT == DT_FP8) {
-          u32x4 lo, hi;
+          u32x4 lo, hi, v0, v1;
 #pragma unroll
           for (int w = 0; w < 2; ++w) {
             lo[2 * w] = fp8x2_to_16<F16, false>(kreg[c][w]);
             lo[2 * w + 1] = fp8x2_to_16<F16, true>(kreg[c][w]);
             hi[2 * w] = fp8x2_to_16<F16, false>(kreg[c][w + 2]);
             hi[2 * w + 1] = fp8x2_to_16<F16, true>(kreg[c][w + 2]);
+            v0[2 * w] = fp8x2_to_16<F16, false>(vreg[c][w]);
+            v0[2 * w + 1] = fp8x2_to_16<F16, true>(vreg[c][w]);
+            v1[2 * w] = fp8x2_to_16<F16, false>(vreg[c][w + 2]);
+            v1[2 * w + 1] = fp8x2_to_16<F16, true>(vreg[c][w + 2]);
           }
-          *reinterpret_cast<u32x4 *>(dst) = lo;
-          *reinterpret_cast<u32x4 *>(dst + 8) = hi;
-        } else {
-          *reinterpret_cast<u32x4 *>(dst) = kreg[c];
-        }
-      }
-    }
+          *reinterpret_cast<u32x4 *>(kdst) = lo;
+          *reinterpret_cast<u32x4 *>(kdst + 8) = hi;
+          u32x4 vv[2] = {v0, v1};
+          if (tok0 + EPC > L) {  // slots at or past the end may hold anything: zero them
 #pragma unroll
-    for (int c = 0; c < VPT; ++c) {
-      const int ch = tid + c * NT;
-      if (ch < VCH) {
-        const int pg = ch / (D * ELT);
-        const int cc = ch % (D * ELT);
-        const int d = cc / ELT;               // value row
-        const int tg = cc % ELT;              // token group within the page row
-        const int tok0 = kbase_tok + 16 * pg + tg * EPC;
-        uint16_t *dst = &v_lds[buf][d * VSTR + 16 * pg + tg * EPC];
-        u32x4 w16[EPC / 8];
-        if constexpr (KVDT == DT_FP8) {
+            for (int q = 0; q < 2; ++q)
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            w16[w >> 1][2 * (w & 1)] = fp8x2_to_16<F16, false>(vreg[c][w]);
-            w16[w >> 1][2 * (w & 1) + 1] = fp8x2_to_16<F16, true>(vreg[c][w]);
+              for (int e = 0; e < 4; ++e) {
+                const int tk = tok0 + 8 * q + 2 * e;
+                uint32_t wv = vv[q][e];
+                if (tk >= L) wv &= 0xffff0000u;
+                if (tk + 1 >= L) wv &= 0x0000ffffu;
+                vv[q][e] = wv;
+              }
           }
+          *reinterpret_cast<u32x4 *>(vdst) = vv[0];
+          *reinterpret_cast<u32x4 *>(vdst + 8) = vv[1];
         } else {
-          w16[0] = vreg[c];
-        }
-        // zero slots at or past the end of the sequence (they may hold NaN)
-        if (tok0 + EPC > L) {
-#pragma unroll
-          for (int q = 0; q < EPC / 8; ++q)
+          *reinterpret_cast<u32x4 *>(kdst) = kreg[c];
+          u32x4 vv = vreg[c];
+          if (tok0 + EPC > L) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int tk = tok0 + 8 * q + 2 * e;
-              uint32_t wv = w16[q][e];
+              const int tk = tok0 + 2 * e;
+              uint32_t wv = vv[e];
               if (tk >= L) wv &= 0xffff0000u;
               if (tk + 1 >= L) wv &= 0x0000ffffu;
-              w16[q][e] = wv;
+              vv[e] = wv;
             }
+          }
+          *reinterpret_cast<u32x4 *>(vdst) = vv;
         }
-#pragma unroll
-        for (int q = 0; q < EPC / 8; ++q) *reinterpret_cast<u32x4 *>(dst + 8 * q) = w16[q];
       }
     }
   };
@@ -248,102 +229,84 @@ __global__ __launch_bounds__(HPW * 128) void prefill_mfma(PrefillArgs a) {
   auto compute = [&](int t, int buf) {
     const int kt0 = t * kTileK;
     if (!wave_has_rows || kt0 >= wave_key_end) return;
-    bool keep_row[2] = {true, true};
+    bool keep = true;
     if constexpr (MASK) {
-      const int kb = kt0 / a.mask_block;
-      bool any = false;
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int pr = pos_row[nb];
-        bool k = false;
-        if (pr >= 0) {
-          const int qb = pr / a.mask_block;
-          k = qb < a.mask_nqb && kb < a.mask_nkb && mrow[(int64_t)qb * a.mask_nkb + kb] != 0;
-        }
-        keep_row[nb] = k;
-        any |= k;
+      keep = false;
+      if (pos_row >= 0) {
+        const int qb = pos_row / a.mask_block, kb = kt0 / a.mask_block;
+        keep = qb < a.mask_nqb && kb < a.mask_nkb && mrow[(int64_t)qb * a.mask_nkb + kb] != 0;
       }
-      if (!__builtin_amdgcn_ballot_w64(any)) return;
+      if (!__builtin_amdgcn_ballot_w64(keep)) return;
     }
-    const bool diag = (kt0 + kTileK - 1 > wave_first_pos) || (kt0 + kTileK > L);
     const uint16_t *kl = k_lds[buf];
     const uint16_t *vl = v_lds[buf];
 
-    // S^T[mb][nb]: keys 32mb + kperm(m), rows 32nb + nl
-    f32x16 s[2][2];
+    // S^T[mb]: keys 32mb + kperm(m) of the tile, rows nl
+    f32x16 s[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[mb][nb][i] = 0.f;
+      for (int i = 0; i < 16; ++i) s[mb][i] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const u32x4 ka = *reinterpret_cast<const u32x4 *>(kl + (32 * mb + nl) * KSTR + 16 * ks + 8 * hh);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) s[mb][nb] = mfma32(ka, qf[nb][ks], s[mb][nb], F16);
+        s[mb] = mfma32(ka, qf[ks], s[mb], F16);
       }
     }
 
-    // softmax, rows 32nb + nl; lane half hh holds keys 32mb + 16g' + 8hh + 4(g&1) + i'
-    u32x4 pf[2][2][2];  // [mb][kk][nb]: P^T fragment, keys 32mb + 16kk + 8hh .. +8
-    float alpha[2];
-    bool need_rescale = false;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      float x[32];
+    // masking only where a tile reaches past some row's position (or a row drops the tile)
+    const bool diag = (kt0 + kTileK - 1 > wave_first_pos) || (kt0 + kTileK > L);
+    bool need_mask = diag;
+    if constexpr (MASK) need_mask = need_mask || __builtin_amdgcn_ballot_w64(!keep) != 0;
+    if (need_mask) {
+      const int lim = keep ? min(pos_row, L - 1) : -1;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float v = s[mb][nb][i] * sc;
-          if (diag || MASK) {
-            const int key = kt0 + 32 * mb + 16 * (i >> 3) + 8 * hh + 4 * ((i >> 2) & 1) + (i & 3);
-            const bool ok = key <= pos_row[nb] && key < L && keep_row[nb];
-            v = ok ? v : kNegInf;
-          }
-          x[16 * mb + i] = v;
+          const int key = kt0 + 32 * mb + 16 * (i >> 3) + 8 * hh + 4 * ((i >> 2) & 1) + (i & 3);
+          s[mb][i] = key <= lim ? s[mb][i] : kNegInf;
         }
-      float mx = x[0];
-#pragma unroll
-      for (int e = 1; e + 1 < 32; e += 2) mx = max3(mx, x[e], x[e + 1]);
-      mx = __builtin_fmaxf(mx, x[31]);
-      mx = __builtin_fmaxf(mx, shfl_xor(mx, 32));
-      const float m_old = m_run[nb];
-      const bool grow = mx > m_old + kLazy;
-      const float m_new = grow ? mx : m_old;
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      alpha[nb] = grow ? fast_exp2(m_old - m_use) : 1.0f;
-      need_rescale |= grow;
-      m_run[nb] = m_new;
-      float lsum = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          u32x4 f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0 = fast_exp2(x[16 * mb + 8 * kk + 2 * e] - m_use);
-            const float p1 = fast_exp2(x[16 * mb + 8 * kk + 2 * e + 1] - m_use);
-            const uint32_t w = F16 ? pack_f16x2(p0, p1) : pack_bf16x2(p0, p1);
-            f[e] = w;
-            lsum = F16 ? dot2_f16(w, 0x3C003C00u, lsum) : dot2_bf16(w, 0x3F803F80u, lsum);
-          }
-          pf[mb][kk][nb] = f;
-        }
-      l_run[nb] = l_run[nb] * alpha[nb] + lsum;
-    }
-    if (__builtin_amdgcn_ballot_w64(need_rescale)) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) oacc[db][nb] *= alpha[nb];
     }
 
-    // O^T[db][nb] += V^T[32 rows, 16 keys] P^T[16 keys, 32 rows]
+    // online softmax (lazy rescaling) for row nl; the two lane halves hold
+    // keys 16g' + 8hh + ... of each 32-key block
+    float mx = kNegInf;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) mx = max3(mx, s[mb][i], s[mb][i + 1]);
+    mx = max_xor32(mx);
+    const float mxs = mx * sc;
+    const bool grow = mxs > m_run + kLazy;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? mxs : m_run;
+      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+    float lsum = 0.f;
+    u32x4 pf[2][2];   // [mb][kk]: P^T fragment, keys 32mb + 16kk + 8hh .. +8
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(__builtin_fmaf(s[mb][8 * kk + 2 * e], sc, -m_use));
+          const float p1 = fast_exp2(__builtin_fmaf(s[mb][8 * kk + 2 * e + 1], sc, -m_use));
+          const uint32_t w = F16 ? pack_f16x2(p0, p1) : pack_bf16x2(p0, p1);
+          pf[mb][kk][e] = w;
+          lsum = F16 ? dot2_f16(w, 0x3C003C00u, lsum) : dot2_bf16(w, 0x3F803F80u, lsum);
+        }
+    l_run += lsum;
+
+    // O^T[db] += V^T[32 rows, 16 keys] P^T[16 keys, 32 rows]
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -351,12 +314,11 @@ __global__ __launch_bounds__(HPW * 128) void prefill_mfma(PrefillArgs a) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const u32x4 va = *reinterpret_cast<const u32x4 *>(vl + (32 * db + nl) * VSTR + 32 * mb + 16 * kk + 8 * hh);
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) oacc[db][nb] = mfma32(va, pf[mb][kk][nb], oacc[db][nb], F16);
+          oacc[db] = mfma32(va, pf[mb][kk], oacc[db], F16);
         }
   };
 
-  // ---- tile loop ----
+  // ---- tile loop (double-buffered LDS, one barrier per tile) ----
   if (nt > 0) {
     if constexpr (!MASK) {
       gload(0);
@@ -380,22 +342,22 @@ __global__ __launch_bounds__(HPW * 128) void prefill_mfma(PrefillArgs a) {
         int base = 0;
         for (int c0 = 0; c0 < wn; c0 += NT) {
           const int t = w0 + c0 + tid;
-          bool keep = false;
+          bool kept = false;
           if (c0 + tid < wn) {
             const int kb = (t * kTileK) / a.mask_block;
-            for (int qb = qb_lo; qb <= qb_hi && !keep; ++qb)
-              keep = qb < a.mask_nqb && kb < a.mask_nkb && kb <= qb &&
+            for (int qb = qb_lo; qb <= qb_hi && !kept; ++qb)
+              kept = qb < a.mask_nqb && kb < a.mask_nkb && kb <= qb &&
                      mrow[(int64_t)qb * a.mask_nkb + kb] != 0;
           }
-          const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+          const uint64_t bal = __builtin_amdgcn_ballot_w64(kept);
           const int below = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
           if (lane == 0) list_count[wave] = __builtin_popcountll(bal);
           __syncthreads();
           int wbase = base;
           for (int w = 0; w < wave; ++w) wbase += list_count[w];
-          if (keep) tile_list[wbase + below] = t;
+          if (kept) tile_list[wbase + below] = t;
           int tot = 0;
-          for (int w = 0; w < NT / 64; ++w) tot += list_count[w];
+          for (int w = 0; w < NW; ++w) tot += list_count[w];
           __syncthreads();
           base += tot;
         }
@@ -406,9 +368,9 @@ __global__ __launch_bounds__(HPW * 128) void prefill_mfma(PrefillArgs a) {
         __syncthreads();
         for (int idx = 0; idx < cnt; ++idx) {
           const int buf = idx & 1;
-          const int t = tile_list[idx];
+          const int t = __builtin_amdgcn_readfirstlane(tile_list[idx]);
           const bool more = idx + 1 < cnt;
-          const int tn = more ? tile_list[idx + 1] : 0;
+          const int tn = more ? __builtin_amdgcn_readfirstlane(tile_list[idx + 1]) : 0;
           if (more) gload(tn);
           compute(t, buf);
           if (more) lstore(tn, buf ^ 1);
@@ -421,43 +383,38 @@ __global__ __launch_bounds__(HPW * 128) void prefill_mfma(PrefillArgs a) {
   // ---- epilogue: sink, normalisation, output ----
   if (!wave_has_rows) return;
   const float sink = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
-  char *obase = reinterpret_cast<char *>(a.o);
+  const float l = sum_xor32(l_run);
+  const float M = __builtin_fmaxf(m_run, sink);
+  float scale_o = 0.f, lse = kNegInf;
+  if (M != kNegInf) {
+    const float em = fast_exp2(m_run - M);
+    const float Z = l * em + fast_exp2(sink - M);
+    scale_o = em * a.v_scale / Z;
+    lse = (M + __builtin_log2f(Z)) * kLn2;
+  }
+  if (row < a.n_q) {
+    char *obase = reinterpret_cast<char *>(a.o);
+    const int64_t orow = (int64_t)b * a.o_sb + (int64_t)row * a.o_sr + (int64_t)h * a.o_sh;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const float l = l_run[nb] + shfl_xor(l_run[nb], 32);
-    const float m = m_run[nb];
-    const float M = __builtin_fmaxf(m, sink);
-    float scale_o = 0.f, lse = kNegInf;
-    if (M != kNegInf) {
-      const float em = fast_exp2(m - M);
-      const float Z = l * em + fast_exp2(sink - M);
-      scale_o = em * a.v_scale / Z;
-      lse = (M + __builtin_log2f(Z)) * kLn2;
-    }
-    const int i = q0 + 32 * nb + nl;
-    if (i < a.n_q) {
-      const int64_t orow = (int64_t)b * a.o_sb + (int64_t)i * a.o_sr + (int64_t)h * a.o_sh;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = 32 * db + 8 * g + 4 * hh;
-          const float v0 = oacc[db][nb][4 * g + 0] * scale_o;
-          const float v1 = oacc[db][nb][4 * g + 1] * scale_o;
-          const float v2 = oacc[db][nb][4 * g + 2] * scale_o;
-          const float v3 = oacc[db][nb][4 * g + 3] * scale_o;
-          if (a.o_dtype == DT_BF16) {
-            u32x2 w = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-            *reinterpret_cast<u32x2 *>(obase + (orow + d0) * 2) = w;
-          } else if (a.o_dtype == DT_F16) {
-            u32x2 w = {pack_f16x2(v0, v1), pack_f16x2(v2, v3)};
-            *reinterpret_cast<u32x2 *>(obase + (orow + d0) * 2) = w;
-          } else {
-            *reinterpret_cast<f32x4 *>(obase + (orow + d0) * 4) = f32x4{v0, v1, v2, v3};
-          }
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * hh;
+        const float v0 = oacc[db][4 * g + 0] * scale_o;
+        const float v1 = oacc[db][4 * g + 1] * scale_o;
+        const float v2 = oacc[db][4 * g + 2] * scale_o;
+        const float v3 = oacc[db][4 * g + 3] * scale_o;
+        if (a.o_dtype == DT_BF16) {
+          const u32x2 w = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+          *reinterpret_cast<u32x2 *>(obase + (orow + d0) * 2) = w;
+        } else if (a.o_dtype == DT_F16) {
+          const u32x2 w = {pack_f16x2(v0, v1), pack_f16x2(v2, v3)};
+          *reinterpret_cast<u32x2 *>(obase + (orow + d0) * 2) = w;
+        } else {
+          *reinterpret_cast<f32x4 *>(obase + (orow + d0) * 4) = f32x4{v0, v1, v2, v3};
         }
-      if (a.lse && hh == 0) a.lse[((int64_t)b * a.Hq + h) * a.n_q + i] = lse;
-    }
+      }
+    if (a.lse && hh == 0) a.lse[((int64_t)b * a.Hq + h) * a.n_q + row] = lse;
   }
 }
 
@@ -472,9 +429,9 @@ bool prefill_supported(int kv, int qd, int D) {
 template <int KV, int QD, int D, int HPW>
 static hipError_t prefill_m(const PrefillArgs &a, hipStream_t s) {
   if (a.mask)
-    hipLaunchKernelGGL((prefill_mfma<KV, QD, D, HPW, true>), dim3(a.num_wg), dim3(HPW * 128), 0, s, a);
+    hipLaunchKernelGGL((prefill_mfma<KV, QD, D, HPW, true>), dim3(a.num_wg), dim3(HPW * 256), 0, s, a);
   else
-    hipLaunchKernelGGL((prefill_mfma<KV, QD, D, HPW, false>), dim3(a.num_wg), dim3(HPW * 128), 0, s, a);
+    hipLaunchKernelGGL((prefill_mfma<KV, QD, D, HPW, false>), dim3(a.num_wg), dim3(HPW * 256), 0, s, a);
   return hipGetLastError();
 }
 
