@@ -156,6 +156,9 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
   if (lds > ctx->lds_per_block)
     return fail(err, ATTN_ERR_UNSUPPORTED, "decode needs %zu bytes of LDS, the device has %zu", lds, ctx->lds_per_block);
 
+  // Partitions: the K/V table capacity is cut so that one round of resident
+  // workgroups covers every (sequence, KV head, row block) once; a second,
+  // partly filled round would run at a fraction of the occupancy.
   const int64_t cap = (int64_t)kv->page_table_stride * kPage;
   const int rows_per_wg = pl->mfma ? rows : pl->rb;
   const int64_t tmin = round_up(std::max<int64_t>(256, 64 * (int64_t)rows_per_wg), kTGran);
@@ -164,7 +167,10 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
     T = round_up(ceil_div(cap, opts->num_splits), kTGran);
   } else {
     const int64_t groups = (int64_t)io->batch * kv->num_kv_heads * pl->row_blocks;
-    const int64_t target = std::max<int64_t>(1, ceil_div(4 * (int64_t)ctx->num_cus, groups));
+    const int per_cu = ctx->host_only ? (pl->mfma ? 1 : 3)
+                                      : pa::decode_blocks_per_cu(pl->mfma, kv->dtype, io->q_dtype, D, rows);
+    const int64_t slots = (int64_t)ctx->num_cus * per_cu;
+    const int64_t target = std::max<int64_t>(1, slots / groups);
     T = std::max(tmin, round_up(ceil_div(cap, target), kTGran));
   }
   const int64_t P = ceil_div(cap, T);

@@ -61,6 +61,8 @@ hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t s);
 bool decode_mfma_supported(int kv_dtype, int q_dtype, int D, int rows);
 bool decode_valu_supported(int kv_dtype, int q_dtype, int D);
+// resident workgroups per CU of the partial kernel selected for these arguments
+int decode_blocks_per_cu(bool mfma, int kv_dtype, int q_dtype, int D, int rows);
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 bool prefill_supported(int kv_dtype, int q_dtype, int D);

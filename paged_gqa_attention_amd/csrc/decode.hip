@@ -814,6 +814,56 @@ hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s) {
   }
 }
 
+// ---- resident workgroups per CU of the partial kernel a launch would use ----
+
+template <typename K>
+static int occupancy_of(K kernel) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, 0) != hipSuccess) n = 1;
+  return n > 0 ? n : 1;
+}
+
+template <int KV, int QD, int D>
+static int valu_occ(int rows) {
+  static int cache[2] = {0, 0};
+  const int k = rows <= 4 ? 0 : 1;
+  if (!cache[k])
+    cache[k] = k == 0 ? occupancy_of(decode_valu<KV, QD, D, 4>) : occupancy_of(decode_valu<KV, QD, D, 8>);
+  return cache[k];
+}
+
+template <int KV, int QD, int D>
+static int mfma_occ(int rows) {
+  static int cache[3] = {0, 0, 0};
+  const int nb = (rows + 15) / 16;
+  const int k = nb <= 1 ? 0 : nb == 2 ? 1 : 2;
+  if (!cache[k])
+    cache[k] = k == 0 ? occupancy_of(decode_mfma<KV, QD, D, 1>)
+             : k == 1 ? occupancy_of(decode_mfma<KV, QD, D, 2>)
+                      : occupancy_of(decode_mfma<KV, QD, D, 4>);
+  return cache[k];
+}
+
+template <int KV, int QD>
+static int occ_d(bool mfma, int D, int rows) {
+  if (mfma) return D == 64 ? mfma_occ<KV, QD, 64>(rows) : mfma_occ<KV, QD, 128>(rows);
+  return D == 64 ? valu_occ<KV, QD, 64>(rows) : valu_occ<KV, QD, 128>(rows);
+}
+
+int decode_blocks_per_cu(bool mfma, int kv, int qd, int D, int rows) {
+  switch (kv) {
+    case DT_F32:
+      if (qd == DT_F32) return occ_d<DT_F32, DT_F32>(false, D, rows);
+      if (qd == DT_BF16) return occ_d<DT_F32, DT_BF16>(false, D, rows);
+      return occ_d<DT_F32, DT_F16>(false, D, rows);
+    case DT_BF16: return occ_d<DT_BF16, DT_BF16>(mfma, D, rows);
+    case DT_F16: return occ_d<DT_F16, DT_F16>(mfma, D, rows);
+    default:
+      if (qd == DT_BF16) return occ_d<DT_FP8, DT_BF16>(mfma, D, rows);
+      return occ_d<DT_FP8, DT_F16>(mfma, D, rows);
+  }
+}
+
 template <int ODT>
 static hipError_t merge_o(const DecodeArgs &a, hipStream_t s) {
   dim3 grid(a.rows, a.Hkv, a.B);
