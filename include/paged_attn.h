@@ -177,7 +177,9 @@ size_t attn_paged_decode_workspace_bytes(const attn_ctx *ctx, const attn_io *io,
 /* Decode / verify: q_rows in [1, 8].  Q dtype: F32/F16/BF16 with F32 K/V,
  * equal to the K/V dtype for F16/BF16 K/V, F16 or BF16 with FP8 K/V.
  * `workspace` is device memory of at least the queried size (16-byte
- * aligned).  block_mask must be NULL. */
+ * aligned, contents irrelevant) for the partition partials; it may be reused
+ * by consecutive calls on one stream but not by calls that can run
+ * concurrently.  block_mask must be NULL. */
 attn_status attn_paged_decode(attn_ctx *ctx, const attn_io *io, const attn_kv *kv,
                               const attn_opts *opts, void *workspace, size_t workspace_bytes,
                               void *hip_stream, char **err);

@@ -319,6 +319,12 @@ def attn_debug_gather_kv(ctx: Context, kv: attn_kv, b: int, seq_len: int, k_out:
 
 # ---- convenience: whole calls on torch tensors -----------------------------------------
 
+def decode_workspace(ctx: Context, io: attn_io, kv: attn_kv, opts: attn_opts, device):
+    """A decode workspace of the size the library asks for."""
+    nb = attn_paged_decode_workspace_bytes(ctx, io, kv, opts)
+    return torch.empty(max(nb, 16), dtype=torch.uint8, device=device)
+
+
 def paged_decode(ctx: Context, q, k_pages, v_pages, page_table, seq_lens, *, k_scale=1.0,
                  v_scale=1.0, softmax_scale=0.0, sinks=None, out=None, out_dtype=None,
                  lse=None, num_splits=0, workspace=None, stream=None):
@@ -329,8 +335,7 @@ def paged_decode(ctx: Context, q, k_pages, v_pages, page_table, seq_lens, *, k_s
     kv = make_kv(k_pages, v_pages, page_table, seq_lens, k_scale, v_scale)
     op = make_opts(softmax_scale, sinks, None, 128, num_splits)
     if workspace is None:
-        nb = attn_paged_decode_workspace_bytes(ctx, io, kv, op)
-        workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
+        workspace = decode_workspace(ctx, io, kv, op, q.device)
     attn_paged_decode(ctx, io, kv, op, workspace, stream)
     return o
 

@@ -119,10 +119,11 @@ attn_status check_ctx(const attn_ctx *ctx, char **err) {
 struct DecodePlan {
   bool mfma;
   int rows, rb, row_blocks, P, T;
-  size_t ws_bytes, ws_o_bytes;
+  size_t ws_bytes, ws_o_bytes, ws_ml_bytes;
 };
 
 constexpr int kTGran = 128;   // partition granularity (tokens)
+constexpr int kTMax = 8192;   // partition size limit (page ids a wave preloads)
 
 attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *kv, const attn_opts *opts,
                         DecodePlan *pl, char **err) {
@@ -173,13 +174,16 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
     const int64_t target = std::max<int64_t>(1, slots / groups);
     T = std::max(tmin, round_up(ceil_div(cap, target), kTGran));
   }
+  // a wave preloads the page ids of its pages: at most 8192 tokens per partition
+  T = std::min<int64_t>(T, kTMax);
   const int64_t P = ceil_div(cap, T);
   if (P > 65535) return fail(err, ATTN_ERR_UNSUPPORTED, "too many partitions (%lld)", (long long)P);
   pl->P = (int)P;
   pl->T = (int)T;
   const int64_t slots = (int64_t)io->batch * kv->num_kv_heads * rows * P;
   pl->ws_o_bytes = (size_t)round_up(slots * D * 4, 256);
-  pl->ws_bytes = pl->ws_o_bytes + (size_t)round_up(slots * 2 * 4, 256);
+  pl->ws_ml_bytes = (size_t)round_up(slots * 2 * 4, 256);
+  pl->ws_bytes = pl->ws_o_bytes + pl->ws_ml_bytes;
   return ATTN_OK;
 }
 
@@ -366,7 +370,8 @@ attn_status attn_paged_decode(attn_ctx *ctx, const attn_io *io, const attn_kv *k
   DeviceGuard g(ctx->device);
   if (!g.ok) return fail(err, ATTN_ERR_DEVICE, "cannot select device %d", ctx->device);
   hipStream_t s = (hipStream_t)hip_stream;
-  st = launched(pl.mfma ? pa::launch_decode_mfma(a, s) : pa::launch_decode_valu(a, s), err, "decode partial launch");
+  st = launched(pl.mfma ? pa::launch_decode_mfma(a, s) : pa::launch_decode_valu(a, s), err,
+                "decode partial launch");
   if (st != ATTN_OK) return st;
   return launched(pa::launch_decode_merge(a, s), err, "decode merge launch");
 }

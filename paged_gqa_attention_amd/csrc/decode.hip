@@ -52,6 +52,91 @@ __device__ __forceinline__ void wave_scales(const float (*m_w)[NR], int wave, in
 }
 
 // ==================================================================================
+// Log-sum-exp merge of the partitions + sink, one wave per output row
+// ==================================================================================
+template <int D>
+__device__ __forceinline__ void merge_row(const DecodeArgs &a, int b, int kvh, int rr, int lane) {
+  constexpr int DPL = D / 64;
+  constexpr int CH = 8;                  // partitions whose outputs are loaded at once
+  const int L = min(a.lens[b], a.capacity);
+  const int Pl = (L + a.T - 1) / a.T;    // live partitions
+  const int h = kvh * a.G + rr / a.R, i = rr % a.R;
+  const int64_t base = (((int64_t)b * a.Hkv + kvh) * a.rows + rr) * a.P;
+  const float sink = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
+
+  float o[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
+  float M = sink, zp = 0.f;
+  // partitions in chunks of 64 for the statistics and CH for the outputs; all
+  // loads of a chunk are issued before any of them is used
+  for (int p0 = 0; p0 < Pl; p0 += 64) {
+    const int pm = p0 + lane;
+    const float mp = pm < Pl ? a.ws_ml[(base + pm) * 2] : kNegInf;
+    const float lp = pm < Pl ? a.ws_ml[(base + pm) * 2 + 1] : 0.f;
+    float Mc = mp;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) Mc = __builtin_fmaxf(Mc, shfl_xor(Mc, m));
+    const float Mn = __builtin_fmaxf(M, Mc);
+    if (Mn == kNegInf) continue;
+    const float rescale = fast_exp2(M - Mn);   // earlier chunks (M = -inf: 0)
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[e] *= rescale;
+    zp *= rescale;
+    M = Mn;
+    const float w = (mp == kNegInf) ? 0.f : fast_exp2(mp - M);
+    zp += w * lp;
+    const int cnt = min(64, Pl - p0);
+    for (int q0 = 0; q0 < cnt; q0 += CH) {
+      float ov[CH][DPL];
+#pragma unroll
+      for (int q = 0; q < CH; ++q) {
+        const int qq = q0 + q < cnt ? q0 + q : cnt - 1;
+        const float *op = a.ws_o + (base + p0 + qq) * D;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) ov[q][e] = op[lane + 64 * e];
+      }
+#pragma unroll
+      for (int q = 0; q < CH; ++q) {
+        if (q0 + q < cnt) {
+          const float wq = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(w), q0 + q));
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) o[e] = __builtin_fmaf(wq, ov[q][e], o[e]);
+        }
+      }
+    }
+  }
+  float Z = 0.f;
+  if (M != kNegInf) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) zp += shfl_xor(zp, m);
+    Z = zp + fast_exp2(sink - M);
+  }
+  const float inv = (M == kNegInf) ? 0.f : a.v_scale / Z;
+  char *orow = reinterpret_cast<char *>(a.o);
+  const int64_t obase = (int64_t)b * a.o_sb + (int64_t)i * a.o_sr + (int64_t)h * a.o_sh;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) {
+    const float v = o[e] * inv;
+    if (a.o_dtype == DT_F32) store_out<DT_F32>(orow, obase + lane + 64 * e, v);
+    else if (a.o_dtype == DT_BF16) store_out<DT_BF16>(orow, obase + lane + 64 * e, v);
+    else store_out<DT_F16>(orow, obase + lane + 64 * e, v);
+  }
+  if (a.lse && lane == 0) {
+    const float lse = (M == kNegInf) ? kNegInf : (M + __builtin_log2f(Z)) * kLn2;
+    a.lse[((int64_t)b * a.Hq + h) * a.R + i] = lse;
+  }
+}
+
+// one workgroup of 4 waves per (4 rows, KV head, sequence)
+template <int D>
+__global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rr = blockIdx.x * kWaves + wave, kvh = blockIdx.y, b = blockIdx.z;
+  if (rr < a.rows) merge_row<D>(a, b, kvh, rr, lane);
+}
+
+// ==================================================================================
 // VALU partial kernel
 // ==================================================================================
 //
@@ -72,6 +157,10 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
   constexpr int MR = RB / 4;         // softmax rows per lane
   constexpr int QW = (KVDT == DT_F32) ? 4 : (KVDT == DT_FP8 ? 8 : 4);  // Q words per K chunk
 
+  // query rows of the workgroup, in the arithmetic's representation:
+  // FP32 for FP32 K/V, else the 16-bit Q codes
+  constexpr int QE = (KVDT == DT_F32) ? 4 : 2;
+  __shared__ __attribute__((aligned(16))) char q_lds[RB * D * QE];
   __shared__ float p_lds[kWaves][16][RB];
   __shared__ float alpha_lds[kWaves][RB];
   __shared__ float m_w[kWaves][RB];
@@ -80,8 +169,8 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform_int(threadIdx.x >> 6);
-  const int p = blockIdx.x, b = blockIdx.z;
-  const int kvh = blockIdx.y / a.row_blocks, rb = blockIdx.y % a.row_blocks;
+  const int kvh = blockIdx.x / a.row_blocks, rb = blockIdx.x % a.row_blocks;
+  const int p = blockIdx.y, b = blockIdx.z;
   const int L = min(a.lens[b], a.capacity);
   const int t0 = p * a.T;
   if (t0 >= L) return;  // empty partition: the merge never reads it
@@ -89,51 +178,44 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
   const int n = lane >> 2, qq = lane & 3;
   const int tg = lane % CPR;
 
-  // ---- query rows of this block ----
-  int pos[RB];
-  uint32_t q[RB][NL][QW];
-#pragma unroll
-  for (int r = 0; r < RB; ++r) {
+  // ---- query rows of this block -> LDS ----
+  for (int idx = threadIdx.x; idx < RB * D; idx += 256) {
+    const int r = idx / D, d = idx % D;
     const int rr = rb * RB + r;
     const bool ok = rr < a.rows;
     const int h = kvh * a.G + (ok ? rr / a.R : 0);
     const int i = ok ? rr % a.R : 0;
-    pos[r] = ok ? L - a.R + i : -1;
-    const char *qrow = reinterpret_cast<const char *>(a.q) +
-                       ((int64_t)b * a.q_sb + (int64_t)i * a.q_sr + (int64_t)h * a.q_sh) *
-                           (QDT == DT_F32 ? 4 : 2);
-#pragma unroll
-    for (int c = 0; c < NL; ++c) {
-      const int e0 = (4 * c + qq) * EPC;  // first element of this lane's chunk
-      if constexpr (KVDT == DT_F32) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float v;
-          if constexpr (QDT == DT_F32) v = reinterpret_cast<const float *>(qrow)[e0 + e];
-          else if constexpr (QDT == DT_BF16)
-            v = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(qrow)[e0 + e] << 16);
-          else v = (float)reinterpret_cast<const _Float16 *>(qrow)[e0 + e];
-          q[r][c][e] = ok ? __float_as_uint(v) : 0u;
-        }
-      } else {
-        // 16-bit Q words, EPC elements
-#pragma unroll
-        for (int w = 0; w < QW; w += 4) {
-          u32x4 v = ld16(qrow + (e0 + 2 * w) * 2);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) q[r][c][w + e] = ok ? v[e] : 0u;
-        }
-      }
+    const int64_t qi = (int64_t)b * a.q_sb + (int64_t)i * a.q_sr + (int64_t)h * a.q_sh + d;
+    if constexpr (KVDT == DT_F32) {
+      float v;
+      if constexpr (QDT == DT_F32) v = reinterpret_cast<const float *>(a.q)[qi];
+      else if constexpr (QDT == DT_BF16)
+        v = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(a.q)[qi] << 16);
+      else v = (float)reinterpret_cast<const _Float16 *>(a.q)[qi];
+      reinterpret_cast<float *>(q_lds)[idx] = ok ? v : 0.f;
+    } else {
+      const uint16_t v = reinterpret_cast<const uint16_t *>(a.q)[qi];
+      reinterpret_cast<uint16_t *>(q_lds)[idx] = ok ? v : (uint16_t)0;
     }
   }
+  __syncthreads();
+  // the lane's Q words for row r and chunk c (QW 32-bit words)
+  auto q_words = [&](int r, int c, uint32_t *w) {
+    const int e0 = (4 * c + qq) * EPC;
+    const char *src = q_lds + ((size_t)r * D + e0) * QE;
+#pragma unroll
+    for (int k = 0; k < QW; k += 4) {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(src + 4 * k);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[k + e] = v[e];
+    }
+  };
+  // position of the rows this lane handles in the softmax: r = qq + 4k
   int pos_mine[MR];
 #pragma unroll
   for (int k = 0; k < MR; ++k) {
-    int v = pos[4 * k];
-    v = qq == 1 ? pos[4 * k + 1] : v;
-    v = qq == 2 ? pos[4 * k + 2] : v;
-    v = qq == 3 ? pos[4 * k + 3] : v;
-    pos_mine[k] = v;
+    const int rr = rb * RB + qq + 4 * k;
+    pos_mine[k] = rr < a.rows ? L - a.R + rr % a.R : -1;
   }
 
   float m_run[MR], l_run[MR];
@@ -149,11 +231,24 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
   const char *vbase = reinterpret_cast<const char *>(a.v) + (int64_t)kvh * a.v_sh * ELT;
   const int32_t *pt = a.page_table + (int64_t)b * a.pt_stride;
   const int pg_end = (t1 + 15) >> 4;
-  int pg = (t0 >> 4) + wave;
+  const int pg_first = (t0 >> 4) + wave;
+  int pg = pg_first;
 
-  u32x4 kc[NL], vc[NL];
+  // This wave's page ids (its k-th page is pg_first + 4k, k < 128: partitions
+  // hold at most 8192 tokens), loaded once, coalesced, and broadcast per page.
+  int ids[2];
+#pragma unroll
+  for (int hlf = 0; hlf < 2; ++hlf) {
+    const int idx = pg_first + (64 * hlf + lane) * kWaves;
+    ids[hlf] = idx < pg_end ? pt[idx] : 0;
+  }
+  auto page_id = [&](int page_idx) -> int64_t {
+    const int k = (page_idx - pg_first) / kWaves;
+    return k < 64 ? __builtin_amdgcn_readlane(ids[0], k) : __builtin_amdgcn_readlane(ids[1], k - 64);
+  };
+
   auto load_page = [&](int page_idx, u32x4 *kd, u32x4 *vd) {
-    const int64_t pid = pt[page_idx];
+    const int64_t pid = page_id(page_idx);
     const char *kp = kbase + pid * a.k_sp * ELT + n * (D * ELT) + qq * 16;
     const char *vp = vbase + pid * a.v_sp * ELT + lane * 16;
 #pragma unroll
@@ -162,13 +257,8 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
       vd[c] = ld16(vp + c * 1024);
     }
   };
-  if (pg < pg_end) load_page(pg, kc, vc);
 
-  for (; pg < pg_end; pg += kWaves) {
-    u32x4 kn[NL], vn[NL];
-    const int pgn = pg + kWaves;
-    if (pgn < pg_end) load_page(pgn, kn, vn);
-
+  auto process_page = [&](const int pg, const u32x4 *kc, const u32x4 *vc) {
     // ---- scores of this lane's token for all rows ----
     float s[RB];
 #pragma unroll
@@ -176,27 +266,29 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
       float acc = 0.f;
 #pragma unroll
       for (int c = 0; c < NL; ++c) {
+        uint32_t qw[QW];
+        q_words(r, c, qw);
         if constexpr (KVDT == DT_F32) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(__uint_as_float(q[r][c][e]),
+          for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(__uint_as_float(qw[e]),
                                                            __uint_as_float(kc[c][e]), acc);
         } else if constexpr (KVDT == DT_BF16) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc = dot2_bf16(q[r][c][e], kc[c][e], acc);
+          for (int e = 0; e < 4; ++e) acc = dot2_bf16(qw[e], kc[c][e], acc);
         } else if constexpr (KVDT == DT_F16) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc = dot2_f16(q[r][c][e], kc[c][e], acc);
+          for (int e = 0; e < 4; ++e) acc = dot2_f16(qw[e], kc[c][e], acc);
         } else {  // FP8 K -> 16-bit pairs of Q's type
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             uint32_t lo = fp8x2_to_16<QDT != DT_BF16, false>(kc[c][e]);
             uint32_t hi = fp8x2_to_16<QDT != DT_BF16, true>(kc[c][e]);
             if constexpr (QDT == DT_BF16) {
-              acc = dot2_bf16(q[r][c][2 * e], lo, acc);
-              acc = dot2_bf16(q[r][c][2 * e + 1], hi, acc);
+              acc = dot2_bf16(qw[2 * e], lo, acc);
+              acc = dot2_bf16(qw[2 * e + 1], hi, acc);
             } else {
-              acc = dot2_f16(q[r][c][2 * e], lo, acc);
-              acc = dot2_f16(q[r][c][2 * e + 1], hi, acc);
+              acc = dot2_f16(qw[2 * e], lo, acc);
+              acc = dot2_f16(qw[2 * e + 1], hi, acc);
             }
           }
         }
@@ -258,8 +350,20 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
     }
     wave_lds_sync();
 
-#pragma unroll
-    for (int c = 0; c < NL; ++c) { kc[c] = kn[c]; vc[c] = vn[c]; }
+  };
+
+  // Two page buffers in ping-pong: while one page is processed the other's
+  // loads stay in flight (no register copies, which would force a full wait).
+  u32x4 kA[NL], vA[NL], kB[NL], vB[NL];
+  if (pg < pg_end) load_page(pg, kA, vA);
+  if (pg + kWaves < pg_end) load_page(pg + kWaves, kB, vB);
+  for (; pg < pg_end; pg += 2 * kWaves) {
+    process_page(pg, kA, vA);
+    if (pg + 2 * kWaves < pg_end) load_page(pg + 2 * kWaves, kA, vA);
+    if (pg + kWaves < pg_end) {
+      process_page(pg + kWaves, kB, vB);
+      if (pg + 3 * kWaves < pg_end) load_page(pg + 3 * kWaves, kB, vB);
+    }
   }
 
   // ---- wave totals: l over the 16 token lanes of a row, o over the token groups ----
@@ -384,7 +488,7 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform_int(threadIdx.x >> 6);
-  const int p = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int kvh = blockIdx.x, p = blockIdx.y, b = blockIdx.z;
   const int L = min(a.lens[b], a.capacity);
   const int t0 = p * a.T;
   if (t0 >= L) return;
@@ -424,18 +528,25 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
   const int32_t *pt = a.page_table + (int64_t)b * a.pt_stride;
   const int pg_end = (t1 + 15) >> 4;
   const int pp_end = (t1 + 31) >> 5;
-  int pp = (t0 >> 5) + wave;
+  const int pp_first = (t0 >> 5) + wave;
+  int pp = pp_first;
+
+  // Page ids of this wave's page pairs (pair k = pp_first + 4k, k < 64:
+  // partitions hold at most 8192 tokens), loaded once and broadcast per pair.
+  int ids0, ids1;
+  {
+    const int ppi = pp_first + lane * kWaves;
+    const int p0 = 2 * ppi, p1 = 2 * ppi + 1;
+    ids0 = p0 < pg_end ? pt[p0] : 0;
+    ids1 = p1 < pg_end ? pt[p1] : ids0;
+  }
 
   // K rows: A row m = n of MFMA `a` holds token 8*(n/4) + 4a + n%4 (page-pair local)
   // V rows: value row 16*mb + n, tokens 8*j .. 8*j+7 (page j/2, offset 8*(j&1))
-  u32x4 kf[2][KL];
-  u32x2 vf8[MB];   // FP8 V: 8 bytes per fragment
-  u32x4 vf16[MB];
   auto load_pair = [&](int ppi, u32x4 (*kd)[KL], u32x4 *vd16, u32x2 *vd8) {
-    const int pg0 = 2 * ppi;
-    const bool has1 = (pg0 + 1) < pg_end;
-    const int64_t pid0 = pt[pg0];
-    const int64_t pid1 = has1 ? pt[pg0 + 1] : pid0;
+    const int k = (ppi - pp_first) / kWaves;
+    const int64_t pid0 = __builtin_amdgcn_readlane(ids0, k);
+    const int64_t pid1 = __builtin_amdgcn_readlane(ids1, k);
 #pragma unroll
     for (int aa = 0; aa < 2; ++aa) {
       const int tok = 8 * (n >> 2) + 4 * aa + (n & 3);
@@ -456,15 +567,7 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
       else vd16[mb] = ld16(row);
     }
   };
-  if (pp < pp_end) load_pair(pp, kf, vf16, vf8);
-
-  for (; pp < pp_end; pp += kWaves) {
-    u32x4 kn[2][KL];
-    u32x2 vn8[MB];
-    u32x4 vn16[MB];
-    const int ppn = pp + kWaves;
-    if (ppn < pp_end) load_pair(ppn, kn, vn16, vn8);
-
+  auto process_pair = [&](const int pp, const u32x4 (*kf)[KL], const u32x4 *vf16, const u32x2 *vf8) {
     // ---- S^T = K Q^T ----
     f32x4 s[NB][2];
 #pragma unroll
@@ -564,12 +667,21 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
       for (int nb = 0; nb < NB; ++nb) oacc[mb][nb] = mfma16<F16>(vfr, pf[nb], oacc[mb][nb]);
     }
 
-#pragma unroll
-    for (int aa = 0; aa < 2; ++aa)
-#pragma unroll
-      for (int u = 0; u < KL; ++u) kf[aa][u] = kn[aa][u];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) { vf16[mb] = vn16[mb]; vf8[mb] = vn8[mb]; }
+  };
+
+  // two page-pair buffers in ping-pong (no register copies of in-flight loads)
+  u32x4 kA[2][KL], kB[2][KL];
+  u32x4 vA16[MB], vB16[MB];
+  u32x2 vA8[MB], vB8[MB];
+  if (pp < pp_end) load_pair(pp, kA, vA16, vA8);
+  if (pp + kWaves < pp_end) load_pair(pp + kWaves, kB, vB16, vB8);
+  for (; pp < pp_end; pp += 2 * kWaves) {
+    process_pair(pp, kA, vA16, vA8);
+    if (pp + 2 * kWaves < pp_end) load_pair(pp + 2 * kWaves, kA, vA16, vA8);
+    if (pp + kWaves < pp_end) {
+      process_pair(pp + kWaves, kB, vB16, vB8);
+      if (pp + 3 * kWaves < pp_end) load_pair(pp + 3 * kWaves, kB, vB16, vB8);
+    }
   }
 
   // ---- wave totals ----
@@ -629,65 +741,6 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
       a.ws_ml[slot * 2 + 0] = M;
       a.ws_ml[slot * 2 + 1] = l;
     }
-  }
-}
-
-// ==================================================================================
-// Log-sum-exp merge of the partitions + sink, one wave per output row
-// ==================================================================================
-template <int ODT, int D>
-__global__ __launch_bounds__(64) void decode_merge(DecodeArgs a) {
-  constexpr int DPL = D / 64;
-  const int lane = threadIdx.x;
-  const int rr = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int L = min(a.lens[b], a.capacity);
-  const int Pl = (L + a.T - 1) / a.T;  // live partitions
-  const int h = kvh * a.G + rr / a.R, i = rr % a.R;
-  const int64_t base = (((int64_t)b * a.Hkv + kvh) * a.rows + rr) * a.P;
-  const float sink = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
-
-  float M = sink;
-  for (int p = lane; p < Pl; p += 64) M = __builtin_fmaxf(M, a.ws_ml[(base + p) * 2]);
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) M = __builtin_fmaxf(M, shfl_xor(M, m));
-
-  float o[DPL];
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-  float Z = 0.f;
-  if (M != kNegInf) {
-    Z = fast_exp2(sink - M);
-    for (int p0 = 0; p0 < Pl; p0 += 64) {
-      const int pm = p0 + lane;
-      float w = 0.f;
-      if (pm < Pl) {
-        const float mp = a.ws_ml[(base + pm) * 2];
-        const float lp = a.ws_ml[(base + pm) * 2 + 1];
-        w = (mp == kNegInf) ? 0.f : fast_exp2(mp - M);
-        Z += w * lp;
-      }
-      const int cnt = min(64, Pl - p0);
-      for (int q = 0; q < cnt; ++q) {
-        const float wq = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(w), q));
-        const float *op = a.ws_o + (base + p0 + q) * D;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) o[e] = __builtin_fmaf(wq, op[lane + 64 * e], o[e]);
-      }
-    }
-    // Z: the sink term counted once (lane 0), partition terms summed over lanes
-    float zs = Z - (lane == 0 ? 0.f : fast_exp2(sink - M));
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) zs += shfl_xor(zs, m);
-    Z = zs;
-  }
-  const float inv = (M == kNegInf) ? 0.f : a.v_scale / Z;
-  char *orow = reinterpret_cast<char *>(a.o);
-  const int64_t obase = (int64_t)b * a.o_sb + (int64_t)i * a.o_sr + (int64_t)h * a.o_sh;
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) store_out<ODT>(orow, obase + lane + 64 * e, o[e] * inv);
-  if (a.lse && lane == 0) {
-    const float lse = (M == kNegInf) ? kNegInf : (M + __builtin_log2f(Z)) * kLn2;
-    a.lse[((int64_t)b * a.Hq + h) * a.R + i] = lse;
   }
 }
 
@@ -761,7 +814,7 @@ bool decode_mfma_supported(int kv, int qd, int D, int rows) {
 
 template <int KV, int QD, int D>
 static hipError_t valu_rb(const DecodeArgs &a, hipStream_t s) {
-  dim3 grid(a.P, a.Hkv * a.row_blocks, a.B);
+  dim3 grid(a.Hkv * a.row_blocks, a.P, a.B);   // KV heads of one page run side by side
   const int rb = (a.rows + a.row_blocks - 1) / a.row_blocks;
   if (rb <= 4) hipLaunchKernelGGL((decode_valu<KV, QD, D, 4>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((decode_valu<KV, QD, D, 8>), grid, dim3(256), 0, s, a);
@@ -789,7 +842,7 @@ hipError_t launch_decode_valu(const DecodeArgs &a, hipStream_t s) {
 
 template <int KV, int QD, int D>
 static hipError_t mfma_nb(const DecodeArgs &a, hipStream_t s) {
-  dim3 grid(a.P, a.Hkv, a.B);
+  dim3 grid(a.Hkv, a.P, a.B);
   const int nb = (a.rows + 15) / 16;
   switch (nb) {
     case 1: hipLaunchKernelGGL((decode_mfma<KV, QD, D, 1>), grid, dim3(256), 0, s, a); break;
@@ -864,18 +917,11 @@ int decode_blocks_per_cu(bool mfma, int kv, int qd, int D, int rows) {
   }
 }
 
-template <int ODT>
-static hipError_t merge_o(const DecodeArgs &a, hipStream_t s) {
-  dim3 grid(a.rows, a.Hkv, a.B);
-  if (a.D == 64) hipLaunchKernelGGL((decode_merge<ODT, 64>), grid, dim3(64), 0, s, a);
-  else hipLaunchKernelGGL((decode_merge<ODT, 128>), grid, dim3(64), 0, s, a);
-  return hipGetLastError();
-}
-
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t s) {
-  if (a.o_dtype == DT_F32) return merge_o<DT_F32>(a, s);
-  if (a.o_dtype == DT_BF16) return merge_o<DT_BF16>(a, s);
-  return merge_o<DT_F16>(a, s);
+  dim3 grid((a.rows + kWaves - 1) / kWaves, a.Hkv, a.B);
+  if (a.D == 64) hipLaunchKernelGGL((decode_merge<64>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((decode_merge<128>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_debug_gather(const void *k, const void *v, int64_t k_sp, int64_t k_sh,

@@ -324,3 +324,25 @@ def test_prefill_row_matches_decode():
         q1.q = p.q[:, i:i + 1].clone()
         o1, _ = run(Dev(q1))
         assert np.max(np.abs(o1[0, 0] - o[0, i])) <= 1e-2
+
+
+def test_decode_workspace_reuse():
+    """Consecutive calls of different shapes share one workspace (contents
+    left by one call never leak into the next)."""
+    _say("workspace reuse")
+    p1 = synth.make_decode(79, 3, 32, 8, 128, [1500, 700, 2300], 1, kv_dtype=DT_BF16, stride=160)
+    p2 = synth.make_decode(80, 3, 32, 8, 128, [2400, 10, 900], 8, kv_dtype=DT_BF16, stride=160)
+    d1, d2 = Dev(p1), Dev(p2)
+    o1 = torch.empty(d1.q.shape, dtype=torch.bfloat16, device="cuda")
+    o2 = torch.empty(d2.q.shape, dtype=torch.bfloat16, device="cuda")
+    io1, kv1, op1 = pa.make_io(d1.q, o1), pa.make_kv(d1.k, d1.v, d1.pt, d1.lens), pa.make_opts()
+    io2, kv2, op2 = pa.make_io(d2.q, o2), pa.make_kv(d2.k, d2.v, d2.pt, d2.lens), pa.make_opts()
+    n = max(pa.attn_paged_decode_workspace_bytes(ctx(), io1, kv1, op1),
+            pa.attn_paged_decode_workspace_bytes(ctx(), io2, kv2, op2))
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")   # NaN-filled
+    for _ in range(2):
+        pa.attn_paged_decode(ctx(), io1, kv1, op1, ws)
+        pa.attn_paged_decode(ctx(), io2, kv2, op2, ws)
+    torch.cuda.synchronize()
+    check_full(p1, o1.double().cpu().numpy(), None)
+    check_full(p2, o2.double().cpu().numpy(), None)
