@@ -10,7 +10,7 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/paged_attn.h"
+#include "paged_attn.h"
 #include "attn_internal.h"
 
 struct attn_ctx {
@@ -256,8 +256,9 @@ attn_status prefill_common(attn_ctx *ctx, const attn_io *io, const attn_kv *kv, 
   a.mask_nqb = opts->mask_q_blocks; a.mask_nkb = opts->mask_k_blocks;
   a.q_tiles = (int)ceil_div(io->q_rows, 128);
   a.heads_per_wg = (G % 2 == 0) ? 2 : 1;
-  const int64_t ntask = (int64_t)a.q_tiles * a.B * a.Hkv;
-  const int64_t nwg = round_up(ntask, 8) * (G / a.heads_per_wg);
+  // groups dealt over 8 XCDs (padded), each with q_tiles tasks of G/HPW workgroups
+  const int64_t groups = (int64_t)a.B * a.Hkv;
+  const int64_t nwg = round_up(groups, 8) * a.q_tiles * (G / a.heads_per_wg);
   if (nwg > INT32_MAX) return fail(err, ATTN_ERR_UNSUPPORTED, "prefill grid too large");
   a.num_wg = (int)nwg;
   if (ctx->host_only) return fail(err, ATTN_ERR_DEVICE, "host-only context: nothing enqueued");

@@ -165,8 +165,11 @@ __device__ __forceinline__ float sum_xor16(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 3-input maximum in one instruction (operands are never NaN where it is used)
 __device__ __forceinline__ float max3(float a, float b, float c) {
-  return __builtin_fmaxf(a, __builtin_fmaxf(b, c));
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 }  // namespace pa

@@ -18,10 +18,10 @@
 // paragraph of the Geramy/LSE README).  Sinks are added to the softmax
 // denominator at the end (TokenSpeed-Kernel-AMD page, "Attention").
 //
-// Workgroup order: tasks (query tile, sequence, KV head) are ordered
-// heaviest-first and dealt round-robin to the 8 XCDs; the G/HPW workgroups of
-// one task land on the same XCD back to back so their K/V tiles come from
-// that XCD's L2.
+// Workgroup order: (sequence, KV head) groups are dealt to the 8 XCDs; an
+// XCD runs a group's query tiles back to back, heaviest first, with the G/HPW
+// workgroups of one query tile adjacent, so resident workgroups share K/V
+// tiles through that XCD's L2.
 #include "attn_internal.h"
 #include "common.h"
 
@@ -80,16 +80,18 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
   __shared__ int list_count[MASK ? NW : 1];
 
   // ---- task of this workgroup ----
-  const int wpt = a.G / HPW;  // workgroups per task
+  // Workgroups are dispatched round-robin over the XCDs (block x -> XCD x % 8).
+  // Each XCD receives whole (sequence, KV head) groups and runs a group's
+  // query tiles back to back, heaviest first, so the query tiles that are
+  // resident together stream the same K/V tiles through that XCD's L2.
+  const int wpt = a.G / HPW;  // workgroups per (query tile, group) task
   const int x = blockIdx.x;
   const int xcd = x % kXcds, slot = x / kXcds;
-  const int task = (slot / wpt) * kXcds + xcd;
-  const int hp = slot % wpt;
-  const int ntask = a.q_tiles * a.B * a.Hkv;
-  if (task >= ntask) return;
-  const int kvh = task % a.Hkv;
-  const int b = (task / a.Hkv) % a.B;
-  const int qt = a.q_tiles - 1 - task / (a.Hkv * a.B);
+  const int task_local = slot / wpt, hp = slot % wpt;
+  const int gi = (task_local / a.q_tiles) * kXcds + xcd;
+  const int qt = a.q_tiles - 1 - task_local % a.q_tiles;
+  if (gi >= a.B * a.Hkv) return;
+  const int b = gi / a.Hkv, kvh = gi % a.Hkv;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -273,11 +275,16 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
 
     // online softmax (lazy rescaling) for row nl; the two lane halves hold
     // keys 16g' + 8hh + ... of each 32-key block
-    float mx = kNegInf;
+    // row max as a tree of 3-input maxima (32 values -> 11 -> 4 -> 1)
+    float t1[11];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = max3(mx, s[mb][i], s[mb][i + 1]);
+    for (int k = 0; k < 10; ++k) {
+      const int a0 = 3 * k, a1 = 3 * k + 1, a2 = 3 * k + 2;
+      t1[k] = max3(s[a0 >> 4][a0 & 15], s[a1 >> 4][a1 & 15], s[a2 >> 4][a2 & 15]);
+    }
+    t1[10] = __builtin_fmaxf(s[1][14], s[1][15]);
+    float mx = max3(max3(t1[0], t1[1], t1[2]), max3(t1[3], t1[4], t1[5]),
+                    max3(t1[6], t1[7], max3(t1[8], t1[9], t1[10])));
     mx = max_xor32(mx);
     const float mxs = mx * sc;
     const bool grow = mxs > m_run + kLazy;
@@ -290,7 +297,7 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
       m_run = m_new;
     }
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-    float lsum = 0.f;
+    float lsum[4] = {0.f, 0.f, 0.f, 0.f};   // independent chains of the row sum
     u32x4 pf[2][2];   // [mb][kk]: P^T fragment, keys 32mb + 16kk + 8hh .. +8
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -302,9 +309,9 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
           const float p1 = fast_exp2(__builtin_fmaf(s[mb][8 * kk + 2 * e + 1], sc, -m_use));
           const uint32_t w = F16 ? pack_f16x2(p0, p1) : pack_bf16x2(p0, p1);
           pf[mb][kk][e] = w;
-          lsum = F16 ? dot2_f16(w, 0x3C003C00u, lsum) : dot2_bf16(w, 0x3F803F80u, lsum);
+          lsum[e] = F16 ? dot2_f16(w, 0x3C003C00u, lsum[e]) : dot2_bf16(w, 0x3F803F80u, lsum[e]);
         }
-    l_run += lsum;
+    l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
 
     // O^T[db] += V^T[32 rows, 16 keys] P^T[16 keys, 32 rows]
 #pragma unroll
