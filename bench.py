@@ -1,6 +1,8 @@
 """Benchmark of the paged GQA attention hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--all]
+    python bench.py --only decode|prefill|copy [--steps K] [--warmup W]
+    python bench.py --pmc-summary FETCH_DIR WRITE_DIR
 
 Prints ONE JSON line.  ``value`` is paged decode throughput in GB/s of
 algorithmic HBM bytes (every live K/V element once, plus Q, O and the used
@@ -16,6 +18,12 @@ stream, bracketed by synchronisation, timed with HIP events on that stream.
 The FP64 CPU oracle is timed on a bounded sample of rows of the same
 workload (``cpu_baseline``).  ``--all`` also prints the other workloads to
 stderr (not part of the JSON line).
+
+``--only`` runs one workload without the CPU baseline, for profiling under
+rocprofv3 (``copy`` is a 1 GiB device-to-device copy whose counter readings
+calibrate HBM byte counts).  ``--pmc-summary`` turns two rocprofv3 ``--pmc``
+CSV outputs (FETCH_SIZE, then WRITE_SIZE, each over the three ``--only`` runs)
+into profiles/hbm_counters.json, which fills ``roofline.traffic``.
 """
 from __future__ import annotations
 
@@ -57,6 +65,72 @@ def _traffic(key: str, src_hash: str, launches_per_call: int = 1):
     if not rec or rec.get("src_hash") != src_hash:
         return None
     return rec.get("bytes_per_call")
+
+
+COPY_BYTES = 1 << 30
+
+
+def _pmc_rows(directory: str):
+    """(kernel name, counter, value) of every dispatch in rocprofv3 CSV output."""
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"]),
+                             (path, r.get("Dispatch_Id", ""))))   # ids restart per process
+    return rows
+
+
+def pmc_summary(fetch_dir: str, write_dir: str):
+    """HBM bytes per call of the decode and prefill workloads from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads for
+    the 1 GiB copy; written to profiles/hbm_counters.json."""
+    out = {}
+    per = {}
+    for cname, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        acc_k = {}
+        for kname, cn, v, did in _pmc_rows(d):
+            if cn != cname:
+                continue
+            key = (kname, did)
+            acc_k[key] = acc_k.get(key, 0.0) + v   # counters are summed over dimensions
+        per[cname] = acc_k
+    def run_of(did):   # which --only run a dispatch came from (the CSV file's name)
+        return os.path.basename(did[0]).split("_")[0]
+
+    def mean(cname, run, pred):
+        vals = [v for (k, did), v in per[cname].items() if run_of(did) == run and pred(k)]
+        return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+    # the 1 GiB copy: the largest dispatches of the copy run
+    def copy_mean(cname):
+        vals = [v for (k, did), v in per[cname].items() if run_of(did) == "copy"]
+        big = [v for v in vals if v >= 0.9 * max(vals)]
+        return sum(big) / len(big)
+    f_scale = COPY_BYTES / (copy_mean("FETCH_SIZE") * 1024)
+    w_scale = COPY_BYTES / (copy_mean("WRITE_SIZE") * 1024)
+    groups = {
+        "decode_bf16_16k": ("decode", ("decode_valu", "decode_merge"),
+                            _src_hash("decode.hip", "common.h")),
+        "prefill_bf16_8k_b16": ("prefill", ("prefill_mfma",), _src_hash("prefill.hip", "common.h")),
+    }
+    for key, (run, kernels, h) in groups.items():
+        total = 0.0
+        parts = {}
+        for kn in kernels:
+            fm, nf = mean("FETCH_SIZE", run, lambda k, kn=kn: kn in k)
+            wm, nw = mean("WRITE_SIZE", run, lambda k, kn=kn: kn in k)
+            fb, wb = fm * 1024 * f_scale, wm * 1024 * w_scale
+            parts[kn] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "dispatches": [nf, nw]}
+            total += fb + wb
+        out[key] = {"src_hash": h, "bytes_per_call": round(total), "kernels": parts}
+    out["calibration"] = {"copy_bytes": COPY_BYTES, "fetch_scale": round(f_scale, 4),
+                          "write_scale": round(w_scale, 4)}
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, "hbm_counters.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def time_calls(fn, steps: int, warmup: int):
@@ -168,7 +242,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--all", action="store_true")
+    ap.add_argument("--only", choices=["decode", "prefill", "copy"])
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path; "
               "a sharded deployment runs one copy per GPU on its share of the heads.",
@@ -182,9 +261,20 @@ def main():
 
     torch.manual_seed(0)
     dev = "cuda"
+    if args.only == "copy":
+        a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        ms = time_calls(lambda: b.copy_(a), args.steps, args.warmup)
+        print(json.dumps({"workload": "copy 1 GiB", "ms": round(ms, 4),
+                          "GB/s": round(2 * COPY_BYTES / ms / 1e6, 1)}), flush=True)
+        return
     ctx = pa.attn_open(0)
+    if args.only:
+        args.no_cpu = True
 
     # ---------------- decode @16K (the headline) ----------------
+    if args.only == "prefill":
+        return only_prefill(ctx, args)
     t_gen = time.perf_counter()
     p = synth.config2(q_rows=1, lens=[16384] * 16, device=dev)
     call, (P, T), keep = decode_setup(ctx, p, dev)
@@ -202,6 +292,10 @@ def main():
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline_decode(p)   # the oracle copies the inputs to host memory
+    if args.only == "decode":
+        print(json.dumps({"workload": "decode", "ms": round(ms, 5), "GB/s": round(gbs, 1),
+                          "splits": P, "roofline": roof}), flush=True)
+        return
     del keep, call, p
     torch.cuda.empty_cache()
 
@@ -242,6 +336,17 @@ def main():
     if args.all:
         extra(ctx, args)
     print(json.dumps(line), flush=True)
+
+
+def only_prefill(ctx, args):
+    import synth
+    from paged_gqa_attention_amd import accounting as acc
+    pp = synth.config4(seq_len=8192, batch=16, device="cuda")
+    pcall, pkeep = prefill_setup(ctx, pp, "cuda")
+    pms = time_calls(pcall, args.steps, args.warmup)
+    flops = acc.attention_flops(acc.causal_pairs(8192, 8192), 64, 64, 16)
+    print(json.dumps({"workload": "prefill", "ms": round(pms, 4),
+                      "TFLOP/s": round(flops / (pms * 1e-3) / 1e12, 1)}), flush=True)
 
 
 def extra(ctx, args):

@@ -124,6 +124,8 @@ struct DecodePlan {
 
 constexpr int kTGran = 128;   // partition granularity (tokens)
 constexpr int kTMax = 8192;   // partition size limit (page ids a wave preloads)
+constexpr int kValuWgPerCu = 2;   // decode_valu workgroups per CU the planner counts on
+constexpr int kMfmaWgPerCu = 1;   // decode_mfma workgroups per CU the planner counts on
 
 attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *kv, const attn_opts *opts,
                         DecodePlan *pl, char **err) {
@@ -168,8 +170,14 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
     T = round_up(ceil_div(cap, opts->num_splits), kTGran);
   } else {
     const int64_t groups = (int64_t)io->batch * kv->num_kv_heads * pl->row_blocks;
-    const int per_cu = ctx->host_only ? (pl->mfma ? 1 : 3)
-                                      : pa::decode_blocks_per_cu(pl->mfma, kv->dtype, io->q_dtype, D, rows);
+    // Resident workgroups are counted at no more than kValuWgPerCu (VALU
+    // kernel) or kMfmaWgPerCu (MFMA kernel) per CU: that many already reach
+    // the HBM read rate, and the longer partitions leave fewer idle
+    // workgroups when sequences are shorter than the capacity.
+    const int cap_cu = pl->mfma ? kMfmaWgPerCu : kValuWgPerCu;
+    int per_cu = ctx->host_only ? cap_cu
+                                : pa::decode_blocks_per_cu(pl->mfma, kv->dtype, io->q_dtype, D, rows);
+    per_cu = std::max(1, std::min(per_cu, cap_cu));
     const int64_t slots = (int64_t)ctx->num_cus * per_cu;
     const int64_t target = std::max<int64_t>(1, slots / groups);
     T = std::max(tmin, round_up(ceil_div(cap, target), kTGran));

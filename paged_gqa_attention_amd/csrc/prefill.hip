@@ -2,7 +2,7 @@
 // block mask) over a paged K/V cache, for gfx950.
 //
 // A workgroup owns a 128-row query tile of HPW (1 or 2) query heads of one
-// KV group; each wave owns 64 rows of one head.  64-key K/V tiles are
+// KV group; each wave owns 32 rows of one head.  64-key K/V tiles are
 // gathered through the page table into LDS (double buffered) and shared by
 // all waves.  Per wave and tile:
 //     S^T = K Q^T        (32x32x16 MFMA, FP32 accumulators)
