@@ -3,6 +3,7 @@
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--all]
     python bench.py --only decode|prefill|copy [--steps K] [--warmup W]
     python bench.py --pmc-summary FETCH_DIR WRITE_DIR
+    python bench.py --counter-summary PMC_DIR
 
 Prints ONE JSON line.  ``value`` is paged decode throughput in GB/s of
 algorithmic HBM bytes (every live K/V element once, plus Q, O and the used
@@ -133,6 +134,20 @@ def pmc_summary(fetch_dir: str, write_dir: str):
     print(json.dumps(out))
 
 
+def counter_summary(directory: str):
+    """Mean per dispatch of every counter of this library's kernels in rocprofv3
+    --pmc CSV output (counters summed over their dimensions per dispatch)."""
+    per = {}
+    for kname, cn, v, did in _pmc_rows(directory):
+        if "pa::" not in kname:
+            continue
+        d = per.setdefault(kname, {}).setdefault(cn, {})
+        d[did] = d.get(did, 0.0) + v
+    out = {k: {cn: {"mean": sum(d.values()) / len(d), "dispatches": len(d)} for cn, d in cs.items()}
+           for k, cs in per.items()}
+    print(json.dumps(out, indent=1))
+
+
 def time_calls(fn, steps: int, warmup: int):
     import torch
     for _ in range(warmup):
@@ -147,6 +162,47 @@ def time_calls(fn, steps: int, warmup: int):
     e1.record(s)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps   # ms per call
+
+
+SCRUB_BYTES = 512 << 20
+
+
+def per_call_stats(fn, n: int = 50):
+    """Median / p10 / p90 of single calls, each after an untimed 512 MiB read that
+    evicts the 256 MiB Infinity Cache and the L2s (HIP events on the current stream)."""
+    import torch
+    scrub = torch.ones(SCRUB_BYTES // 4, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    fn()
+    for i in range(n):
+        scrub.sum()   # a read: evicts without leaving dirty lines to write back
+        ev[i][0].record(s)
+        fn()
+        ev[i][1].record(s)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    q = lambda f: t[min(n - 1, int(round(f * (n - 1))))]
+    return {"median": round(q(0.5), 5), "p10": round(q(0.1), 5), "p90": round(q(0.9), 5), "n": n,
+            "before_each": "512 MiB scrub read"}
+
+
+def read_ceiling(ctx, steps: int = 10):
+    """Read-only probe rates over 1 GiB: contiguous, and 4 KiB tiles in a shuffled order."""
+    import torch
+    import paged_gqa_attention_amd as pa
+    nbytes = 1 << 30
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    g = torch.Generator().manual_seed(7)
+    order = torch.randperm(nbytes // 4096, generator=g).to(torch.int32).cuda()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = {}
+    for name, pat, o in (("contiguous", 0, None), ("paged_4k_tiles", 1, order)):
+        ms = time_calls(lambda: pa.attn_debug_read_probe(ctx, buf, pat, o, sink), steps, 2)
+        out[name] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    out["unit"] = "GB/s"
+    return out
 
 
 def decode_setup(ctx, p, dev="cuda", num_splits=0):
@@ -244,9 +300,13 @@ def main():
     ap.add_argument("--all", action="store_true")
     ap.add_argument("--only", choices=["decode", "prefill", "copy"])
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--counter-summary", metavar="DIR")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path; "
@@ -283,12 +343,13 @@ def main():
     nbytes = acc.decode_bytes(p.seq_lens.tolist(), 1, 32, 8, 128, synth.DT_BF16,
                               synth.DT_BF16, synth.DT_BF16)
     gbs = nbytes / (ms * 1e-3) / 1e9
+    dec_pc = None if args.only else per_call_stats(call)
     dec_hash = _src_hash("decode.hip", "common.h")
     traffic = _traffic("decode_bf16_16k", dec_hash)
     roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": "decode_valu<bf16,bf16,128,4> + decode_merge (one attn_paged_decode call)",
-            "bytes_per_call": nbytes}
+            "bytes_per_call": nbytes, "per_call_ms": dec_pc}
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline_decode(p)   # the oracle copies the inputs to host memory
@@ -304,6 +365,7 @@ def main():
     pcall, pkeep = prefill_setup(ctx, pp, dev)
     psteps = max(3, args.steps // 2)
     pms = time_calls(pcall, psteps, max(1, args.warmup // 2))
+    pre_pc = per_call_stats(pcall, 20)
     flops = acc.attention_flops(acc.causal_pairs(8192, 8192), 64, 64, 16)
     tfs = flops / (pms * 1e-3) / 1e12
     pre_hash = _src_hash("prefill.hip", "common.h")
@@ -315,7 +377,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tfs, 1), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tfs / BF16_PEAK_TFLOPS, 4),
                      "traffic": _traffic("prefill_bf16_8k_b16", pre_hash),
-                     "kernel": "prefill_mfma<bf16,bf16,64,2,false>"},
+                     "kernel": "prefill_mfma<bf16,bf16,64,2,false>", "per_call_ms": pre_pc},
     }
     if not args.no_cpu:
         prefill["cpu_baseline"] = cpu_baseline_prefill(pp)
@@ -332,6 +394,7 @@ def main():
                    "num_splits": P, "tokens_per_split": T, "bytes_per_call": nbytes,
                    "input_gen_s": round(gen_s, 2)},
         "roofline": roof, "cpu_baseline": cpu, "prefill": prefill,
+        "read_ceiling": read_ceiling(ctx),
     }
     if args.all:
         extra(ctx, args)

@@ -200,6 +200,18 @@ attn_status attn_prefill_blocksparse(attn_ctx *ctx, const attn_io *io, const att
 attn_status attn_debug_gather_kv(attn_ctx *ctx, const attn_kv *kv, int32_t b, int32_t seq_len,
                                  float *k_out, float *v_out, void *hip_stream, char **err);
 
+/* Measurement hook: a read-only HBM probe, the practical read ceiling the
+ * decode kernels are compared with.  pattern 0 streams [buf, buf + bytes)
+ * contiguously; pattern 1 reads the 4 KiB tiles buf + 4096 * tile_order[i],
+ * i < bytes / 4096, in that order (tile_order: device int32 array whose
+ * entries lie in [0, bytes / 4096), trusted), the access pattern of a paged
+ * pool.  buf must be 16-byte aligned and bytes a positive multiple of 4096.
+ * `sink` (device, one word) is written only if the data XOR to a fixed
+ * constant: it exists so that no load can be optimised away. */
+attn_status attn_debug_read_probe(attn_ctx *ctx, const void *buf, size_t bytes, int32_t pattern,
+                                  const int32_t *tile_order, uint32_t *sink, void *hip_stream,
+                                  char **err);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,7 @@ _DT = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF
 EXPORTED = [
     "attn_abi_version", "attn_open", "attn_open_host_only", "attn_close", "attn_free",
     "attn_paged_decode_plan", "attn_paged_decode_workspace_bytes", "attn_paged_decode",
-    "attn_prefill", "attn_prefill_blocksparse", "attn_debug_gather_kv",
+    "attn_prefill", "attn_prefill_blocksparse", "attn_debug_gather_kv", "attn_debug_read_probe",
 ]
 
 
@@ -116,6 +116,8 @@ def load_library(path: str = LIB_PATH):
     lib.attn_debug_gather_kv.argtypes = [vp, P(attn_kv), ctypes.c_int32, ctypes.c_int32, vp, vp,
                                          vp, cp]
     lib.attn_debug_gather_kv.restype = st
+    lib.attn_debug_read_probe.argtypes = [vp, vp, ctypes.c_size_t, ctypes.c_int32, vp, vp, vp, cp]
+    lib.attn_debug_read_probe.restype = st
     _lib = lib
     return lib
 
@@ -315,6 +317,17 @@ def attn_debug_gather_kv(ctx: Context, kv: attn_kv, b: int, seq_len: int, k_out:
     err = ctypes.c_char_p()
     _check(lib.attn_debug_gather_kv(ctx.handle, ctypes.byref(kv), b, seq_len, _ptr(k_out),
                                     _ptr(v_out), _stream_ptr(stream), ctypes.byref(err)), err)
+
+
+def attn_debug_read_probe(ctx: Context, buf: torch.Tensor, pattern: int,
+                          tile_order: Optional[torch.Tensor], sink: torch.Tensor, stream=None):
+    """Read-only HBM probe over ``buf`` (pattern 0 contiguous, 1 4 KiB tiles in
+    ``tile_order``); a measurement hook."""
+    lib = load_library()
+    err = ctypes.c_char_p()
+    _check(lib.attn_debug_read_probe(ctx.handle, _ptr(buf), buf.numel() * buf.element_size(),
+                                     pattern, _ptr(tile_order), _ptr(sink), _stream_ptr(stream),
+                                     ctypes.byref(err)), err)
 
 
 # ---- convenience: whole calls on torch tensors -----------------------------------------

@@ -415,4 +415,26 @@ attn_status attn_debug_gather_kv(attn_ctx *ctx, const attn_kv *kv, int32_t b, in
                   err, "debug gather launch");
 }
 
+attn_status attn_debug_read_probe(attn_ctx *ctx, const void *buf, size_t bytes, int32_t pattern,
+                                  const int32_t *tile_order, uint32_t *sink, void *hip_stream,
+                                  char **err) {
+  attn_status st;
+  if ((st = check_ctx(ctx, err)) != ATTN_OK) return st;
+  if (!buf || !sink) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "buf / sink is NULL");
+  if (reinterpret_cast<uintptr_t>(buf) % 16 != 0)
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "buf is not 16-byte aligned");
+  if (bytes == 0 || bytes % 4096 != 0)
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "bytes must be a positive multiple of 4096");
+  if (pattern != 0 && pattern != 1) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "pattern must be 0 or 1");
+  if (pattern == 1 && !tile_order) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "tile_order is NULL");
+  if (pattern == 1 && bytes / 4096 > (size_t)INT32_MAX)
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "too many tiles");
+  if (ctx->host_only) return fail(err, ATTN_ERR_DEVICE, "host-only context: nothing enqueued");
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return fail(err, ATTN_ERR_DEVICE, "cannot select device %d", ctx->device);
+  return launched(pa::launch_read_probe(buf, bytes, pattern, tile_order, sink, ctx->num_cus,
+                                        (hipStream_t)hip_stream),
+                  err, "read probe launch");
+}
+
 }  // extern "C"

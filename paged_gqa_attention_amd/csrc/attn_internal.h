@@ -72,4 +72,8 @@ hipError_t launch_debug_gather(const void *k, const void *v, int64_t k_sp, int64
                                float k_scale, float v_scale, const int32_t *pt_row, int seq_len,
                                float *k_out, float *v_out, hipStream_t s);
 
+// read-only HBM probes (pattern 0: contiguous, 1: 4 KiB tiles in `order`)
+hipError_t launch_read_probe(const void *buf, size_t bytes, int pattern, const int32_t *order,
+                             uint32_t *sink, int num_cus, hipStream_t s);
+
 }  // namespace pa

@@ -186,3 +186,18 @@ def test_prefill_validation(hctx):
     # FP32 K/V prefill is not implemented
     io, kv, op = _prefill_args(dtype=torch.float32)
     assert _status(lambda: pa.attn_prefill(hctx, io, kv, op, stream=0)) == pa.ATTN_ERR_UNSUPPORTED
+
+
+def test_read_probe_validation(hctx):
+    buf = FakeTensor((1 << 20,), torch.uint8, 0x100000)
+    order = FakeTensor((256,), torch.int32, 0x200000)
+    sink = FakeTensor((1,), torch.int32, 0x300000)
+    probe = lambda b, pat, o, s: _status(lambda: pa.attn_debug_read_probe(hctx, b, pat, o, s, stream=0))
+    # valid requests validate, then a planning-only context enqueues nothing
+    assert probe(buf, 0, None, sink) == pa.ATTN_ERR_DEVICE
+    assert probe(buf, 1, order, sink) == pa.ATTN_ERR_DEVICE
+    assert probe(buf, 2, order, sink) == pa.ATTN_ERR_INVALID_ARGUMENT           # no such pattern
+    assert probe(buf, 1, None, sink) == pa.ATTN_ERR_INVALID_ARGUMENT            # tiles need an order
+    assert probe(buf, 0, None, None) == pa.ATTN_ERR_INVALID_ARGUMENT            # no sink
+    assert probe(FakeTensor((1000,), torch.uint8, 0x100000), 0, None, sink) == pa.ATTN_ERR_INVALID_ARGUMENT
+    assert probe(FakeTensor((4096,), torch.uint8, 0x100004), 0, None, sink) == pa.ATTN_ERR_INVALID_ARGUMENT
