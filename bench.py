@@ -205,6 +205,29 @@ def read_ceiling(ctx, steps: int = 10):
     return out
 
 
+def append_bench(ctx, B, n_new, Hkv, d, kv_dtype, src_dtype, steps, warmup):
+    """attn_kv_append of n_new rows per sequence into a shuffled page pool whose
+    sequences end exactly at the new rows; returns (ms per call, algorithmic bytes)."""
+    import torch
+    import paged_gqa_attention_amd as pa
+    import synth
+    pages_per_seq = (n_new + 15) // 16 + 1
+    npages = B * pages_per_seq
+    g = torch.Generator().manual_seed(11)
+    pt = torch.randperm(npages, generator=g).to(torch.int32).view(B, pages_per_seq).cuda()
+    lens = torch.full((B,), pages_per_seq * 16 - 5, dtype=torch.int32, device="cuda")
+    kp = torch.zeros((npages, Hkv, 16, d), dtype=kv_dtype, device="cuda")
+    vp = torch.zeros((npages, Hkv, d, 16), dtype=kv_dtype, device="cuda")
+    k, v = synth.append_rows(12, B, n_new, Hkv, d, dtype=src_dtype, device="cuda")
+    kv = pa.make_kv(kp, vp, pt, lens, 0.05 if kv_dtype == torch.float8_e4m3fn else 1.0,
+                    0.05 if kv_dtype == torch.float8_e4m3fn else 1.0)
+    rows = pa.make_rows(k, v)
+    ms = time_calls(lambda: pa.attn_kv_append(ctx, kv, rows), steps, warmup)
+    elt_src, elt_dst = k.element_size(), kp.element_size()
+    nbytes = 2 * B * n_new * Hkv * d * (elt_src + elt_dst) + 4 * B * ((n_new + 15) // 16 + 1)
+    return ms, nbytes
+
+
 def decode_setup(ctx, p, dev="cuda", num_splits=0):
     import torch
     import paged_gqa_attention_amd as pa
@@ -395,10 +418,30 @@ def main():
                    "input_gen_s": round(gen_s, 2)},
         "roofline": roof, "cpu_baseline": cpu, "prefill": prefill,
         "read_ceiling": read_ceiling(ctx),
+        "kv_append": kv_append_summary(ctx, args),
     }
     if args.all:
         extra(ctx, args)
     print(json.dumps(line), flush=True)
+
+
+def kv_append_summary(ctx, args):
+    """K/V append of a whole prefill (16 x 8,192 rows, Hkv=8, d=64, bf16 -> bf16)
+    against the HBM roofline, and one decode step's append (16 x 1 row, d=128)."""
+    import torch
+    ms, nbytes = append_bench(ctx, 16, 8192, 8, 64, torch.bfloat16, torch.bfloat16,
+                              args.steps, args.warmup)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    ms8, nb8 = append_bench(ctx, 16, 8192, 8, 64, torch.float8_e4m3fn, torch.bfloat16,
+                            args.steps, args.warmup)
+    ms1, _ = append_bench(ctx, 16, 1, 8, 128, torch.bfloat16, torch.bfloat16, args.steps, args.warmup)
+    torch.cuda.empty_cache()
+    return {"workload": "attn_kv_append 16 x 8192 rows, Hkv=8, d=64, bf16 -> bf16 pool",
+            "ms": round(ms, 4), "bytes_per_call": nbytes,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
+            "fp8_pool_GBs": round(nb8 / (ms8 * 1e-3) / 1e9, 1),
+            "decode_step_16x1_rows_d128_us": round(ms1 * 1e3, 2)}
 
 
 def only_prefill(ctx, args):

@@ -2,8 +2,9 @@
  * paged_attn.h - C ABI of the gfx950 (MI355X) paged grouped-query attention
  * library (libpaged_attn.so).
  *
- * Three operations, each defined by scaled dot-product attention over a
- * paged K/V cache with FP32 accumulation and FP32 softmax state:
+ * Three attention operations, each defined by scaled dot-product attention
+ * over a paged K/V cache with FP32 accumulation and FP32 softmax state, and
+ * the K/V append that fills the cache (attn_kv_append, below):
  *
  *   attn_paged_decode        decode / speculative verify: 1-8 query rows per
  *                            sequence, K/V split into partitions and merged
@@ -193,6 +194,35 @@ attn_status attn_prefill(attn_ctx *ctx, const attn_io *io, const attn_kv *kv,
 /* Block-sparse causal prefill: as attn_prefill, with block_mask required. */
 attn_status attn_prefill_blocksparse(attn_ctx *ctx, const attn_io *io, const attn_kv *kv,
                                      const attn_opts *opts, void *hip_stream, char **err);
+
+/* New K/V rows for attn_kv_append. */
+typedef struct {
+  const void *k, *v;            /* [batch][n_new][num_kv_heads][head_dim] through the strides */
+  int32_t dtype;                /* F32, F16 or BF16 */
+  int32_t batch;
+  int32_t n_new;                /* rows per sequence, >= 1 */
+  int32_t pad0;
+  int64_t stride_b, stride_row, stride_head;   /* elements, shared by k and v */
+} attn_kv_rows;
+
+/* K/V append, the step before decode / verify (Geramy/LSE README, "K/V
+ * storage": the cache is kept in 16-bit or FP8 storage; Geramy/LSE releases,
+ * v0.4.20, "Correctness": K/V writes checked against CPU references).
+ * Row i of sequence b (0 <= i < n_new) is written to position
+ * p = L_b - n_new + i, L_b = min(seq_lens[b], page_table_stride * 16), i.e.
+ * seq_lens already counts the new rows, as in the attention calls; rows with
+ * p < 0 are skipped.  Its K row goes to slot p % 16 of K tile
+ * (page_table[b][p / 16], head), its V row to the same slot of the V tile.
+ * The stored value is src / scale (k_scale or v_scale; one IEEE
+ * single-precision division) rounded to the pool's dtype to nearest, ties to
+ * even: F16 and BF16 overflow to infinity, FP8 e4m3fn saturates at +-448, NaN
+ * stays NaN (F32 stores the quotient).  Only those slots are written: the
+ * pool memory (k_pages / v_pages) must be writable, and the pages for the new
+ * positions must already be in the page table.  Base pointers and strides are
+ * 16-byte aligned, head_dim contiguous.  Appends of one call must not target
+ * the same slot twice (distinct sequences own distinct pages). */
+attn_status attn_kv_append(attn_ctx *ctx, const attn_kv *kv, const attn_kv_rows *rows,
+                           void *hip_stream, char **err);
 
 /* Test hook: gather sequence b's K and V through the page table and
  * dequantise them exactly as the attention kernels do, into FP32 arrays

@@ -77,6 +77,8 @@ def _load():
         _lib.orc_merge.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_void_p, ctypes.c_double, ctypes.c_void_p,
                                    ctypes.c_void_p]
+        _lib.orc_encode_array.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_float, ctypes.c_void_p]
         _lib.orc_attend_rows.restype = ctypes.c_int
         _lib.orc_attend_rows.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int64,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -209,3 +211,45 @@ def decode_codes(dtype: int, codes: np.ndarray) -> np.ndarray:
     out = np.zeros(codes.size, dtype=np.float64)
     lib.orc_decode_array(dtype, codes.ctypes.data, codes.size, out.ctypes.data)
     return out
+
+
+_CODE_NP = {0: np.uint32, 1: np.uint16, 2: np.uint16, 3: np.uint8}
+
+
+def encode(dtype: int, x, scale: float = 1.0) -> np.ndarray:
+    """Storage codes of float32 values x / scale in ``dtype`` (F32: the quotient's
+    bits): round-to-nearest-even, IEEE overflow to infinity, e4m3fn saturating
+    at +-448 (attn_oracle.c, "Encoding for the K/V append step")."""
+    lib = _load()
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    out = np.zeros(x.shape, dtype=_CODE_NP[dtype])
+    lib.orc_encode_array(dtype, x.size, x.ctypes.data, float(np.float32(scale)), out.ctypes.data)
+    return out
+
+
+def kv_append(kv_dtype: int, k_codes: np.ndarray, v_codes: np.ndarray, page_table: np.ndarray,
+              seq_lens: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, k_scale: float = 1.0,
+              v_scale: float = 1.0, page_size: int = 16):
+    """Expected K/V pools after appending n_new rows per sequence.
+
+    k_codes [pages][Hkv][16][d] and v_codes [pages][Hkv][d][16] hold storage codes;
+    k_new / v_new are float32 [B][n_new][Hkv][d] (the source rows, exactly
+    widened).  Row i of sequence b lands at position L_b - n_new + i, where
+    L_b = seq_lens[b] clamped to the page table's capacity; rows at negative
+    positions are dropped.  Everything else in the pools is left as it was.
+    """
+    B, n_new = k_new.shape[0], k_new.shape[1]
+    cap = page_table.shape[1] * page_size
+    kc = encode(kv_dtype, k_new, k_scale)
+    vc = encode(kv_dtype, v_new, v_scale)
+    k_out, v_out = k_codes.copy(), v_codes.copy()
+    for b in range(B):
+        L = min(int(seq_lens[b]), cap)
+        for i in range(n_new):
+            pos = L - n_new + i
+            if pos < 0:
+                continue
+            page, slot = int(page_table[b, pos // page_size]), pos % page_size
+            k_out[page, :, slot, :] = kc[b, i]
+            v_out[page, :, :, slot] = vc[b, i]
+    return k_out, v_out

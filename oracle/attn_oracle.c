@@ -302,3 +302,88 @@ int orc_attend_rows(const orc_problem *P, int64_t nrows, const int32_t *rows, do
     for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
   return nthreads;
 }
+
+/* ------------------------------------------------------------------------
+ * Encoding for the K/V append step.  The cache is kept in 16-bit or FP8
+ * storage (Geramy/LSE README, "K/V storage") and the writes into it are
+ * checked against CPU references (Geramy/LSE releases, v0.4.20,
+ * "Correctness").
+ *
+ * A stored value is the source value divided by the per-tensor scale (one
+ * IEEE single-precision division; the scale is 1 except for FP8), rounded to
+ * the storage format with round-to-nearest, ties to even (IEEE 754
+ * roundTiesToEven).  IEEE formats overflow to infinity; e4m3fn has no
+ * infinity, and a value beyond its largest finite magnitude (448) is stored as
+ * +-448 (saturation).  NaN stays NaN.
+ *
+ * The rounding is evaluated from the definition in double precision: the
+ * value's quantum (the spacing of the format's grid at its magnitude) is a
+ * power of two, so a / quantum is exact and rint() applies the tie rule.
+ * ------------------------------------------------------------------------ */
+
+/* code of a finite, non-negative grid value r of a format with eb exponent
+ * bits, mb mantissa bits and bias (2^(eb-1) - 1) */
+static uint32_t pack_grid_value(double r, int eb, int mb) {
+  const int bias = (1 << (eb - 1)) - 1;
+  const int emin = 1 - bias;
+  if (r == 0.0) return 0u;
+  int k;
+  (void)frexp(r, &k);
+  const int e = k - 1;                        /* r = 1.f * 2^e */
+  if (e < emin)                               /* subnormal: field 0 */
+    return (uint32_t)(r / ldexp(1.0, emin - mb));
+  const uint32_t field = (uint32_t)(e + bias);
+  const uint32_t mant = (uint32_t)(r / ldexp(1.0, e - mb)) - (1u << mb);
+  return (field << mb) | mant;
+}
+
+/* round-to-nearest-even of |x| onto the grid of a format with eb / mb bits */
+static double round_to_grid(double a, int eb, int mb) {
+  const int bias = (1 << (eb - 1)) - 1;
+  const int emin = 1 - bias;
+  if (a == 0.0) return 0.0;
+  int k;
+  (void)frexp(a, &k);
+  int e = k - 1;
+  if (e < emin) e = emin;
+  const double q = ldexp(1.0, e - mb);
+  return rint(a / q) * q;
+}
+
+/* IEEE binary16 (eb 5, mb 10) and bfloat16 (eb 8, mb 7) */
+static uint32_t enc_ieee(double x, int eb, int mb) {
+  const uint32_t sign = signbit(x) ? 1u : 0u;
+  const uint32_t sbit = sign << (eb + mb);
+  const uint32_t inf = ((1u << eb) - 1u) << mb;
+  if (isnan(x)) return sbit | inf | (1u << (mb - 1));          /* quiet NaN */
+  const double a = fabs(x);
+  const int bias = (1 << (eb - 1)) - 1;
+  const double maxfin = ldexp(2.0 - ldexp(1.0, -mb), ((1 << eb) - 2) - bias);
+  if (isinf(a)) return sbit | inf;
+  const double r = round_to_grid(a, eb, mb);
+  if (r > maxfin) return sbit | inf;
+  return sbit | pack_grid_value(r, eb, mb);
+}
+
+/* OCP e4m3fn: bias 7, no infinities, S.1111.111 is NaN, largest finite 448 */
+static uint32_t enc_e4m3fn(double x) {
+  const uint32_t sbit = signbit(x) ? 0x80u : 0u;
+  if (isnan(x)) return sbit | 0x7Fu;
+  const double a = fabs(x);
+  const double r = isinf(a) ? 448.0 : round_to_grid(a, 4, 3);
+  if (r >= 448.0) return sbit | 0x7Eu;                          /* saturate */
+  return sbit | pack_grid_value(r, 4, 3);
+}
+
+/* out[i] = code of x[i] / scale in `dtype` (F32 stores the quotient itself) */
+void orc_encode_array(int32_t dtype, int64_t n, const float *x, float scale, void *out) {
+  for (int64_t i = 0; i < n; ++i) {
+    const float y = x[i] / scale;              /* one IEEE single division */
+    switch (dtype) {
+      case ORC_F32: ((float *)out)[i] = y; break;
+      case ORC_F16: ((uint16_t *)out)[i] = (uint16_t)enc_ieee((double)y, 5, 10); break;
+      case ORC_BF16: ((uint16_t *)out)[i] = (uint16_t)enc_ieee((double)y, 8, 7); break;
+      default: ((uint8_t *)out)[i] = (uint8_t)enc_e4m3fn((double)y); break;
+    }
+  }
+}

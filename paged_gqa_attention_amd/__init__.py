@@ -31,7 +31,8 @@ _DT = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF
 EXPORTED = [
     "attn_abi_version", "attn_open", "attn_open_host_only", "attn_close", "attn_free",
     "attn_paged_decode_plan", "attn_paged_decode_workspace_bytes", "attn_paged_decode",
-    "attn_prefill", "attn_prefill_blocksparse", "attn_debug_gather_kv", "attn_debug_read_probe",
+    "attn_prefill", "attn_prefill_blocksparse", "attn_kv_append", "attn_debug_gather_kv",
+    "attn_debug_read_probe",
 ]
 
 
@@ -77,6 +78,16 @@ class attn_opts(ctypes.Structure):
     ]
 
 
+class attn_kv_rows(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32), ("batch", ctypes.c_int32),
+        ("n_new", ctypes.c_int32), ("pad0", ctypes.c_int32),
+        ("stride_b", ctypes.c_int64), ("stride_row", ctypes.c_int64),
+        ("stride_head", ctypes.c_int64),
+    ]
+
+
 _lib = None
 
 
@@ -116,6 +127,8 @@ def load_library(path: str = LIB_PATH):
     lib.attn_debug_gather_kv.argtypes = [vp, P(attn_kv), ctypes.c_int32, ctypes.c_int32, vp, vp,
                                          vp, cp]
     lib.attn_debug_gather_kv.restype = st
+    lib.attn_kv_append.argtypes = [vp, P(attn_kv), P(attn_kv_rows), vp, cp]
+    lib.attn_kv_append.restype = st
     lib.attn_debug_read_probe.argtypes = [vp, vp, ctypes.c_size_t, ctypes.c_int32, vp, vp, vp, cp]
     lib.attn_debug_read_probe.restype = st
     _lib = lib
@@ -214,6 +227,19 @@ def make_kv(k_pages: torch.Tensor, v_pages: torch.Tensor, page_table: torch.Tens
     return kv
 
 
+def make_rows(k: torch.Tensor, v: torch.Tensor) -> attn_kv_rows:
+    """New K/V rows [B][n_new][Hkv][d] (head_dim contiguous, k and v of one layout)."""
+    if k.dim() != 4 or v.shape != k.shape or v.dtype != k.dtype or v.stride() != k.stride():
+        raise AttnError(ATTN_ERR_INVALID_ARGUMENT, "k and v must be [B][n_new][Hkv][d] of one layout")
+    if k.stride(3) != 1:
+        raise AttnError(ATTN_ERR_INVALID_ARGUMENT, "head_dim must be contiguous")
+    r = attn_kv_rows()
+    r.k, r.v, r.dtype = _ptr(k), _ptr(v), _dtype(k)
+    r.batch, r.n_new = k.shape[0], k.shape[1]
+    r.stride_b, r.stride_row, r.stride_head = k.stride(0), k.stride(1), k.stride(2)
+    return r
+
+
 def make_io(q: torch.Tensor, o: torch.Tensor, lse: Optional[torch.Tensor] = None) -> attn_io:
     """Q and O as [B][rows][Hq][d] (head_dim contiguous); lse float32 [B][Hq][rows]."""
     if q.dim() != 4 or o.shape != q.shape:
@@ -309,6 +335,13 @@ def attn_prefill_blocksparse(ctx: Context, io: attn_io, kv: attn_kv, opts: attn_
     _check(lib.attn_prefill_blocksparse(ctx.handle, ctypes.byref(io), ctypes.byref(kv),
                                         ctypes.byref(opts), _stream_ptr(stream),
                                         ctypes.byref(err)), err)
+
+
+def attn_kv_append(ctx: Context, kv: attn_kv, rows: attn_kv_rows, stream=None):
+    lib = load_library()
+    err = ctypes.c_char_p()
+    _check(lib.attn_kv_append(ctx.handle, ctypes.byref(kv), ctypes.byref(rows), _stream_ptr(stream),
+                              ctypes.byref(err)), err)
 
 
 def attn_debug_gather_kv(ctx: Context, kv: attn_kv, b: int, seq_len: int, k_out: torch.Tensor,

@@ -415,6 +415,57 @@ attn_status attn_debug_gather_kv(attn_ctx *ctx, const attn_kv *kv, int32_t b, in
                   err, "debug gather launch");
 }
 
+attn_status attn_kv_append(attn_ctx *ctx, const attn_kv *kv, const attn_kv_rows *rows,
+                           void *hip_stream, char **err) {
+  attn_status st;
+  if ((st = check_ctx(ctx, err)) != ATTN_OK) return st;
+  if ((st = check_kv(kv, err)) != ATTN_OK) return st;
+  if (!rows) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "rows is NULL");
+  if (!rows->k || !rows->v) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "rows k / v is NULL");
+  if (rows->dtype != ATTN_F32 && rows->dtype != ATTN_F16 && rows->dtype != ATTN_BF16)
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "rows dtype must be F32, F16 or BF16");
+  if (rows->batch < 1 || rows->n_new < 1)
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "batch and n_new must be >= 1");
+  if (!aligned16(rows->k) || !aligned16(rows->v))
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "rows k and v must be 16-byte aligned");
+  const int sb = elt_bytes(rows->dtype);
+  const int64_t rs[3] = {rows->stride_b, rows->stride_row, rows->stride_head};
+  for (int i = 0; i < 3; ++i) {
+    if (rs[i] < 0) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "negative rows stride");
+    if ((rs[i] * sb) % 16) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "rows strides must be multiples of 16 bytes");
+  }
+  if (rows->stride_head < kv->head_dim)
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "rows head stride below head_dim");
+  if (ctx->host_only) return fail(err, ATTN_ERR_DEVICE, "host-only context: nothing enqueued");
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return fail(err, ATTN_ERR_DEVICE, "cannot select device %d", ctx->device);
+  pa::AppendArgs a{};
+  a.k_src = rows->k;
+  a.v_src = rows->v;
+  a.src_dtype = rows->dtype;
+  a.s_b = rows->stride_b;
+  a.s_r = rows->stride_row;
+  a.s_h = rows->stride_head;
+  a.k = const_cast<void *>(kv->k_pages);
+  a.v = const_cast<void *>(kv->v_pages);
+  a.k_sp = kv->k_stride_page;
+  a.k_sh = kv->k_stride_head;
+  a.v_sp = kv->v_stride_page;
+  a.v_sh = kv->v_stride_head;
+  a.kv_dtype = kv->dtype;
+  a.page_table = kv->page_table;
+  a.pt_stride = kv->page_table_stride;
+  a.capacity = (int32_t)std::min<int64_t>((int64_t)kv->page_table_stride * kPage, INT32_MAX);
+  a.lens = kv->seq_lens;
+  a.B = rows->batch;
+  a.n_new = rows->n_new;
+  a.Hkv = kv->num_kv_heads;
+  a.D = kv->head_dim;
+  a.k_scale = kv->k_scale;
+  a.v_scale = kv->v_scale;
+  return launched(pa::launch_kv_append(a, (hipStream_t)hip_stream), err, "K/V append launch");
+}
+
 attn_status attn_debug_read_probe(attn_ctx *ctx, const void *buf, size_t bytes, int32_t pattern,
                                   const int32_t *tile_order, uint32_t *sink, void *hip_stream,
                                   char **err) {

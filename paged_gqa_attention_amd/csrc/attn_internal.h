@@ -56,6 +56,24 @@ struct PrefillArgs {
   int32_t num_wg;         // total workgroups
 };
 
+// K/V append: new rows [B][n_new][Hkv][D] (source strides) into the paged pool
+struct AppendArgs {
+  const void *k_src, *v_src;
+  int32_t src_dtype;
+  int64_t s_b, s_r, s_h;  // source strides (elements)
+  void *k, *v;
+  int64_t k_sp, k_sh, v_sp, v_sh;
+  int32_t kv_dtype;
+  const int32_t *page_table;
+  int32_t pt_stride;
+  int32_t capacity;
+  const int32_t *lens;
+  int32_t B, n_new, Hkv, D;
+  float k_scale, v_scale;
+};
+
+hipError_t launch_kv_append(const AppendArgs &a, hipStream_t s);
+
 hipError_t launch_decode_valu(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t s);

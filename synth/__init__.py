@@ -370,3 +370,37 @@ def store_logical_kv(p: Problem, b: int, g: int, k=None, v=None):
                 pool[ids[pg], g, :, : t1 - t0] = blk.transpose(0, 1)
             else:
                 pool[ids[pg], g, : t1 - t0, :] = blk
+
+
+_CODE_VIEW = {torch.float32: torch.int32, torch.float16: torch.int16, torch.bfloat16: torch.int16,
+              torch.float8_e4m3fn: torch.uint8}
+_CODE_NP = {torch.float32: "uint32", torch.float16: "uint16", torch.bfloat16: "uint16",
+            torch.float8_e4m3fn: "uint8"}
+
+
+def pool_codes(pool: torch.Tensor):
+    """The raw storage codes of a K or V pool as a numpy array of unsigned ints."""
+    t = pool.detach().cpu().contiguous()
+    return t.view(_CODE_VIEW[t.dtype]).numpy().view(_CODE_NP[t.dtype])
+
+
+def with_pool_codes(p: Problem, k_codes, v_codes) -> Problem:
+    """A copy of p whose K/V pools hold the given raw storage codes."""
+    import copy
+    import numpy as np
+    q = copy.copy(p)
+    dt = p.k_pool.dtype
+    view = _CODE_VIEW[dt]
+    conv = lambda c: torch.from_numpy(np.ascontiguousarray(c).view(
+        {torch.int32: np.int32, torch.int16: np.int16, torch.uint8: np.uint8}[view])).view(dt)
+    q.k_pool, q.v_pool = conv(k_codes), conv(v_codes)
+    return q
+
+
+def append_rows(seed: int, batch: int, n_new: int, num_kv_heads: int, head_dim: int,
+                dtype=torch.bfloat16, device="cpu"):
+    """New K and V rows [B][n_new][Hkv][d] ~ N(0,1), rounded once to `dtype`."""
+    shape = (batch, n_new, num_kv_heads, head_dim)
+    k = normal(seed, 0, shape).to(dtype)
+    v = normal(seed, 1, shape).to(dtype)
+    return k.to(device), v.to(device)

@@ -201,3 +201,26 @@ def test_read_probe_validation(hctx):
     assert probe(buf, 0, None, None) == pa.ATTN_ERR_INVALID_ARGUMENT            # no sink
     assert probe(FakeTensor((1000,), torch.uint8, 0x100000), 0, None, sink) == pa.ATTN_ERR_INVALID_ARGUMENT
     assert probe(FakeTensor((4096,), torch.uint8, 0x100004), 0, None, sink) == pa.ATTN_ERR_INVALID_ARGUMENT
+
+
+def test_kv_append_validation(hctx):
+    _, kv, _ = _decode_args(B=2, R=1, Hq=8, Hkv=2, d=64, stride=8)
+    k = FakeTensor((2, 3, 2, 64), torch.bfloat16, 0x700000)
+    v = FakeTensor((2, 3, 2, 64), torch.bfloat16, 0x800000)
+    rows = pa.make_rows(k, v)
+    app = lambda r: _status(lambda: pa.attn_kv_append(hctx, kv, r, stream=0))
+    assert app(rows) == pa.ATTN_ERR_DEVICE                       # valid: nothing enqueued
+    bad = pa.make_rows(k, v)
+    bad.n_new = 0
+    assert app(bad) == pa.ATTN_ERR_INVALID_ARGUMENT
+    bad = pa.make_rows(k, v)
+    bad.dtype = pa.ATTN_FP8_E4M3                                 # rows are F32/F16/BF16
+    assert app(bad) == pa.ATTN_ERR_INVALID_ARGUMENT
+    bad = pa.make_rows(k, v)
+    bad.stride_row = 65                                          # 130 bytes: not 16-byte multiple
+    assert app(bad) == pa.ATTN_ERR_INVALID_ARGUMENT
+    bad = pa.make_rows(k, v)
+    bad.v = 0x800008
+    assert app(bad) == pa.ATTN_ERR_INVALID_ARGUMENT              # misaligned
+    kv.k_scale = 0.0
+    assert app(rows) == pa.ATTN_ERR_INVALID_ARGUMENT             # the scale divides
