@@ -143,85 +143,100 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
                              : nullptr;
 
   // ---- staging: global -> registers -> LDS.  The 4 page ids of a tile are
-  // workgroup-uniform scalar loads; then every thread issues its 16-byte loads.
+  // workgroup-uniform scalar loads.  Each wave's 64 consecutive 16-byte chunks
+  // of a K or V tile lie in one page, so a load is a wave-uniform page base
+  // (scalar 64-bit arithmetic) plus a per-lane offset inside the page that,
+  // like the chunk's LDS position, is the same for every tile and computed
+  // once here.
+  static_assert(64 % CPK == 0 && 16 % (64 / CPK) == 0, "a wave's K chunks span one page");
+  static_assert((D * ELT) % 64 == 0, "a wave's V chunks span one page");
+  const int64_t k_page_bytes = a.k_sp * ELT, v_page_bytes = a.v_sp * ELT;
+  int k_pg[KPT], v_pg[KPT];                 // page of the tile (wave-uniform)
+  uint32_t k_goff[KPT], v_goff[KPT];        // byte offset inside the page tile
+  uint32_t k_loff[KPT], v_loff[KPT];        // element offset inside an LDS buffer
+  int v_tok0[KPT];                          // first token of the V chunk in its tile
+#pragma unroll
+  for (int c = 0; c < KPT; ++c) {
+    const int ch = tid + c * NT;
+    const int key = ch / CPK, part = ch % CPK;
+    k_pg[c] = __builtin_amdgcn_readfirstlane(key >> 4);
+    k_goff[c] = (uint32_t)(((key & 15) * D + part * EPC) * ELT);
+    k_loff[c] = (uint32_t)(((key & ~31) | kperm(key & 31)) * KSTR + part * EPC);
+    const int vpg = ch / (D * ELT), cc = ch % (D * ELT);
+    const int d = cc / ELT, tg = cc % ELT;          // value row, token group
+    v_pg[c] = __builtin_amdgcn_readfirstlane(vpg);
+    v_goff[c] = (uint32_t)(cc * 16);
+    v_loff[c] = (uint32_t)(d * VSTR + 16 * vpg + tg * EPC);
+    v_tok0[c] = 16 * vpg + tg * EPC;
+  }
+
   u32x4 kreg[KPT], vreg[KPT];
   auto gload = [&](int t) {
     t = __builtin_amdgcn_readfirstlane(t);
-    int64_t pid[4];
+    int pid[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) pid[k] = pt[min(4 * t + k, npages - 1)];
 #pragma unroll
     for (int c = 0; c < KPT; ++c) {
       const int ch = tid + c * NT;
       if (KCH % NT == 0 || ch < KCH) {
-        const int key = ch / CPK, part = ch % CPK;
-        const int pg = key >> 4;
-        const int64_t p = pg == 0 ? pid[0] : pg == 1 ? pid[1] : pg == 2 ? pid[2] : pid[3];
-        kreg[c] = ld16(kbase + (p * a.k_sp + (key & 15) * D + part * EPC) * ELT);
-        const int vpg = ch / (D * ELT), cc = ch % (D * ELT);
-        const int64_t pv = vpg == 0 ? pid[0] : vpg == 1 ? pid[1] : vpg == 2 ? pid[2] : pid[3];
-        vreg[c] = ld16(vbase + (pv * a.v_sp + (int64_t)cc * EPC) * ELT);
+        const int kp = k_pg[c], vp = v_pg[c];
+        const int pk = kp == 0 ? pid[0] : kp == 1 ? pid[1] : kp == 2 ? pid[2] : pid[3];
+        const int pv = vp == 0 ? pid[0] : vp == 1 ? pid[1] : vp == 2 ? pid[2] : pid[3];
+        const char *kpage = kbase + (int64_t)__builtin_amdgcn_readfirstlane(pk) * k_page_bytes;
+        const char *vpage = vbase + (int64_t)__builtin_amdgcn_readfirstlane(pv) * v_page_bytes;
+        kreg[c] = ld16(kpage + k_goff[c]);
+        vreg[c] = ld16(vpage + v_goff[c]);
       }
     }
   };
   auto lstore = [&](int t, int buf) {
     const int kbase_tok = t * kTileK;
+    // V slots at or past the end may hold anything: zero them (last tile only)
+    const bool tail = kbase_tok + kTileK > L;
 #pragma unroll
     for (int c = 0; c < KPT; ++c) {
       const int ch = tid + c * NT;
       if (KCH % NT == 0 || ch < KCH) {
-        const int key = ch / CPK, part = ch % CPK;
-        const int krow = (key & ~31) | kperm(key & 31);
-        uint16_t *kdst = &k_lds[buf][krow * KSTR + part * EPC];
-        const int vpg = ch / (D * ELT), cc = ch % (D * ELT);
-        const int d = cc / ELT, tg = cc % ELT;          // value row, token group
-        const int tok0 = kbase_tok + 16 * vpg + tg * EPC;
-        uint16_t *vdst = &v_lds[buf][d * VSTR + 16 * vpg + tg * EPC];
+        uint16_t *kdst = &k_lds[buf][k_loff[c]];
+        uint16_t *vdst = &v_lds[buf][v_loff[c]];
+        constexpr int NQ = EPC / 8;   // 16-byte LDS words per V chunk
+        u32x4 vv[NQ];
         if constexpr (KVDT == DT_FP8) {
-          u32x4 lo, hi, v0, v1;
+          u32x4 lo, hi;
 #pragma unroll
           for (int w = 0; w < 2; ++w) {
             lo[2 * w] = fp8x2_to_16<F16, false>(kreg[c][w]);
             lo[2 * w + 1] = fp8x2_to_16<F16, true>(kreg[c][w]);
             hi[2 * w] = fp8x2_to_16<F16, false>(kreg[c][w + 2]);
             hi[2 * w + 1] = fp8x2_to_16<F16, true>(kreg[c][w + 2]);
-            v0[2 * w] = fp8x2_to_16<F16, false>(vreg[c][w]);
-            v0[2 * w + 1] = fp8x2_to_16<F16, true>(vreg[c][w]);
-            v1[2 * w] = fp8x2_to_16<F16, false>(vreg[c][w + 2]);
-            v1[2 * w + 1] = fp8x2_to_16<F16, true>(vreg[c][w + 2]);
           }
           *reinterpret_cast<u32x4 *>(kdst) = lo;
           *reinterpret_cast<u32x4 *>(kdst + 8) = hi;
-          u32x4 vv[2] = {v0, v1};
-          if (tok0 + EPC > L) {  // slots at or past the end may hold anything: zero them
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int tk = tok0 + 8 * q + 2 * e;
-                uint32_t wv = vv[q][e];
-                if (tk >= L) wv &= 0xffff0000u;
-                if (tk + 1 >= L) wv &= 0x0000ffffu;
-                vv[q][e] = wv;
-              }
+          for (int w = 0; w < 4; ++w) {
+            vv[w >> 1][2 * (w & 1)] = fp8x2_to_16<F16, false>(vreg[c][w]);
+            vv[w >> 1][2 * (w & 1) + 1] = fp8x2_to_16<F16, true>(vreg[c][w]);
           }
-          *reinterpret_cast<u32x4 *>(vdst) = vv[0];
-          *reinterpret_cast<u32x4 *>(vdst + 8) = vv[1];
         } else {
           *reinterpret_cast<u32x4 *>(kdst) = kreg[c];
-          u32x4 vv = vreg[c];
-          if (tok0 + EPC > L) {
+          vv[0] = vreg[c];
+        }
+        if (tail) {
+          const int tok0 = kbase_tok + v_tok0[c];
+#pragma unroll
+          for (int q = 0; q < NQ; ++q)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int tk = tok0 + 2 * e;
-              uint32_t wv = vv[e];
+              const int tk = tok0 + 8 * q + 2 * e;
+              uint32_t wv = vv[q][e];
               if (tk >= L) wv &= 0xffff0000u;
               if (tk + 1 >= L) wv &= 0x0000ffffu;
-              vv[e] = wv;
+              vv[q][e] = wv;
             }
-          }
-          *reinterpret_cast<u32x4 *>(vdst) = vv;
         }
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) *reinterpret_cast<u32x4 *>(vdst + 8 * q) = vv[q];
       }
     }
   };
