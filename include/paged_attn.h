@@ -32,6 +32,10 @@
  *     o = sum_j e^{s_j - m} v_j / Z,  lse = m + ln Z.
  * No sink means sink_h = -inf.  A row with no allowed key gets o = 0 and
  * lse = sink_h (-inf without sinks).
+ * Ragged rows: with attn_opts.rows_per_seq, sequence b has only its first
+ * n_b = rows_per_seq[b] rows (n = n_b above, so they sit at its last n_b
+ * positions); the O and lse entries of its rows n_b .. q_rows-1 are left
+ * untouched.
  *
  * Memory layout (all device memory, element strides):
  *   K pool   tile (page, kv_head) at k_pages + page*k_stride_page +
@@ -85,7 +89,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 typedef enum {
   ATTN_OK = 0,
@@ -142,6 +146,9 @@ typedef struct {
   int32_t mask_heads;           /* 1 (shared) or num_kv_heads */
   int32_t mask_block;           /* tokens per mask block: a multiple of 64 */
   int32_t mask_q_blocks, mask_k_blocks;
+  const int32_t *rows_per_seq;  /* nullable device int32 [batch]: query rows of each
+                                   sequence (ragged verify / chunked prefill), values
+                                   clamped to [0, q_rows]; see "Semantics" */
 } attn_opts;
 
 /* ABI version of the loaded library (ATTN_ABI_VERSION). */

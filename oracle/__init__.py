@@ -55,6 +55,7 @@ class _Problem(ctypes.Structure):
         ("mask", ctypes.c_void_p),
         ("mask_heads", ctypes.c_int32), ("mask_block", ctypes.c_int32),
         ("mask_nqb", ctypes.c_int32), ("mask_nkb", ctypes.c_int32),
+        ("rows_per_seq", ctypes.c_void_p),
     ]
 
 
@@ -103,6 +104,8 @@ class OracleProblem:
         self.q = cpu(p.q)
         self.sinks = cpu(p.sinks).to(torch.float32) if p.sinks is not None else None
         self.mask = cpu(p.mask).to(torch.uint8) if p.mask is not None else None
+        rps = getattr(p, "rows_per_seq", None)
+        self.rows_per_seq = cpu(rps).to(torch.int32) if rps is not None else None
         d, hkv, page = p.head_dim, p.num_kv_heads, self.k.shape[2]
         s = _Problem()
         s.kv_dtype = p.kv_dtype
@@ -128,6 +131,7 @@ class OracleProblem:
         else:
             s.mask = None
             s.mask_heads, s.mask_block, s.mask_nqb, s.mask_nkb = 1, 128, 0, 0
+        s.rows_per_seq = self.rows_per_seq.data_ptr() if self.rows_per_seq is not None else None
         self.struct = s
 
     def all_rows(self) -> np.ndarray:

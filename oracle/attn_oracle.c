@@ -26,7 +26,8 @@
  *
  * Readings where the pages are silent (kept identical on the GPU side):
  *   query head h uses KV head floor(h / G), G = Hq / Hkv;
- *   row i of n_q rows sits at absolute position L - n_q + i (bottom-right
+ *   row i of the n rows of a sequence (n = n_q, or the sequence's own row
+ *   count when rows vary per sequence) sits at absolute position L - n + i (bottom-right
  *   causal alignment) and sees keys j <= that position;
  *   a sink is one logit per query head in the units of the scaled score,
  *   natural base, contributing exp(sink) to the denominator and no value;
@@ -61,6 +62,7 @@ typedef struct {
   const float *sinks;            /* NULL or [Hq] */
   const uint8_t *mask;           /* NULL or [batch][mask_heads][mask_nqb][mask_nkb] */
   int32_t mask_heads, mask_block, mask_nqb, mask_nkb;
+  const int32_t *rows_per_seq;   /* NULL or [batch]: sequence b has rows 0 .. r_b - 1 */
 } orc_problem;
 
 /* ---- storage decoding (bit formulas, one per format) ---------------------- */
@@ -158,6 +160,11 @@ static int key_allowed(const orc_problem *P, int b, int g, int64_t pos, int64_t 
   return P->mask[idx] != 0;
 }
 
+/* rows of sequence b (all n_q unless they vary per sequence) */
+static int64_t rows_of(const orc_problem *P, int b) {
+  return P->rows_per_seq ? P->rows_per_seq[b] : P->n_q;
+}
+
 static double scale_of(const orc_problem *P) {
   return P->softmax_scale > 0 ? P->softmax_scale : 1.0 / sqrt((double)P->head_dim);
 }
@@ -184,7 +191,7 @@ static double score(const orc_problem *P, const double *q, int b, int g, int64_t
 void orc_attend_partial(const orc_problem *P, int b, int i, int h, int64_t j0, int64_t j1,
                         double *o, double *m_out, double *l_out) {
   int G = P->num_q_heads / P->num_kv_heads, g = h / G, d = P->head_dim;
-  int64_t L = P->seq_lens[b], pos = L - P->n_q + i;
+  int64_t L = P->seq_lens[b], pos = L - rows_of(P, b) + i;
   if (j1 > L) j1 = L;
   double q[1024];
   load_query(P, b, i, h, q);
@@ -235,8 +242,13 @@ void orc_merge(int n, int d, const double *o_parts, const double *m, const doubl
 static void attend_row(const orc_problem *P, int b, int i, int h, double *o, double *lse,
                        double *s_buf) {
   int G = P->num_q_heads / P->num_kv_heads, g = h / G, d = P->head_dim;
-  int64_t L = P->seq_lens[b], pos = L - P->n_q + i;
+  int64_t L = P->seq_lens[b], pos = L - rows_of(P, b) + i;
   double sink = P->sinks ? (double)P->sinks[h] : -INFINITY;
+  if (i >= rows_of(P, b)) {            /* no such row: marked NaN (not part of the output) */
+    for (int c = 0; c < d; ++c) o[c] = NAN;
+    *lse = NAN;
+    return;
+  }
   double q[1024];
   load_query(P, b, i, h, q);
   double m = sink;

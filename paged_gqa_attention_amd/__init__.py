@@ -28,6 +28,8 @@ ATTN_F32, ATTN_F16, ATTN_BF16, ATTN_FP8_E4M3 = 0, 1, 2, 3
 _DT = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16,
        torch.float8_e4m3fn: ATTN_FP8_E4M3}
 
+ABI_VERSION = 2   # include/paged_attn.h ATTN_ABI_VERSION
+
 EXPORTED = [
     "attn_abi_version", "attn_open", "attn_open_host_only", "attn_close", "attn_free",
     "attn_paged_decode_plan", "attn_paged_decode_workspace_bytes", "attn_paged_decode",
@@ -75,6 +77,7 @@ class attn_opts(ctypes.Structure):
         ("sinks", ctypes.c_void_p), ("block_mask", ctypes.c_void_p),
         ("mask_heads", ctypes.c_int32), ("mask_block", ctypes.c_int32),
         ("mask_q_blocks", ctypes.c_int32), ("mask_k_blocks", ctypes.c_int32),
+        ("rows_per_seq", ctypes.c_void_p),
     ]
 
 
@@ -100,6 +103,10 @@ def load_library(path: str = LIB_PATH):
         raise AttnError(ATTN_ERR_DEVICE, f"{path} is not built; run "
                         "`python -m paged_gqa_attention_amd.build`")
     lib = ctypes.CDLL(path)
+    lib.attn_abi_version.restype = ctypes.c_int
+    if lib.attn_abi_version() != ABI_VERSION:
+        raise AttnError(ATTN_ERR_DEVICE, f"{path} has ABI {lib.attn_abi_version()}, the binding "
+                        f"expects {ABI_VERSION}: rebuild it")
     P = ctypes.POINTER
     vp, st, cp = ctypes.c_void_p, ctypes.c_int, P(ctypes.c_char_p)
     lib.attn_abi_version.restype = ctypes.c_int
@@ -263,8 +270,13 @@ def make_io(q: torch.Tensor, o: torch.Tensor, lse: Optional[torch.Tensor] = None
 
 def make_opts(softmax_scale: float = 0.0, sinks: Optional[torch.Tensor] = None,
               block_mask: Optional[torch.Tensor] = None, mask_block: int = 128,
-              num_splits: int = 0) -> attn_opts:
+              num_splits: int = 0, rows_per_seq: Optional[torch.Tensor] = None) -> attn_opts:
+    """rows_per_seq: optional int32 [B], the query rows of each sequence (ragged)."""
     op = attn_opts()
+    if rows_per_seq is not None and (rows_per_seq.dtype != torch.int32 or
+                                     not rows_per_seq.is_contiguous()):
+        raise AttnError(ATTN_ERR_INVALID_ARGUMENT, "rows_per_seq must be contiguous int32 [B]")
+    op.rows_per_seq = _ptr(rows_per_seq)
     op.softmax_scale = float(softmax_scale)
     op.num_splits = int(num_splits)
     if sinks is not None and (sinks.dtype != torch.float32 or not sinks.is_contiguous()):
@@ -282,7 +294,7 @@ def make_opts(softmax_scale: float = 0.0, sinks: Optional[torch.Tensor] = None,
         op.block_mask = None
         op.mask_heads, op.mask_q_blocks, op.mask_k_blocks = 1, 1, 1
     op.mask_block = int(mask_block)
-    op._keep = (sinks, block_mask)
+    op._keep = (sinks, block_mask, rows_per_seq)
     return op
 
 
@@ -373,13 +385,14 @@ def decode_workspace(ctx: Context, io: attn_io, kv: attn_kv, opts: attn_opts, de
 
 def paged_decode(ctx: Context, q, k_pages, v_pages, page_table, seq_lens, *, k_scale=1.0,
                  v_scale=1.0, softmax_scale=0.0, sinks=None, out=None, out_dtype=None,
-                 lse=None, num_splits=0, workspace=None, stream=None):
-    """Decode / verify rows ``q`` [B][R][Hq][d]; returns the output tensor."""
+                 lse=None, num_splits=0, workspace=None, stream=None, rows_per_seq=None):
+    """Decode / verify rows ``q`` [B][R][Hq][d]; returns the output tensor.  With
+    ``rows_per_seq`` (int32 [B]) sequence b has only its first rows_per_seq[b] rows."""
     o = out if out is not None else torch.empty(q.shape, dtype=out_dtype or q.dtype,
                                                  device=q.device)
     io = make_io(q, o, lse)
     kv = make_kv(k_pages, v_pages, page_table, seq_lens, k_scale, v_scale)
-    op = make_opts(softmax_scale, sinks, None, 128, num_splits)
+    op = make_opts(softmax_scale, sinks, None, 128, num_splits, rows_per_seq)
     if workspace is None:
         workspace = decode_workspace(ctx, io, kv, op, q.device)
     attn_paged_decode(ctx, io, kv, op, workspace, stream)
@@ -388,13 +401,14 @@ def paged_decode(ctx: Context, q, k_pages, v_pages, page_table, seq_lens, *, k_s
 
 def prefill(ctx: Context, q, k_pages, v_pages, page_table, seq_lens, *, k_scale=1.0,
             v_scale=1.0, softmax_scale=0.0, sinks=None, out=None, out_dtype=None, lse=None,
-            block_mask=None, mask_block=128, stream=None):
-    """Causal (optionally block-sparse) prefill of ``q`` [B][S_q][Hq][d]."""
+            block_mask=None, mask_block=128, stream=None, rows_per_seq=None):
+    """Causal (optionally block-sparse) prefill of ``q`` [B][S_q][Hq][d]; with
+    ``rows_per_seq`` (int32 [B]) sequence b has only its first rows_per_seq[b] rows."""
     o = out if out is not None else torch.empty(q.shape, dtype=out_dtype or q.dtype,
                                                  device=q.device)
     io = make_io(q, o, lse)
     kv = make_kv(k_pages, v_pages, page_table, seq_lens, k_scale, v_scale)
-    op = make_opts(softmax_scale, sinks, block_mask, mask_block)
+    op = make_opts(softmax_scale, sinks, block_mask, mask_block, rows_per_seq=rows_per_seq)
     if block_mask is None:
         attn_prefill(ctx, io, kv, op, stream)
     else:

@@ -136,6 +136,8 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
   if (!opts) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "opts is NULL");
   if (opts->block_mask) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "attn_paged_decode takes no block mask");
   if (opts->num_splits < 0) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "num_splits must be >= 0");
+  if (reinterpret_cast<uintptr_t>(opts->rows_per_seq) & 3u)
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "rows_per_seq must be 4-byte aligned");
   if (io->q_rows > 8) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "decode q_rows %d outside [1, 8]", io->q_rows);
   const int G = io->num_q_heads / kv->num_kv_heads;
   const int rows = G * io->q_rows;
@@ -228,6 +230,8 @@ attn_status prefill_common(attn_ctx *ctx, const attn_io *io, const attn_kv *kv, 
   if ((st = check_io(io, kv, err)) != ATTN_OK) return st;
   if (!opts) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "opts is NULL");
   if (!sparse && opts->block_mask) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "attn_prefill takes no block mask (use attn_prefill_blocksparse)");
+  if (reinterpret_cast<uintptr_t>(opts->rows_per_seq) & 3u)
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "rows_per_seq must be 4-byte aligned");
   if (sparse) {
     if (!opts->block_mask) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "attn_prefill_blocksparse needs a block mask");
     if (opts->mask_block < 64 || opts->mask_block % 64)
@@ -259,6 +263,7 @@ attn_status prefill_common(attn_ctx *ctx, const attn_io *io, const attn_kv *kv, 
   a.o = io->o;
   a.o_sb = io->o_stride_b; a.o_sr = io->o_stride_row; a.o_sh = io->o_stride_head;
   a.lse = io->lse;
+  a.rows_b = opts->rows_per_seq;
   a.mask = sparse ? opts->block_mask : nullptr;
   a.mask_heads = opts->mask_heads; a.mask_block = opts->mask_block;
   a.mask_nqb = opts->mask_q_blocks; a.mask_nkb = opts->mask_k_blocks;
@@ -371,6 +376,7 @@ attn_status attn_paged_decode(attn_ctx *ctx, const attn_io *io, const attn_kv *k
   a.o = io->o;
   a.o_sb = io->o_stride_b; a.o_sr = io->o_stride_row; a.o_sh = io->o_stride_head;
   a.lse = io->lse;
+  a.rows_b = opts->rows_per_seq;
   a.P = pl.P; a.T = pl.T;
   a.row_blocks = pl.row_blocks;
   a.ws_o = reinterpret_cast<float *>(workspace);

@@ -6,6 +6,11 @@
 
 namespace pa {
 
+// rows of sequence b: all R, or the per-sequence count clamped to [0, R]
+__device__ __forceinline__ int seq_rows(const int32_t *rows_b, int b, int R) {
+  return rows_b ? min(max(rows_b[b], 0), R) : R;
+}
+
 // Everything a decode launch needs; all pointers are device pointers.
 struct DecodeArgs {
   const void *q;
@@ -30,6 +35,7 @@ struct DecodeArgs {
   int32_t row_blocks;     // VALU path: ceil(rows / rows_per_block)
   float *ws_o;            // [B][Hkv][rows][P][D]   unnormalised partial outputs
   float *ws_ml;           // [B][Hkv][rows][P][2]   partial max (log2 units) and sum
+  const int32_t *rows_b;  // nullable [B]: rows of each sequence (<= R); the rest are skipped
 };
 
 struct PrefillArgs {
@@ -51,6 +57,7 @@ struct PrefillArgs {
   float *lse;             // nullable [B][Hq][n_q]
   const uint8_t *mask;    // nullable
   int32_t mask_heads, mask_block, mask_nqb, mask_nkb;
+  const int32_t *rows_b;  // nullable [B]: rows of each sequence (<= n_q); the rest are skipped
   int32_t q_tiles;        // ceil(n_q / 128)
   int32_t heads_per_wg;   // 1 or 2 query heads of one group per workgroup
   int32_t num_wg;         // total workgroups

@@ -133,7 +133,8 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rr = blockIdx.x * kWaves + wave, kvh = blockIdx.y, b = blockIdx.z;
-  if (rr < a.rows) merge_row<D>(a, b, kvh, rr, lane);
+  // rows past a sequence's own row count are not part of the output
+  if (rr < a.rows && rr % a.R < seq_rows(a.rows_b, b, a.R)) merge_row<D>(a, b, kvh, rr, lane);
 }
 
 // ==================================================================================
@@ -211,11 +212,12 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
     }
   };
   // position of the rows this lane handles in the softmax: r = qq + 4k
+  const int nrows = seq_rows(a.rows_b, b, a.R);   // rows of this sequence
   int pos_mine[MR];
 #pragma unroll
   for (int k = 0; k < MR; ++k) {
     const int rr = rb * RB + qq + 4 * k;
-    pos_mine[k] = rr < a.rows ? L - a.R + rr % a.R : -1;
+    pos_mine[k] = (rr < a.rows && rr % a.R < nrows) ? L - nrows + rr % a.R : -1;
   }
 
   float m_run[MR], l_run[MR];
@@ -497,6 +499,7 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
 
   // ---- Q^T fragments: B[k = d][n = row] ----
   u32x4 qf[NB][KC];
+  const int nrows = seq_rows(a.rows_b, b, a.R);   // rows of this sequence
   int pos[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -504,7 +507,7 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
     const bool ok = rr < a.rows;
     const int h = kvh * a.G + (ok ? rr / a.R : 0);
     const int i = ok ? rr % a.R : 0;
-    pos[nb] = ok ? L - a.R + i : -1;
+    pos[nb] = (ok && i < nrows) ? L - nrows + i : -1;
     const char *qrow = reinterpret_cast<const char *>(a.q) +
                        ((int64_t)b * a.q_sb + (int64_t)i * a.q_sr + (int64_t)h * a.q_sh) * 2;
 #pragma unroll

@@ -99,24 +99,26 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
   const int h = kvh * a.G + hp * HPW + (wave >> 2);
   const int q0 = qt * kTileQ + (wave & 3) * 32;  // first row of this wave
   const int L = min(a.lens[b], a.capacity);
-  const int off = L - a.n_q;                      // position of row i is off + i
+  const int nq = seq_rows(a.rows_b, b, a.n_q);    // rows of this sequence
+  if (qt * kTileQ >= nq) return;                  // the whole workgroup has no rows
+  const int off = L - nq;                         // position of row i is off + i
   const int nl = lane & 31, hh = lane >> 5;
   const int npages = (L + kPage - 1) / kPage;
 
-  const int tile_last = min(qt * kTileQ + kTileQ, a.n_q) - 1;
-  const int wave_last = min(q0 + 32, a.n_q) - 1;
-  const bool wave_has_rows = q0 < a.n_q;
+  const int tile_last = min(qt * kTileQ + kTileQ, nq) - 1;
+  const int wave_last = min(q0 + 32, nq) - 1;
+  const bool wave_has_rows = q0 < nq;
   const int key_end = min(L, off + tile_last + 1);  // keys any row of the tile can see
   const int nt = key_end > 0 ? (key_end + kTileK - 1) / kTileK : 0;
   const int wave_key_end = wave_has_rows ? min(L, off + wave_last + 1) : 0;
   const int wave_first_pos = off + q0;
   const int row = q0 + nl;
-  const int pos_row = row < a.n_q ? off + row : -1;
+  const int pos_row = row < nq ? off + row : -1;
 
   // ---- Q^T fragments: B[k = d][n = row]; lane (row nl, k half hh) ----
   u32x4 qf[KS];
   {
-    const bool ok = row < a.n_q;
+    const bool ok = row < nq;
     const char *qrow = reinterpret_cast<const char *>(a.q) +
                        ((int64_t)b * a.q_sb + (int64_t)(ok ? row : 0) * a.q_sr +
                         (int64_t)h * a.q_sh) * 2;
@@ -414,7 +416,7 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
     scale_o = em * a.v_scale / Z;
     lse = (M + __builtin_log2f(Z)) * kLn2;
   }
-  if (row < a.n_q) {
+  if (row < nq) {
     char *obase = reinterpret_cast<char *>(a.o);
     const int64_t orow = (int64_t)b * a.o_sb + (int64_t)row * a.o_sr + (int64_t)h * a.o_sh;
 #pragma unroll

@@ -146,6 +146,8 @@ class Problem:
     mask_block: int = 128
     seed: int = 0
     meta: dict = field(default_factory=dict)
+    rows_per_seq: Optional[torch.Tensor] = None   # int32 [B]: valid rows of each sequence
+
 
     @property
     def num_pages(self) -> int:
@@ -225,9 +227,11 @@ def _build_pool(seed, lens, stride, hkv, d, kv_dtype, pool_pages=None, device="c
 
 def make_decode(seed, batch, num_q_heads, num_kv_heads, head_dim, lens, q_rows,
                 kv_dtype=DT_BF16, q_dtype=None, o_dtype=None, stride=None, sinks=False,
-                softmax_scale=0.0, device="cpu", extra_pages=0) -> Problem:
+                softmax_scale=0.0, device="cpu", extra_pages=0, rows_per_seq=None) -> Problem:
     """Paged decode / speculative-verify problem: ``q_rows`` rows per sequence
-    sit at the last q_rows positions of each sequence (lens include them)."""
+    sit at the last q_rows positions of each sequence (lens include them).
+    With ``rows_per_seq`` (a list, each <= q_rows) sequence b has only its first
+    rows_per_seq[b] rows, at its last rows_per_seq[b] positions."""
     lens = [int(x) for x in lens]
     assert len(lens) == batch
     if stride is None:
@@ -242,9 +246,14 @@ def make_decode(seed, batch, num_q_heads, num_kv_heads, head_dim, lens, q_rows,
     sk = None
     if sinks:
         sk = normal(seed, 4, (num_q_heads,), device).to(torch.float32)
-    return Problem("decode", batch, q_rows, num_q_heads, num_kv_heads, head_dim, kv_dtype,
-                   q_dtype, o_dtype, torch.tensor(lens, dtype=torch.int32, device=device), pt,
-                   k_pool, v_pool, q, ks, vs, softmax_scale, sk, None, 128, seed)
+    p = Problem("decode", batch, q_rows, num_q_heads, num_kv_heads, head_dim, kv_dtype,
+                q_dtype, o_dtype, torch.tensor(lens, dtype=torch.int32, device=device), pt,
+                k_pool, v_pool, q, ks, vs, softmax_scale, sk, None, 128, seed)
+    if rows_per_seq is not None:
+        assert len(rows_per_seq) == batch and all(0 <= r <= q_rows for r in rows_per_seq)
+        p.rows_per_seq = torch.tensor([int(r) for r in rows_per_seq], dtype=torch.int32,
+                                      device=device)
+    return p
 
 
 def make_prefill(seed, batch, num_q_heads, num_kv_heads, head_dim, seq_len, q_rows=None,

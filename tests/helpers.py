@@ -38,6 +38,7 @@ class Dev:
         self.q = p.q.to(dev)
         self.sinks = p.sinks.to(dev) if p.sinks is not None else None
         self.mask = p.mask.to(dev) if p.mask is not None else None
+        self.rows = p.rows_per_seq.to(dev) if p.rows_per_seq is not None else None
         self.o_dtype = synth.TORCH_DTYPE[p.o_dtype]
 
 
@@ -50,17 +51,23 @@ def run(d: Dev, lse: bool = True, num_splits: int = 0, out_dtype=None):
     if p.kind == "decode":
         pa.paged_decode(ctx(), d.q, d.k, d.v, d.pt, d.lens, k_scale=p.k_scale, v_scale=p.v_scale,
                         softmax_scale=p.softmax_scale, sinks=d.sinks, out=o, lse=lse_t,
-                        num_splits=num_splits)
+                        num_splits=num_splits, rows_per_seq=d.rows)
     else:
         pa.prefill(ctx(), d.q, d.k, d.v, d.pt, d.lens, k_scale=p.k_scale, v_scale=p.v_scale,
                    softmax_scale=p.softmax_scale, sinks=d.sinks, out=o, lse=lse_t,
-                   block_mask=d.mask, mask_block=p.mask_block)
+                   block_mask=d.mask, mask_block=p.mask_block, rows_per_seq=d.rows)
     torch.cuda.synchronize()
     return (o.to(torch.float64).cpu().numpy(),
             lse_t.to(torch.float64).cpu().numpy() if lse else None)
 
 
 def max_err(o_gpu, o_ref):
+    # rows the oracle marks NaN do not exist (ragged rows): the GPU must have
+    # left them untouched (run() pre-fills the outputs with NaN)
+    absent = np.isnan(o_ref)
+    if absent.any():
+        assert np.all(np.isnan(o_gpu[absent])), "a row past its sequence's row count was written"
+        o_gpu, o_ref = np.where(absent, 0.0, o_gpu), np.where(absent, 0.0, o_ref)
     diff = np.abs(o_gpu - o_ref)
     if np.isnan(diff).any():
         return math.inf, np.unravel_index(np.argmax(np.isnan(diff)), diff.shape)
@@ -69,6 +76,10 @@ def max_err(o_gpu, o_ref):
 
 
 def lse_err(l_gpu, l_ref):
+    absent = np.isnan(l_ref)
+    if absent.any():
+        assert np.all(np.isnan(l_gpu[absent])), "an lse past its sequence's row count was written"
+        l_gpu, l_ref = np.where(absent, 0.0, l_gpu), np.where(absent, 0.0, l_ref)
     both_inf = np.isneginf(l_gpu) & np.isneginf(l_ref)
     d = np.where(both_inf, 0.0, np.abs(l_gpu - l_ref))
     return float(np.nan_to_num(d, nan=math.inf).max()) if d.size else 0.0

@@ -34,7 +34,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.attn_abi_version() == 1
+    assert lib.attn_abi_version() == 2
 
 
 def test_open_without_a_gpu_is_a_device_error(lib):

@@ -359,3 +359,34 @@ def test_read_probe_runs_and_keeps_its_sink():
     pa.attn_debug_read_probe(ctx(), buf, 1, order, sink)
     torch.cuda.synchronize()
     assert int(sink.item()) == 7
+
+
+# ---------------------------------------------------------------- ragged rows
+
+@pytest.mark.parametrize("kv_dtype,R,rps,splits", [
+    (DT_BF16, 2, [2, 0, 1, 2], 0),          # VALU path (8 rows per KV head)
+    (DT_BF16, 2, [1, 2, 2, 0], 5),
+    (DT_BF16, 8, [8, 3, 0, 5], 0),          # MFMA path (32 rows per KV head)
+    (DT_FP8, 4, [4, 1, 0, 3], 3),
+    (DT_F32, 1, [1, 0, 1, 1], 0),
+])
+def test_decode_ragged_rows(kv_dtype, R, rps, splits):
+    _say(f"ragged decode kv={kv_dtype} R={R} rows={rps} splits={splits}")
+    p = synth.make_decode(90 + R, 4, 8, 2, 128 if kv_dtype != DT_F32 else 64, [700, 33, 1500, 260], R,
+                          kv_dtype=kv_dtype, sinks=True, rows_per_seq=rps)
+    o, lse = run(Dev(p), num_splits=splits)
+    check_full(p, o, lse)
+
+
+@pytest.mark.parametrize("masked", [False, True])
+def test_prefill_ragged_rows(masked):
+    """Chunked prefill with a different chunk length per sequence."""
+    _say(f"ragged prefill masked={masked}")
+    if masked:
+        p = synth.make_blocksparse(93, 3, 8, 2, 64, 640, mask_block=64, mask_heads=2, keep_prob=0.3)
+    else:
+        p = synth.make_prefill(92, 3, 8, 2, 64, 700, q_rows=300, lens=[400, 350, 700])
+    rows = [p.q_rows, 17, 129] if not masked else [640, 0, 200]
+    p.rows_per_seq = torch.tensor(rows, dtype=torch.int32)
+    o, lse = run(Dev(p))
+    check_full(p, o, lse)

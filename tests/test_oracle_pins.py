@@ -290,6 +290,26 @@ def test_verify_row_equals_decode_at_its_position():
         assert np.array_equal(od[0, 0], o[0, r]) and np.array_equal(ld[0, :, 0], lse[0, :, r])
 
 
+def test_ragged_rows_equal_decode_at_their_positions():
+    """Rows per sequence vary: row i of sequence b (of r_b rows) is the
+    single-row decode at position L_b - r_b + i; rows i >= r_b do not exist."""
+    R, lens, rps = 4, [53, 40, 17, 30], [4, 1, 3, 0]
+    p = synth.make_decode(47, 4, 8, 2, 16, lens, R, kv_dtype=DT_BF16, sinks=True, rows_per_seq=rps)
+    o, lse = oracle.attend_full(p)
+    for b, (L, rb) in enumerate(zip(lens, rps)):
+        for i in range(R):
+            if i >= rb:
+                assert np.all(np.isnan(o[b, i])) and np.all(np.isnan(lse[b, :, i]))
+                continue
+            d = synth.make_decode(47, 1, 8, 2, 16, [L], 1, kv_dtype=DT_BF16)
+            d.k_pool, d.v_pool, d.sinks = p.k_pool, p.v_pool, p.sinks
+            d.page_table = p.page_table[b:b + 1].clone()
+            d.seq_lens = torch.tensor([L - rb + i + 1], dtype=torch.int32)
+            d.q = p.q[b:b + 1, i:i + 1].clone()
+            od, ld = oracle.attend_full(d)
+            assert np.array_equal(od[0, 0], o[b, i]) and np.array_equal(ld[0, :, 0], lse[b, :, i])
+
+
 def test_all_ones_mask_equals_dense_causal():
     p = synth.make_blocksparse(46, 2, 4, 2, 16, 70, mask_block=16, sinks=True)
     p.mask = torch.ones_like(p.mask)
