@@ -68,8 +68,8 @@ attn_status check_kv(const attn_kv *kv, char **err) {
   if (kv->head_dim < 1 || kv->page_size < 1)
     return fail(err, ATTN_ERR_INVALID_ARGUMENT, "head_dim and page_size must be >= 1");
   if (kv->page_size != kPage) return fail(err, ATTN_ERR_UNSUPPORTED, "page_size %d (only 16)", kv->page_size);
-  if (kv->head_dim != 64 && kv->head_dim != 128)
-    return fail(err, ATTN_ERR_UNSUPPORTED, "head_dim %d (only 64 or 128)", kv->head_dim);
+  if (kv->head_dim != 64 && kv->head_dim != 128 && kv->head_dim != 256)
+    return fail(err, ATTN_ERR_UNSUPPORTED, "head_dim %d (only 64, 128 or 256)", kv->head_dim);
   if (!aligned16(kv->k_pages) || !aligned16(kv->v_pages))
     return fail(err, ATTN_ERR_INVALID_ARGUMENT, "K/V pages must be 16-byte aligned");
   const int64_t tile = (int64_t)kPage * kv->head_dim;
@@ -143,10 +143,11 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
   const int rows = G * io->q_rows;
   const int D = kv->head_dim;
   pl->rows = rows;
-  pl->mfma = kv->dtype != ATTN_F32 && rows > 8;
+  // more than 8 rows per KV head go to the MFMA kernel where it exists for
+  // these arguments; otherwise the VALU kernel runs them in blocks of 8 rows
+  pl->mfma = kv->dtype != ATTN_F32 && rows > 8 &&
+             pa::decode_mfma_supported(kv->dtype, io->q_dtype, D, rows);
   if (pl->mfma) {
-    if (!pa::decode_mfma_supported(kv->dtype, io->q_dtype, D, rows))
-      return fail(err, ATTN_ERR_UNSUPPORTED, "decode: K/V dtype %d with Q dtype %d and %d rows per KV head is not supported", kv->dtype, io->q_dtype, rows);
     pl->rb = rows;
     pl->row_blocks = 1;
   } else {

@@ -21,7 +21,8 @@ namespace pa {
 namespace {
 
 constexpr int kAppendThreads = 256;
-constexpr int kAppendPages = 4;    // pages (16 slots each) per workgroup
+// pages (16 slots each) per workgroup: 4, or 2 at head_dim 256 (LDS staging)
+template <int D> constexpr int append_pages() { return D >= 256 ? 2 : 4; }
 
 __device__ __forceinline__ uint32_t enc_bf16(float y) {
   const uint32_t u = __float_as_uint(y);
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append(AppendArgs a) {
   constexpr int ELT = DtInfo<KVDT>::bytes;
   constexpr int SELT = DtInfo<SRC>::bytes;
   constexpr int TPT = D / 8;                  // threads per token row (8 elements each)
-  constexpr int NS = 16 * kAppendPages;       // slots of this workgroup
+  constexpr int NS = 16 * append_pages<D>();       // slots of this workgroup
   constexpr int VG = 16 / ELT;                // slots per 16-byte V store
   __shared__ uint32_t vstage[NS][D + 1];      // V codes [slot][component] (+1: no bank conflicts)
 
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append(AppendArgs a) {
   const int L = min(a.lens[b], a.capacity);
   const int first = max(0, L - a.n_new);      // first position written
   if (first >= L) return;
-  const int page0 = first / 16 + blockIdx.x * kAppendPages;   // first logical page
+  const int page0 = first / 16 + blockIdx.x * append_pages<D>();   // first logical page
   const int p0 = page0 * 16;
   if (p0 >= L) return;
   const int s_lo = max(first, p0) - p0, s_hi = min(L, p0 + NS) - p0;   // slots [s_lo, s_hi)
@@ -186,9 +187,10 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append(AppendArgs a) {
 
 template <int KV, int SRC>
 hipError_t append_d(const AppendArgs &a, hipStream_t s) {
-  const dim3 grid(((a.n_new + 15) / 16 + 1 + kAppendPages - 1) / kAppendPages, a.Hkv, a.B);
-  if (a.D == 64) hipLaunchKernelGGL((kv_append<KV, SRC, 64>), grid, dim3(kAppendThreads), 0, s, a);
-  else hipLaunchKernelGGL((kv_append<KV, SRC, 128>), grid, dim3(kAppendThreads), 0, s, a);
+  auto grid = [&](int pages) { return dim3(((a.n_new + 15) / 16 + 1 + pages - 1) / pages, a.Hkv, a.B); };
+  if (a.D == 64) hipLaunchKernelGGL((kv_append<KV, SRC, 64>), grid(append_pages<64>()), dim3(kAppendThreads), 0, s, a);
+  else if (a.D == 128) hipLaunchKernelGGL((kv_append<KV, SRC, 128>), grid(append_pages<128>()), dim3(kAppendThreads), 0, s, a);
+  else hipLaunchKernelGGL((kv_append<KV, SRC, 256>), grid(append_pages<256>()), dim3(kAppendThreads), 0, s, a);
   return hipGetLastError();
 }
 

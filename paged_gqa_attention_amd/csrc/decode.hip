@@ -798,7 +798,8 @@ __global__ void debug_gather(const void *k, const void *v, int64_t k_sp, int64_t
 // ==================================================================================
 
 bool decode_valu_supported(int kv, int qd, int D) {
-  if (D != 64 && D != 128) return false;
+  if (D != 64 && D != 128 && D != 256) return false;
+  if (D == 256 && kv == DT_F32) return false;   // FP32 K/V: head_dim up to 128
   if (kv == DT_F32) return qd == DT_F32 || qd == DT_F16 || qd == DT_BF16;
   if (kv == DT_BF16) return qd == DT_BF16;
   if (kv == DT_F16) return qd == DT_F16;
@@ -826,7 +827,11 @@ static hipError_t valu_rb(const DecodeArgs &a, hipStream_t s) {
 
 template <int KV, int QD>
 static hipError_t valu_d(const DecodeArgs &a, hipStream_t s) {
-  return a.D == 64 ? valu_rb<KV, QD, 64>(a, s) : valu_rb<KV, QD, 128>(a, s);
+  if (a.D == 64) return valu_rb<KV, QD, 64>(a, s);
+  if constexpr (KV != DT_F32) {
+    if (a.D == 256) return valu_rb<KV, QD, 256>(a, s);
+  }
+  return valu_rb<KV, QD, 128>(a, s);
 }
 
 hipError_t launch_decode_valu(const DecodeArgs &a, hipStream_t s) {
@@ -902,7 +907,10 @@ static int mfma_occ(int rows) {
 
 template <int KV, int QD>
 static int occ_d(bool mfma, int D, int rows) {
-  if (mfma) return D == 64 ? mfma_occ<KV, QD, 64>(rows) : mfma_occ<KV, QD, 128>(rows);
+  if constexpr (KV != DT_F32) {
+    if (mfma) return D == 64 ? mfma_occ<KV, QD, 64>(rows) : mfma_occ<KV, QD, 128>(rows);
+    if (D == 256) return valu_occ<KV, QD, 256>(rows);
+  }
   return D == 64 ? valu_occ<KV, QD, 64>(rows) : valu_occ<KV, QD, 128>(rows);
 }
 
@@ -923,7 +931,8 @@ int decode_blocks_per_cu(bool mfma, int kv, int qd, int D, int rows) {
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t s) {
   dim3 grid((a.rows + kWaves - 1) / kWaves, a.Hkv, a.B);
   if (a.D == 64) hipLaunchKernelGGL((decode_merge<64>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((decode_merge<128>), grid, dim3(256), 0, s, a);
+  else if (a.D == 128) hipLaunchKernelGGL((decode_merge<128>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((decode_merge<256>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

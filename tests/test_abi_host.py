@@ -224,3 +224,25 @@ def test_kv_append_validation(hctx):
     assert app(bad) == pa.ATTN_ERR_INVALID_ARGUMENT              # misaligned
     kv.k_scale = 0.0
     assert app(rows) == pa.ATTN_ERR_INVALID_ARGUMENT             # the scale divides
+
+
+def test_head_dim_256_support(hctx):
+    # decode: any rows (more than 8 per KV head run as blocks of 8); FP32 K/V only up to 128
+    io, kv, op = _decode_args(B=2, R=8, Hq=16, Hkv=2, d=256, stride=64)
+    P, T, W = pa.attn_paged_decode_plan(hctx, io, kv, op)
+    assert P >= 1 and W > 0
+    io, kv, op = _decode_args(B=2, R=1, Hq=8, Hkv=2, d=256, stride=64, dtype=torch.float32)
+    assert _status(lambda: pa.attn_paged_decode_plan(hctx, io, kv, op)) == pa.ATTN_ERR_UNSUPPORTED
+    # prefill is not built for head_dim 256
+    q = FakeTensor((1, 64, 8, 256), torch.bfloat16, 0x500000)
+    o = FakeTensor((1, 64, 8, 256), torch.bfloat16, 0x600000)
+    k = FakeTensor((100, 2, 16, 256), torch.bfloat16, 0x100000)
+    v = FakeTensor((100, 2, 256, 16), torch.bfloat16, 0x200000)
+    pt = FakeTensor((1, 8), torch.int32, 0x300000)
+    lens = FakeTensor((1,), torch.int32, 0x400000)
+    kv = pa.make_kv(k, v, pt, lens)
+    assert _status(lambda: pa.attn_prefill(hctx, pa.make_io(q, o), kv, pa.make_opts(), stream=0)) == \
+        pa.ATTN_ERR_UNSUPPORTED
+    # head_dim 96 is not built anywhere
+    io, kv, op = _decode_args(d=96)
+    assert _status(lambda: pa.attn_paged_decode_plan(hctx, io, kv, op)) == pa.ATTN_ERR_UNSUPPORTED

@@ -112,3 +112,10 @@ def test_attention_over_the_appended_cache(kv_dtype):
     o, lse = run(dev)
     pexp = synth.with_pool_codes(p, exp[0], exp[1])
     check_full(pexp, o, lse)
+
+
+@pytest.mark.parametrize("kv_dtype", [DT_BF16, DT_FP8])
+def test_append_head_dim_256(kv_dtype):
+    _, _, got, exp = _append_case(740 + kv_dtype, kv_dtype, DT_F32, 256, [70, 300, 16], 37, 24)
+    for gt, ex in zip(got, exp):
+        assert np.array_equal(gt, ex)

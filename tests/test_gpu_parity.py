@@ -390,3 +390,36 @@ def test_prefill_ragged_rows(masked):
     p.rows_per_seq = torch.tensor(rows, dtype=torch.int32)
     o, lse = run(Dev(p))
     check_full(p, o, lse)
+
+
+# ---------------------------------------------------------------- head_dim 256 (decode)
+
+@pytest.mark.parametrize("kv_dtype,R,G", [
+    (DT_BF16, 1, 4),      # 4 rows per KV head
+    (DT_F16, 2, 4),       # 8 rows
+    (DT_FP8, 4, 4),       # 16 rows: the VALU kernel in two blocks of 8
+    (DT_BF16, 8, 6),      # 48 rows: six blocks
+])
+def test_decode_head_dim_256(kv_dtype, R, G):
+    _say(f"d256 decode kv={kv_dtype} R={R} G={G}")
+    p = synth.make_decode(95 + R, 3, 2 * G, 2, 256, [900, 45, 2100], R, kv_dtype=kv_dtype,
+                          sinks=True)
+    o, lse = run(Dev(p))
+    check_full(p, o, lse)
+    o2, _ = run(Dev(p), num_splits=7)
+    check_full(p, o2, None)
+
+
+def test_gather_head_dim_256():
+    p = synth.make_decode(98, 1, 4, 2, 256, [77], 1, kv_dtype=DT_FP8)
+    d = Dev(p)
+    kv = pa.make_kv(d.k, d.v, d.pt, d.lens, p.k_scale, p.v_scale)
+    k_out = torch.full((2, 77, 256), float("nan"), device="cuda")
+    v_out = torch.full((2, 77, 256), float("nan"), device="cuda")
+    pa.attn_debug_gather_kv(ctx(), kv, 0, 77, k_out, v_out)
+    torch.cuda.synchronize()
+    for g in range(2):
+        k, v = oracle.gather(p, 0, g)
+        # the kernels scale in FP32: compare with the FP64 values rounded once to FP32
+        assert np.array_equal(k_out[g].double().cpu().numpy(), k.astype(np.float32).astype(np.float64))
+        assert np.array_equal(v_out[g].double().cpu().numpy(), v.astype(np.float32).astype(np.float64))
