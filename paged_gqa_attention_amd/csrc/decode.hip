@@ -295,9 +295,20 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
           }
         }
       }
-      acc += dpp<kDppQuadXor1>(acc);
-      acc += dpp<kDppQuadXor2>(acc);
-      s[r] = acc;
+      s[r] = acc;   // this lane's quarter of the dot product
+    }
+    // quad reduce-scatter: lane qq ends with the full score of row qq + 4k
+    // (two exchange steps; no lane needs the other rows' totals)
+    float mine[MR];
+#pragma unroll
+    for (int k = 0; k < MR; ++k) {
+      const bool o1 = qq & 1, o2 = qq & 2;
+      const float x0 = o1 ? s[4 * k + 1] : s[4 * k], y0 = o1 ? s[4 * k] : s[4 * k + 1];
+      const float x1 = o1 ? s[4 * k + 3] : s[4 * k + 2], y1 = o1 ? s[4 * k + 2] : s[4 * k + 3];
+      const float t0 = x0 + dpp<kDppQuadXor1>(y0);
+      const float t1 = x1 + dpp<kDppQuadXor1>(y1);
+      const float x = o2 ? t1 : t0, y = o2 ? t0 : t1;
+      mine[k] = x + dpp<kDppQuadXor2>(y);
     }
 
     // ---- online softmax for this lane's rows ----
@@ -305,10 +316,7 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
     const bool page_full = (pg * 16 + 16 <= t1);
 #pragma unroll
     for (int k = 0; k < MR; ++k) {
-      float v = s[4 * k];
-      v = qq == 1 ? s[4 * k + 1] : v;
-      v = qq == 2 ? s[4 * k + 2] : v;
-      v = qq == 3 ? s[4 * k + 3] : v;
+      const float v = mine[k];
       const bool valid = tok < t1 && tok <= pos_mine[k];
       const float x = valid ? v * a.score_scale : kNegInf;
       float mx = x;
