@@ -5,11 +5,11 @@ the CPU-baseline leg of ``bench.py``.  The attention library never imports it.
 The arithmetic lives in ``attn_oracle.c`` (plain C, double precision); this
 file only marshals arguments.
 
-Every function here is pinned by ``tests/test_oracle_pins.py`` except the two
-readings the pages leave open and that no mathematics can fix (the FP8
-per-tensor scale choice and the units of the sink logit): those are "parity
-unpinned" and are applied identically by the generator, the oracle and the
-GPU path.
+Every function here is pinned by ``tests/test_oracle_pins.py`` and
+``tests/test_append_oracle.py`` except the readings the pages leave open and
+that no mathematics can fix (the FP8 per-tensor scale choice, the rule that
+picks a per-vector scale, and the units of the sink logit): those are "parity
+unpinned" and are applied identically by the oracle and the GPU path.
 """
 from __future__ import annotations
 
@@ -56,6 +56,8 @@ class _Problem(ctypes.Structure):
         ("mask_heads", ctypes.c_int32), ("mask_block", ctypes.c_int32),
         ("mask_nqb", ctypes.c_int32), ("mask_nkb", ctypes.c_int32),
         ("rows_per_seq", ctypes.c_void_p),
+        ("k_vs", ctypes.c_void_p), ("v_vs", ctypes.c_void_p),
+        ("vs_stride_page", ctypes.c_int64), ("vs_stride_head", ctypes.c_int64),
     ]
 
 
@@ -80,6 +82,10 @@ def _load():
                                    ctypes.c_void_p]
         _lib.orc_encode_array.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
                                           ctypes.c_float, ctypes.c_void_p]
+        _lib.orc_vector_scales.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                           ctypes.c_float, ctypes.c_void_p]
+        _lib.orc_encode_vectors.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         _lib.orc_attend_rows.restype = ctypes.c_int
         _lib.orc_attend_rows.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int64,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -132,6 +138,15 @@ class OracleProblem:
             s.mask = None
             s.mask_heads, s.mask_block, s.mask_nqb, s.mask_nkb = 1, 128, 0, 0
         s.rows_per_seq = self.rows_per_seq.data_ptr() if self.rows_per_seq is not None else None
+        kvs, vvs = getattr(p, "k_vs", None), getattr(p, "v_vs", None)
+        self.k_vs = cpu(kvs).to(torch.float32) if kvs is not None else None
+        self.v_vs = cpu(vvs).to(torch.float32) if vvs is not None else None
+        if self.k_vs is not None:
+            s.k_vs, s.v_vs = self.k_vs.data_ptr(), self.v_vs.data_ptr()
+            s.vs_stride_page, s.vs_stride_head = hkv * page, page
+        else:
+            s.k_vs = s.v_vs = None
+            s.vs_stride_page = s.vs_stride_head = 0
         self.struct = s
 
     def all_rows(self) -> np.ndarray:
@@ -217,13 +232,15 @@ def decode_codes(dtype: int, codes: np.ndarray) -> np.ndarray:
     return out
 
 
-_CODE_NP = {0: np.uint32, 1: np.uint16, 2: np.uint16, 3: np.uint8}
+_CODE_NP = {0: np.uint32, 1: np.uint16, 2: np.uint16, 3: np.uint8, 4: np.uint8}
+# largest finite value of the 8-bit formats (e4m3fn, e5m2)
+FMAX = {3: 448.0, 4: 57344.0}
 
 
 def encode(dtype: int, x, scale: float = 1.0) -> np.ndarray:
     """Storage codes of float32 values x / scale in ``dtype`` (F32: the quotient's
     bits): round-to-nearest-even, IEEE overflow to infinity, e4m3fn saturating
-    at +-448 (attn_oracle.c, "Encoding for the K/V append step")."""
+    at +-448, e5m2 at +-57344 (attn_oracle.c, "Encoding for the K/V append step")."""
     lib = _load()
     x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
     out = np.zeros(x.shape, dtype=_CODE_NP[dtype])
@@ -231,9 +248,35 @@ def encode(dtype: int, x, scale: float = 1.0) -> np.ndarray:
     return out
 
 
+def vector_scales(dtype: int, x) -> np.ndarray:
+    """Per-vector scales (float32, one per vector along the last axis of x) of
+    an 8-bit format: amax over the finite entries / the format's largest
+    finite value, 1 where that is 0."""
+    lib = _load()
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    d = x.shape[-1]
+    n = x.size // d
+    out = np.zeros(x.shape[:-1], dtype=np.float32)
+    lib.orc_vector_scales(n, d, x.ctypes.data, float(FMAX[dtype]), out.ctypes.data)
+    return out
+
+
+def encode_vectors(dtype: int, x, scales) -> np.ndarray:
+    """Codes of x[..., i] / scales[...] (the scale of each vector along the last axis)."""
+    lib = _load()
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    sc = np.ascontiguousarray(np.asarray(scales, dtype=np.float32))
+    assert sc.shape == x.shape[:-1]
+    d = x.shape[-1]
+    out = np.zeros(x.shape, dtype=_CODE_NP[dtype])
+    lib.orc_encode_vectors(dtype, x.size // d, d, x.ctypes.data, sc.ctypes.data, out.ctypes.data)
+    return out
+
+
 def kv_append(kv_dtype: int, k_codes: np.ndarray, v_codes: np.ndarray, page_table: np.ndarray,
               seq_lens: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, k_scale: float = 1.0,
-              v_scale: float = 1.0, page_size: int = 16):
+              v_scale: float = 1.0, page_size: int = 16, k_vs: Optional[np.ndarray] = None,
+              v_vs: Optional[np.ndarray] = None):
     """Expected K/V pools after appending n_new rows per sequence.
 
     k_codes [pages][Hkv][16][d] and v_codes [pages][Hkv][d][16] hold storage codes;
@@ -241,11 +284,22 @@ def kv_append(kv_dtype: int, k_codes: np.ndarray, v_codes: np.ndarray, page_tabl
     widened).  Row i of sequence b lands at position L_b - n_new + i, where
     L_b = seq_lens[b] clamped to the page table's capacity; rows at negative
     positions are dropped.  Everything else in the pools is left as it was.
+
+    With per-vector scale pools k_vs / v_vs (float32 [pages][Hkv][16], 8-bit
+    storage, per-tensor scales 1) each new (token, head) vector is encoded
+    with its own scale (``vector_scales``), which lands in the scale pool's
+    slot; returns (k, v, k_vs, v_vs) then, else (k, v).
     """
     B, n_new = k_new.shape[0], k_new.shape[1]
     cap = page_table.shape[1] * page_size
-    kc = encode(kv_dtype, k_new, k_scale)
-    vc = encode(kv_dtype, v_new, v_scale)
+    per_vector = k_vs is not None
+    if per_vector:
+        ks_new, vs_new = vector_scales(kv_dtype, k_new), vector_scales(kv_dtype, v_new)
+        kc, vc = encode_vectors(kv_dtype, k_new, ks_new), encode_vectors(kv_dtype, v_new, vs_new)
+        k_vs, v_vs = k_vs.copy(), v_vs.copy()
+    else:
+        kc = encode(kv_dtype, k_new, k_scale)
+        vc = encode(kv_dtype, v_new, v_scale)
     k_out, v_out = k_codes.copy(), v_codes.copy()
     for b in range(B):
         L = min(int(seq_lens[b]), cap)
@@ -256,4 +310,7 @@ def kv_append(kv_dtype: int, k_codes: np.ndarray, v_codes: np.ndarray, page_tabl
             page, slot = int(page_table[b, pos // page_size]), pos % page_size
             k_out[page, :, slot, :] = kc[b, i]
             v_out[page, :, :, slot] = vc[b, i]
-    return k_out, v_out
+            if per_vector:
+                k_vs[page, :, slot] = ks_new[b, i]
+                v_vs[page, :, slot] = vs_new[b, i]
+    return (k_out, v_out, k_vs, v_vs) if per_vector else (k_out, v_out)

@@ -35,8 +35,13 @@
  *   block qb (qb from the absolute position), entries outside the mask's
  *   extent count as 0; mh = 0 for one mask head, else the KV head;
  *   a row with no allowed key has o = 0 and lse = sink (or -inf);
- *   FP8 is OCP e4m3fn (bias 7, no infinities, S.1111.111 is NaN), times the
- *   per-tensor scale.
+ *   FP8 is OCP e4m3fn (bias 7, no infinities, S.1111.111 is NaN) and BF8
+ *   is OCP e5m2 (bias 15, with infinities), each times the per-tensor scale
+ *   and, where the cache carries them, the FP32 scale of its (token, head)
+ *   vector (Geramy/LSE README, "K/V storage": fp8 and bf8 kept with scales,
+ *   33,280 bytes per token = codes plus one FP32 scale per K or V vector;
+ *   the architecture paragraph: FP8/BF8 loads decoded with per-vector
+ *   scales).
  */
 #include <math.h>
 #include <pthread.h>
@@ -44,7 +49,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2, ORC_E4M3 = 3 };
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2, ORC_E4M3 = 3, ORC_E5M2 = 4 };
 
 typedef struct {
   int32_t kv_dtype;
@@ -63,6 +68,8 @@ typedef struct {
   const uint8_t *mask;           /* NULL or [batch][mask_heads][mask_nqb][mask_nkb] */
   int32_t mask_heads, mask_block, mask_nqb, mask_nkb;
   const int32_t *rows_per_seq;   /* NULL or [batch]: sequence b has rows 0 .. r_b - 1 */
+  const float *k_vs, *v_vs;      /* NULL, or per-vector scales [page][kv head][16 tokens] */
+  int64_t vs_stride_page, vs_stride_head;   /* floats */
 } orc_problem;
 
 /* ---- storage decoding (bit formulas, one per format) ---------------------- */
@@ -94,6 +101,15 @@ static double dec_e4m3(uint8_t c) {
   return s ? -v : v;
 }
 
+static double dec_e5m2(uint8_t c) {
+  int s = c >> 7, e = (c >> 2) & 31, f = c & 3;
+  double v;
+  if (e == 31) v = f ? NAN : INFINITY;                   /* e5m2 keeps IEEE specials */
+  else if (e == 0) v = ldexp((double)f, -16);            /* f/4 * 2^-14 */
+  else v = ldexp(1.0 + f / 4.0, e - 15);
+  return s ? -v : v;
+}
+
 static double dec_f32(const void *p) {
   float f;
   memcpy(&f, p, 4);
@@ -106,6 +122,7 @@ double orc_decode(int32_t dtype, const void *base, int64_t idx) {
     case ORC_F16: { uint16_t h; memcpy(&h, (const char *)base + 2 * idx, 2); return dec_f16(h); }
     case ORC_BF16: { uint16_t h; memcpy(&h, (const char *)base + 2 * idx, 2); return dec_bf16(h); }
     case ORC_E4M3: return dec_e4m3(((const uint8_t *)base)[idx]);
+    case ORC_E5M2: return dec_e5m2(((const uint8_t *)base)[idx]);
   }
   return NAN;
 }
@@ -117,19 +134,29 @@ void orc_decode_array(int32_t dtype, const void *base, int64_t n, double *out) {
 
 /* ---- paged gather ---------------------------------------------------------- */
 
-/* logical key j of sequence b, KV head g, component c (dequantised, scaled) */
+/* the per-vector scale of token slot t of (page, g), 1 without per-vector scales */
+static double vector_scale(const orc_problem *P, const float *vs, int32_t page, int g, int64_t t) {
+  if (!vs) return 1.0;
+  return (double)vs[page * P->vs_stride_page + g * P->vs_stride_head + t];
+}
+
+/* logical key j of sequence b, KV head g, component c (dequantised, scaled);
+ * the products are exact in double precision (a code has at most 4
+ * significant bits, each scale 24) */
 static double key_at(const orc_problem *P, int b, int g, int64_t j, int c) {
   int32_t page = P->page_table[(int64_t)b * P->page_table_stride + j / P->page_size];
   int64_t t = j % P->page_size;
   int64_t idx = page * P->k_stride_page + g * P->k_stride_head + t * P->head_dim + c;
-  return orc_decode(P->kv_dtype, P->k_pool, idx) * P->k_scale;
+  return orc_decode(P->kv_dtype, P->k_pool, idx) * vector_scale(P, P->k_vs, page, g, t) *
+         P->k_scale;
 }
 
 static double value_at(const orc_problem *P, int b, int g, int64_t j, int c) {
   int32_t page = P->page_table[(int64_t)b * P->page_table_stride + j / P->page_size];
   int64_t t = j % P->page_size;
   int64_t idx = page * P->v_stride_page + g * P->v_stride_head + (int64_t)c * P->page_size + t;
-  return orc_decode(P->kv_dtype, P->v_pool, idx) * P->v_scale;
+  return orc_decode(P->kv_dtype, P->v_pool, idx) * vector_scale(P, P->v_vs, page, g, t) *
+         P->v_scale;
 }
 
 /* K and V of sequence b, KV head g as logical [L][d] FP64 arrays */
@@ -326,7 +353,18 @@ int orc_attend_rows(const orc_problem *P, int64_t nrows, const int32_t *rows, do
  * the storage format with round-to-nearest, ties to even (IEEE 754
  * roundTiesToEven).  IEEE formats overflow to infinity; e4m3fn has no
  * infinity, and a value beyond its largest finite magnitude (448) is stored as
- * +-448 (saturation).  NaN stays NaN.
+ * +-448 (saturation).  e5m2 saturates finite values beyond 57344 the same
+ * way and keeps infinities.  NaN stays NaN.
+ *
+ * With per-vector scales (8-bit storage, Geramy/LSE README "K/V storage":
+ * fp8 and bf8 with scales) each (token, head) vector x of K or V gets its own
+ * scale u = amax / fmax, one single-precision division, where amax is the
+ * largest |x_i| over its finite entries and fmax the format's largest finite
+ * value (448, 57344); u = 1 when that quotient is 0.  Each x_i is then stored
+ * as x_i / u (one single-precision division) rounded as above, and u is
+ * stored beside the codes.  (Reading: the pages fix no rule for the scale;
+ * mapping the vector's largest magnitude to the format's largest code is the
+ * plainest.)
  *
  * The rounding is evaluated from the definition in double precision: the
  * value's quantum (the spacing of the format's grid at its magnitude) is a
@@ -387,15 +425,50 @@ static uint32_t enc_e4m3fn(double x) {
   return sbit | pack_grid_value(r, 4, 3);
 }
 
+/* OCP e5m2: bias 15, IEEE specials (S.11111.00 infinity, S.11111.xx NaN),
+ * largest finite 57344; finite values beyond it saturate */
+static uint32_t enc_e5m2(double x) {
+  const uint32_t sbit = signbit(x) ? 0x80u : 0u;
+  if (isnan(x)) return sbit | 0x7Fu;
+  const double a = fabs(x);
+  if (isinf(a)) return sbit | 0x7Cu;
+  const double r = round_to_grid(a, 5, 2);
+  if (r >= 57344.0) return sbit | 0x7Bu;                        /* saturate */
+  return sbit | pack_grid_value(r, 5, 2);
+}
+
+static void encode_one(int32_t dtype, float y, void *out, int64_t i) {
+  switch (dtype) {
+    case ORC_F32: ((float *)out)[i] = y; break;
+    case ORC_F16: ((uint16_t *)out)[i] = (uint16_t)enc_ieee((double)y, 5, 10); break;
+    case ORC_BF16: ((uint16_t *)out)[i] = (uint16_t)enc_ieee((double)y, 8, 7); break;
+    case ORC_E4M3: ((uint8_t *)out)[i] = (uint8_t)enc_e4m3fn((double)y); break;
+    default: ((uint8_t *)out)[i] = (uint8_t)enc_e5m2((double)y); break;
+  }
+}
+
 /* out[i] = code of x[i] / scale in `dtype` (F32 stores the quotient itself) */
 void orc_encode_array(int32_t dtype, int64_t n, const float *x, float scale, void *out) {
-  for (int64_t i = 0; i < n; ++i) {
-    const float y = x[i] / scale;              /* one IEEE single division */
-    switch (dtype) {
-      case ORC_F32: ((float *)out)[i] = y; break;
-      case ORC_F16: ((uint16_t *)out)[i] = (uint16_t)enc_ieee((double)y, 5, 10); break;
-      case ORC_BF16: ((uint16_t *)out)[i] = (uint16_t)enc_ieee((double)y, 8, 7); break;
-      default: ((uint8_t *)out)[i] = (uint8_t)enc_e4m3fn((double)y); break;
+  for (int64_t i = 0; i < n; ++i) encode_one(dtype, x[i] / scale, out, i);  /* one IEEE division */
+}
+
+/* Per-vector scales of n vectors of d values (x[n][d]) for an 8-bit format
+ * with largest finite value fmax: scales[v] = amax_v / fmax, or 1 if that is 0 */
+void orc_vector_scales(int64_t n, int32_t d, const float *x, float fmax, float *scales) {
+  for (int64_t v = 0; v < n; ++v) {
+    float amax = 0.0f;
+    for (int32_t i = 0; i < d; ++i) {
+      const float a = fabsf(x[v * d + i]);
+      if (isfinite(a) && a > amax) amax = a;
     }
+    const float u = amax / fmax;               /* one IEEE single division */
+    scales[v] = (u == 0.0f) ? 1.0f : u;
   }
+}
+
+/* codes of x[v][i] / scales[v] (each one IEEE single division) */
+void orc_encode_vectors(int32_t dtype, int64_t n, int32_t d, const float *x, const float *scales,
+                        void *out) {
+  for (int64_t v = 0; v < n; ++v)
+    for (int32_t i = 0; i < d; ++i) encode_one(dtype, x[v * d + i] / scales[v], out, v * d + i);
 }

@@ -29,14 +29,16 @@ C2 = 0x94D049BB133111EB
 
 PAGE = 16  # tokens per KV page
 
-DT_F32, DT_F16, DT_BF16, DT_FP8 = 0, 1, 2, 3
+DT_F32, DT_F16, DT_BF16, DT_FP8, DT_BF8 = 0, 1, 2, 3, 4
 TORCH_DTYPE = {
     DT_F32: torch.float32,
     DT_F16: torch.float16,
     DT_BF16: torch.bfloat16,
     DT_FP8: torch.float8_e4m3fn,
+    DT_BF8: torch.float8_e5m2,
 }
-DT_NAMES = {"f32": DT_F32, "f16": DT_F16, "bf16": DT_BF16, "fp8": DT_FP8}
+DT_NAMES = {"f32": DT_F32, "f16": DT_F16, "bf16": DT_BF16, "fp8": DT_FP8, "bf8": DT_BF8}
+EIGHT_BIT = (DT_FP8, DT_BF8)
 
 
 def _s64(u: int) -> int:
@@ -103,21 +105,22 @@ def permutation(seed: int, stream: int, n: int, device="cpu") -> torch.Tensor:
     return torch.argsort(keys, stable=True)
 
 
-def quantize(x64: torch.Tensor, dtype: int, scale: float = 1.0) -> torch.Tensor:
+def quantize(x64: torch.Tensor, dtype: int, scale=1.0) -> torch.Tensor:
     """Round float64 values to the storage dtype (RNE).
 
-    FP8 values are divided by ``scale`` first and stored as OCP e4m3fn codes;
-    the generator keeps |x/scale| <= 240 so no code saturates."""
-    if dtype == DT_FP8:
+    8-bit values are divided by ``scale`` (a number, or a tensor broadcast
+    against x64) first and stored as OCP e4m3fn / e5m2 codes; the generator
+    keeps |x/scale| <= 240 so no code saturates."""
+    if dtype in EIGHT_BIT:
         y = (x64 / scale).to(torch.float32)
-        return y.to(torch.float8_e4m3fn)
+        return y.to(TORCH_DTYPE[dtype])
     return x64.to(TORCH_DTYPE[dtype])
 
 
 def nan_fill(shape, dtype: int) -> torch.Tensor:
     """Storage-dtype tensor of NaN codes, used for page slots past a sequence's end."""
-    if dtype == DT_FP8:
-        return torch.full(shape, 0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn)
+    if dtype in EIGHT_BIT:
+        return torch.full(shape, 0x7F, dtype=torch.uint8).view(TORCH_DTYPE[dtype])
     return torch.full(shape, float("nan"), dtype=TORCH_DTYPE[dtype])
 
 
@@ -147,6 +150,8 @@ class Problem:
     seed: int = 0
     meta: dict = field(default_factory=dict)
     rows_per_seq: Optional[torch.Tensor] = None   # int32 [B]: valid rows of each sequence
+    k_vs: Optional[torch.Tensor] = None   # float32 [num_pages][Hkv][16]: per-vector K scales
+    v_vs: Optional[torch.Tensor] = None   # float32 [num_pages][Hkv][16]: per-vector V scales
 
 
     @property
@@ -162,11 +167,31 @@ class Problem:
         return self.softmax_scale if self.softmax_scale > 0 else 1.0 / math.sqrt(self.head_dim)
 
 
+def _vector_spread(seed, stream, shape, device):
+    """Per-vector magnitude factors 2^U(-1, 1): token vectors of unequal size,
+    so that per-vector scales differ from token to token."""
+    n = int(math.prod(shape))
+    return torch.exp2(2.0 * uniform(seed, stream, n, device) - 1.0).view(*shape, 1)
+
+
+def _per_vector(x64: torch.Tensor, dtype: int):
+    """Codes and float32 scales of vectors along the last axis: the generator's
+    scale is amax / 240 (1 for an all-zero vector)."""
+    amax = x64.abs().amax(dim=-1)
+    sc = (amax / 240.0).to(torch.float32)
+    sc = torch.where(sc == 0, torch.ones_like(sc), sc)
+    return quantize(x64, dtype, sc.to(torch.float64).unsqueeze(-1)), sc
+
+
 def _build_pool(seed, lens, stride, hkv, d, kv_dtype, pool_pages=None, device="cpu",
-                k_scale=None, v_scale=None, extra_pages=0):
+                k_scale=None, v_scale=None, extra_pages=0, vscales=False):
     """Generate logical K/V ~ N(0,1) per (sequence, kv head) and scatter them
     into a shuffled shared page pool.  Returns (k_pool, v_pool, page_table,
-    k_scale, v_scale)."""
+    k_scale, v_scale, k_vs, v_vs); with ``vscales`` (8-bit storage) every
+    (token, head) vector is scaled by 2^U(-1,1) and stored with its own FP32
+    scale in the pools k_vs / v_vs [pages][Hkv][16] (per-tensor scales 1),
+    else k_vs = v_vs = None."""
+    assert not vscales or kv_dtype in EIGHT_BIT
     B = len(lens)
     npages_b = [(int(L) + PAGE - 1) // PAGE for L in lens]
     total = sum(npages_b) + extra_pages
@@ -186,10 +211,16 @@ def _build_pool(seed, lens, stride, hkv, d, kv_dtype, pool_pages=None, device="c
     tdt = TORCH_DTYPE[kv_dtype]
     k_pool = nan_fill((total, hkv, PAGE, d), kv_dtype).to(device)
     v_pool = nan_fill((total, hkv, d, PAGE), kv_dtype).to(device)
+    k_vs = v_vs = None
+    if vscales:
+        # slots past a sequence's end hold NaN scales: they must never be used
+        k_vs = torch.full((total, hkv, PAGE), float("nan"), dtype=torch.float32, device=device)
+        v_vs = torch.full((total, hkv, PAGE), float("nan"), dtype=torch.float32, device=device)
+        k_scale = v_scale = 1.0
 
-    # FP8: per-tensor scale = amax / 240 over the whole logical K (resp. V);
+    # 8-bit: per-tensor scale = amax / 240 over the whole logical K (resp. V);
     # a first pass finds the amax, the second regenerates and quantises
-    if kv_dtype == DT_FP8 and (k_scale is None or v_scale is None):
+    if kv_dtype in EIGHT_BIT and (k_scale is None or v_scale is None):
         amax_k = amax_v = 0.0
         for b in range(B):
             L = int(lens[b])
@@ -205,43 +236,55 @@ def _build_pool(seed, lens, stride, hkv, d, kv_dtype, pool_pages=None, device="c
         L = int(lens[b])
         if L == 0:
             continue
-        kq = quantize(normal(seed, 1000 + 2 * b, (hkv, L, d), device), kv_dtype, k_scale)
-        vq = quantize(normal(seed, 1001 + 2 * b, (hkv, L, d), device), kv_dtype, v_scale)
+        kx = normal(seed, 1000 + 2 * b, (hkv, L, d), device)
+        vx = normal(seed, 1001 + 2 * b, (hkv, L, d), device)
         n = npages_b[b]
         pad = n * PAGE - L
+        ids = page_table[b, :n].to(torch.int64)
+        if vscales:
+            kq, ksc = _per_vector(kx * _vector_spread(seed, 2000 + 2 * b, (hkv, L), device), kv_dtype)
+            vq, vsc = _per_vector(vx * _vector_spread(seed, 2001 + 2 * b, (hkv, L), device), kv_dtype)
+            nanp = torch.full((hkv, pad), float("nan"), dtype=torch.float32, device=device)
+            k_vs[ids] = torch.cat([ksc, nanp], dim=1).view(hkv, n, PAGE).permute(1, 0, 2)
+            v_vs[ids] = torch.cat([vsc, nanp], dim=1).view(hkv, n, PAGE).permute(1, 0, 2)
+        else:
+            kq = quantize(kx, kv_dtype, k_scale)
+            vq = quantize(vx, kv_dtype, v_scale)
         if pad:
             kq = torch.cat([kq, nan_fill((hkv, pad, d), kv_dtype).to(device)], dim=1)
             vq = torch.cat([vq, nan_fill((hkv, pad, d), kv_dtype).to(device)], dim=1)
-        ids = page_table[b, :n].to(torch.int64)
         # [hkv][n*16][d] -> [n][hkv][16][d]; V pages are token-minor: [n][hkv][d][16]
         kt = kq.view(hkv, n, PAGE, d).permute(1, 0, 2, 3)
         vt = vq.view(hkv, n, PAGE, d).permute(1, 0, 3, 2)
-        if kv_dtype == DT_FP8:
+        if kv_dtype in EIGHT_BIT:
             k_pool.view(torch.uint8)[ids] = kt.contiguous().view(torch.uint8)
             v_pool.view(torch.uint8)[ids] = vt.contiguous().view(torch.uint8)
         else:
             k_pool[ids] = kt.to(tdt)
             v_pool[ids] = vt.to(tdt)
-    return k_pool, v_pool, page_table, k_scale, v_scale
+    return k_pool, v_pool, page_table, k_scale, v_scale, k_vs, v_vs
 
 
 def make_decode(seed, batch, num_q_heads, num_kv_heads, head_dim, lens, q_rows,
                 kv_dtype=DT_BF16, q_dtype=None, o_dtype=None, stride=None, sinks=False,
-                softmax_scale=0.0, device="cpu", extra_pages=0, rows_per_seq=None) -> Problem:
+                softmax_scale=0.0, device="cpu", extra_pages=0, rows_per_seq=None,
+                vscales=False) -> Problem:
     """Paged decode / speculative-verify problem: ``q_rows`` rows per sequence
     sit at the last q_rows positions of each sequence (lens include them).
     With ``rows_per_seq`` (a list, each <= q_rows) sequence b has only its first
-    rows_per_seq[b] rows, at its last rows_per_seq[b] positions."""
+    rows_per_seq[b] rows, at its last rows_per_seq[b] positions.  ``vscales``
+    (8-bit K/V): per-vector FP32 scales instead of per-tensor ones."""
     lens = [int(x) for x in lens]
     assert len(lens) == batch
     if stride is None:
         stride = max(1, max((L + PAGE - 1) // PAGE for L in lens))
     if q_dtype is None:
-        q_dtype = DT_BF16 if kv_dtype == DT_FP8 else kv_dtype
+        q_dtype = DT_BF16 if kv_dtype in EIGHT_BIT else kv_dtype
     if o_dtype is None:
         o_dtype = q_dtype
-    k_pool, v_pool, pt, ks, vs = _build_pool(seed, lens, stride, num_kv_heads, head_dim,
-                                             kv_dtype, device=device, extra_pages=extra_pages)
+    k_pool, v_pool, pt, ks, vs, kvs, vvs = _build_pool(seed, lens, stride, num_kv_heads, head_dim,
+                                                       kv_dtype, device=device,
+                                                       extra_pages=extra_pages, vscales=vscales)
     q = quantize(normal(seed, 3, (batch, q_rows, num_q_heads, head_dim), device), q_dtype)
     sk = None
     if sinks:
@@ -249,6 +292,7 @@ def make_decode(seed, batch, num_q_heads, num_kv_heads, head_dim, lens, q_rows,
     p = Problem("decode", batch, q_rows, num_q_heads, num_kv_heads, head_dim, kv_dtype,
                 q_dtype, o_dtype, torch.tensor(lens, dtype=torch.int32, device=device), pt,
                 k_pool, v_pool, q, ks, vs, softmax_scale, sk, None, 128, seed)
+    p.k_vs, p.v_vs = kvs, vvs
     if rows_per_seq is not None:
         assert len(rows_per_seq) == batch and all(0 <= r <= q_rows for r in rows_per_seq)
         p.rows_per_seq = torch.tensor([int(r) for r in rows_per_seq], dtype=torch.int32,
@@ -258,7 +302,7 @@ def make_decode(seed, batch, num_q_heads, num_kv_heads, head_dim, lens, q_rows,
 
 def make_prefill(seed, batch, num_q_heads, num_kv_heads, head_dim, seq_len, q_rows=None,
                  kv_dtype=DT_BF16, sinks=True, lens=None, softmax_scale=0.0, device="cpu",
-                 o_dtype=None) -> Problem:
+                 o_dtype=None, vscales=False) -> Problem:
     """Causal prefill problem: q_rows (default seq_len) query rows at the end
     of each sequence; all K/V (including the rows' own) are in the paged pool."""
     if lens is None:
@@ -266,17 +310,19 @@ def make_prefill(seed, batch, num_q_heads, num_kv_heads, head_dim, seq_len, q_ro
     lens = [int(x) for x in lens]
     q_rows = seq_len if q_rows is None else q_rows
     stride = max(1, max((L + PAGE - 1) // PAGE for L in lens))
-    q_dtype = DT_BF16 if kv_dtype in (DT_FP8, DT_F32) else kv_dtype
+    q_dtype = DT_BF16 if kv_dtype in EIGHT_BIT + (DT_F32,) else kv_dtype
     if kv_dtype == DT_F32:
         q_dtype = DT_F32
-    k_pool, v_pool, pt, ks, vs = _build_pool(seed, lens, stride, num_kv_heads, head_dim,
-                                             kv_dtype, device=device)
+    k_pool, v_pool, pt, ks, vs, kvs, vvs = _build_pool(seed, lens, stride, num_kv_heads, head_dim,
+                                                       kv_dtype, device=device, vscales=vscales)
     q = quantize(normal(seed, 3, (batch, q_rows, num_q_heads, head_dim), device), q_dtype)
     sk = normal(seed, 4, (num_q_heads,), device).to(torch.float32) if sinks else None
-    return Problem("prefill", batch, q_rows, num_q_heads, num_kv_heads, head_dim, kv_dtype,
-                   q_dtype, o_dtype if o_dtype is not None else q_dtype,
-                   torch.tensor(lens, dtype=torch.int32, device=device), pt,
-                   k_pool, v_pool, q, ks, vs, softmax_scale, sk, None, 128, seed)
+    p = Problem("prefill", batch, q_rows, num_q_heads, num_kv_heads, head_dim, kv_dtype,
+                q_dtype, o_dtype if o_dtype is not None else q_dtype,
+                torch.tensor(lens, dtype=torch.int32, device=device), pt,
+                k_pool, v_pool, q, ks, vs, softmax_scale, sk, None, 128, seed)
+    p.k_vs, p.v_vs = kvs, vvs
+    return p
 
 
 def flashprefill_mask(seed, batch, mask_heads, n_blocks, keep_prob=0.1, device="cpu"):
@@ -295,9 +341,9 @@ def flashprefill_mask(seed, batch, mask_heads, n_blocks, keep_prob=0.1, device="
 
 def make_blocksparse(seed, batch, num_q_heads, num_kv_heads, head_dim, seq_len,
                      mask_block=128, mask_heads=1, keep_prob=0.1, sinks=False,
-                     kv_dtype=DT_BF16, device="cpu", mask=None) -> Problem:
+                     kv_dtype=DT_BF16, device="cpu", mask=None, vscales=False) -> Problem:
     p = make_prefill(seed, batch, num_q_heads, num_kv_heads, head_dim, seq_len,
-                     kv_dtype=kv_dtype, sinks=sinks, device=device)
+                     kv_dtype=kv_dtype, sinks=sinks, device=device, vscales=vscales)
     nb = (seq_len + mask_block - 1) // mask_block
     p.kind = "blocksparse"
     p.mask = mask if mask is not None else flashprefill_mask(seed, batch, mask_heads, nb,
@@ -354,13 +400,23 @@ def logical_kv_codes(p: Problem, b: int):
     n = (L + PAGE - 1) // PAGE
     ids = p.page_table[b, :n].to(torch.int64).cpu()
     kp, vp = p.k_pool.cpu(), p.v_pool.cpu()
-    if p.kv_dtype == DT_FP8:
+    if p.kv_dtype in EIGHT_BIT:
         kp, vp = kp.view(torch.uint8), vp.view(torch.uint8)
     k = kp[ids].permute(1, 0, 2, 3).reshape(p.num_kv_heads, n * PAGE, p.head_dim)[:, :L]
     v = vp[ids].permute(1, 0, 3, 2).reshape(p.num_kv_heads, n * PAGE, p.head_dim)[:, :L]
-    if p.kv_dtype == DT_FP8:
-        k, v = k.view(torch.float8_e4m3fn), v.view(torch.float8_e4m3fn)
+    if p.kv_dtype in EIGHT_BIT:
+        k, v = k.view(TORCH_DTYPE[p.kv_dtype]), v.view(TORCH_DTYPE[p.kv_dtype])
     return k.contiguous(), v.contiguous()
+
+
+def logical_vscales(p: Problem, b: int):
+    """The per-vector K and V scales of sequence b as stored: float32 [Hkv][L]."""
+    L = int(p.seq_lens[b])
+    n = (L + PAGE - 1) // PAGE
+    ids = p.page_table[b, :n].to(torch.int64).cpu()
+    ks = p.k_vs.cpu()[ids].permute(1, 0, 2).reshape(p.num_kv_heads, n * PAGE)[:, :L]
+    vs = p.v_vs.cpu()[ids].permute(1, 0, 2).reshape(p.num_kv_heads, n * PAGE)[:, :L]
+    return ks.contiguous(), vs.contiguous()
 
 
 def store_logical_kv(p: Problem, b: int, g: int, k=None, v=None):
@@ -371,7 +427,7 @@ def store_logical_kv(p: Problem, b: int, g: int, k=None, v=None):
     for src, pool, tr in ((k, p.k_pool, False), (v, p.v_pool, True)):
         if src is None:
             continue
-        src = src.to(pool.dtype) if pool.dtype != torch.float8_e4m3fn else src
+        src = src.to(pool.dtype) if pool.dtype not in (torch.float8_e4m3fn, torch.float8_e5m2) else src
         for pg in range(n):
             t0, t1 = pg * PAGE, min(L, pg * PAGE + PAGE)
             blk = src[t0:t1]
@@ -382,9 +438,9 @@ def store_logical_kv(p: Problem, b: int, g: int, k=None, v=None):
 
 
 _CODE_VIEW = {torch.float32: torch.int32, torch.float16: torch.int16, torch.bfloat16: torch.int16,
-              torch.float8_e4m3fn: torch.uint8}
+              torch.float8_e4m3fn: torch.uint8, torch.float8_e5m2: torch.uint8}
 _CODE_NP = {torch.float32: "uint32", torch.float16: "uint16", torch.bfloat16: "uint16",
-            torch.float8_e4m3fn: "uint8"}
+            torch.float8_e4m3fn: "uint8", torch.float8_e5m2: "uint8"}
 
 
 def pool_codes(pool: torch.Tensor):

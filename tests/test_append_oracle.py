@@ -18,7 +18,7 @@ import torch
 sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
 import oracle  # noqa: E402
 import synth  # noqa: E402
-from synth import DT_BF16, DT_F16, DT_F32, DT_FP8  # noqa: E402
+from synth import DT_BF16, DT_BF8, DT_F16, DT_F32, DT_FP8  # noqa: E402
 
 
 def _specials():
@@ -109,6 +109,74 @@ def test_e4m3fn_matches_torch_in_range():
     assert np.array_equal(got, ref)
 
 
+def test_e5m2_every_code_round_trips():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = oracle.decode_codes(DT_BF8, codes).astype(np.float32)
+    got = oracle.encode(DT_BF8, vals)
+    finite = ~np.isnan(vals)
+    assert np.array_equal(got[finite], codes[finite])          # infinities included
+    assert set(got[~finite].tolist()) <= {0x7F, 0xFF}
+
+
+def test_e5m2_ties_saturation_and_specials():
+    codes = np.arange(0, 0x7B, dtype=np.uint8)                  # 0 .. 49152 (0x7A)
+    lo = oracle.decode_codes(DT_BF8, codes)
+    hi = oracle.decode_codes(DT_BF8, codes + 1)
+    mid = ((lo + hi) / 2).astype(np.float32)                    # exact: <= 4 significant bits
+    assert np.array_equal(mid.astype(np.float64), (lo + hi) / 2)
+    even = np.where(codes % 2 == 0, codes, codes + 1).astype(np.uint8)
+    assert np.array_equal(oracle.encode(DT_BF8, mid), even)
+    assert np.array_equal(oracle.encode(DT_BF8, np.nextafter(mid, np.float32(np.inf))), codes + 1)
+    assert np.array_equal(oracle.encode(DT_BF8, np.nextafter(mid, np.float32(0))), codes)
+    assert np.array_equal(oracle.encode(DT_BF8, -mid), even | 0x80)
+    big = np.array([57344.0, 57345.0, 61439.0, 61440.0, 1e6, 3e38], dtype=np.float32)
+    assert np.all(oracle.encode(DT_BF8, big) == 0x7B)           # finite: saturate
+    assert np.all(oracle.encode(DT_BF8, -big) == 0xFB)
+    inf = np.array([np.inf, -np.inf], dtype=np.float32)
+    assert oracle.encode(DT_BF8, inf).tolist() == [0x7C, 0xFC]   # infinities stay
+    assert oracle.encode(DT_BF8, np.array([np.nan], np.float32))[0] in (0x7F, 0xFF)
+    # subnormals are multiples of 2^-16; half of the smallest one ties to zero
+    assert oracle.encode(DT_BF8, np.array([2.0 ** -17, 3 * 2.0 ** -17, 2.0 ** -16], np.float32)).tolist() == [0, 2, 1]
+
+
+def test_e5m2_matches_torch_in_range():
+    x = _random(200000, 5)
+    x = x[np.abs(x) < 57344.0]
+    got = oracle.encode(DT_BF8, x)
+    ref = _torch_codes(x, torch.float8_e5m2, torch.uint8)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("dtype,fmax", [(DT_FP8, 448.0), (DT_BF8, 57344.0)])
+def test_vector_scales_rule(dtype, fmax):
+    g = np.random.default_rng(6)
+    x = (g.standard_normal((300, 64)) * np.exp2(g.integers(-20, 20, (300, 1)))).astype(np.float32)
+    x[0] = 0.0                                                  # all zero: scale 1
+    x[1, :] = 0.0
+    x[1, 5] = np.inf                                            # non-finite entries do not count
+    x[1, 6] = np.nan
+    x[1, 7] = -3.0
+    x[2, :] = 1e-44                                             # quotient underflows to 0: scale 1
+    sc = oracle.vector_scales(dtype, x)
+    amax = np.array([np.max(np.abs(r[np.isfinite(r)]), initial=0.0) for r in x], dtype=np.float32)
+    ref = (amax / np.float32(fmax)).astype(np.float32)
+    ref = np.where(ref == 0, np.float32(1.0), ref)
+    assert np.array_equal(sc, ref)
+    assert sc[0] == 1.0 and sc[2] == 1.0 and sc[1] == np.float32(3.0) / np.float32(fmax)
+    # codes: one single-precision division by the vector's own scale
+    codes = oracle.encode_vectors(dtype, x, sc)
+    q = (x / sc[:, None]).astype(np.float32)
+    assert np.array_equal(codes, oracle.encode(dtype, q))
+    # the largest finite magnitude of each ordinary vector lands on the largest code
+    big = np.abs(codes[3:].astype(np.int32) & 0x7F).max(axis=1)
+    assert np.all(big == (0x7E if dtype == DT_FP8 else 0x7B))
+    # and the dequantised vector is within half a grid step (relative 2^-(m+1)) of x
+    mb = 3 if dtype == DT_FP8 else 2
+    xh = oracle.decode_codes(dtype, codes[3:]).reshape(-1, 64) * sc[3:, None]
+    rel_ok = np.abs(xh - x[3:]) <= np.abs(x[3:]) * 2.0 ** -(mb + 1) + sc[3:, None] * 2.0 ** -(16 if dtype == DT_BF8 else 9)
+    assert np.all(rel_ok)
+
+
 @pytest.mark.parametrize("dtype", [DT_F32, DT_F16, DT_BF16, DT_FP8])
 def test_scale_is_one_single_precision_division(dtype):
     x = _random(50000, 3)
@@ -117,7 +185,42 @@ def test_scale_is_one_single_precision_division(dtype):
     assert np.array_equal(oracle.encode(dtype, x, s), oracle.encode(dtype, q, 1.0))
 
 
-@pytest.mark.parametrize("kv_dtype", [DT_F32, DT_BF16, DT_FP8])
+@pytest.mark.parametrize("kv_dtype", [DT_FP8, DT_BF8])
+def test_per_vector_append_lands_where_the_gather_reads(kv_dtype):
+    lens = [37, 5, 16, 64]
+    n_new = 7
+    p = synth.make_decode(52, 4, 4, 2, 64, lens, 1, kv_dtype=kv_dtype, stride=5, vscales=True)
+    kcodes, vcodes = synth.pool_codes(p.k_pool), synth.pool_codes(p.v_pool)
+    kvs, vvs = p.k_vs.numpy(), p.v_vs.numpy()
+    g = np.random.default_rng(7)
+    knew = (g.standard_normal((4, n_new, 2, 64)) * 3).astype(np.float32)
+    vnew = (g.standard_normal((4, n_new, 2, 64)) / 5).astype(np.float32)
+    pt = p.page_table.numpy()
+    kout, vout, kvs2, vvs2 = oracle.kv_append(kv_dtype, kcodes, vcodes, pt, p.seq_lens.numpy(),
+                                              knew, vnew, k_vs=kvs, v_vs=vvs)
+    p2 = synth.with_pool_codes(p, kout, vout)
+    p2.k_vs, p2.v_vs = torch.from_numpy(kvs2), torch.from_numpy(vvs2)
+    for b, L in enumerate(lens):
+        for gg in range(2):
+            k_old, v_old = oracle.gather(p, b, gg)
+            k_new, v_new = oracle.gather(p2, b, gg)
+            for pos in range(L):
+                i = pos - (L - n_new)
+                if i < 0:
+                    assert np.array_equal(k_new[pos], k_old[pos]) and np.array_equal(v_new[pos], v_old[pos])
+                    continue
+                for src, got in ((knew[b, i, gg], k_new[pos]), (vnew[b, i, gg], v_new[pos])):
+                    amax = np.float32(np.abs(src).max())
+                    u = np.float32(amax / np.float32(oracle.FMAX[kv_dtype]))
+                    exp = oracle.decode_codes(kv_dtype, oracle.encode(kv_dtype, src, u)) * np.float64(u)
+                    assert np.array_equal(got, exp)
+    # only the new slots' scales changed (NaN pad scales compare as unchanged)
+    same = lambda a, b: (a == b) | (np.isnan(a) & np.isnan(b))
+    for new, old in ((kvs2, kvs), (vvs2, vvs)):
+        assert int((~same(new, old)).sum()) <= sum(min(L, n_new) for L in lens) * 2
+
+
+@pytest.mark.parametrize("kv_dtype", [DT_F32, DT_BF16, DT_FP8, DT_BF8])
 def test_append_reference_lands_where_the_gather_reads(kv_dtype):
     # sequences of different lengths, n_new rows each; one sequence shorter
     # than n_new (its first rows are dropped)

@@ -17,7 +17,7 @@ import torch
 
 import oracle
 import synth
-from synth import DT_BF16, DT_F16, DT_F32, DT_FP8, PAGE
+from synth import DT_BF16, DT_BF8, DT_F16, DT_F32, DT_FP8, PAGE
 
 
 # ---------------------------------------------------------------- storage codes
@@ -57,6 +57,21 @@ def test_e4m3fn_every_code():
     assert got[0x38] == 1.0
 
 
+def test_e5m2_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.decode_codes(DT_BF8, codes)
+    # independent route: an e5m2 code is the top byte of an IEEE binary16
+    ref = (codes.astype(np.uint16) << 8).view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert nan.sum() == 6                                       # S.11111.{01,10,11}
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    tref = torch.from_numpy(codes.copy()).view(torch.float8_e5m2).to(torch.float64).numpy()
+    assert np.array_equal(got[~nan], tref[~nan])
+    assert got[0x7B] == 57344.0 and got[0x7C] == math.inf and got[0xFC] == -math.inf
+    assert got[0x01] == 2.0 ** -16 and got[0x04] == 2.0 ** -14 and got[0x3C] == 1.0
+
+
 def test_f32_codes_roundtrip():
     x = synth.normal(9, 0, (1000,)).to(torch.float32)
     got = oracle.decode_codes(DT_F32, x.numpy().view(np.uint32))
@@ -65,15 +80,23 @@ def test_f32_codes_roundtrip():
 
 # ---------------------------------------------------------------- paged gather
 
-@pytest.mark.parametrize("dtype", [DT_F32, DT_F16, DT_BF16, DT_FP8])
-def test_gather_bit_exact(dtype):
-    p = synth.make_decode(11, 3, 4, 2, 64, [37, 16, 5], 1, kv_dtype=dtype, stride=4)
+@pytest.mark.parametrize("dtype,vscales", [(DT_F32, False), (DT_F16, False), (DT_BF16, False),
+                                           (DT_FP8, False), (DT_BF8, False), (DT_FP8, True),
+                                           (DT_BF8, True)])
+def test_gather_bit_exact(dtype, vscales):
+    p = synth.make_decode(11, 3, 4, 2, 64, [37, 16, 5], 1, kv_dtype=dtype, stride=4,
+                          vscales=vscales)
     for b in range(p.batch):
         kc, vc = synth.logical_kv_codes(p, b)
+        if vscales:
+            ks, vs = (t.to(torch.float64).numpy()[..., None] for t in synth.logical_vscales(p, b))
+            assert np.all(np.isfinite(ks)) and np.all(np.isfinite(vs))
         for g in range(p.num_kv_heads):
             k, v = oracle.gather(p, b, g)
             kref = kc[g].to(torch.float64).numpy() * p.k_scale
             vref = vc[g].to(torch.float64).numpy() * p.v_scale
+            if vscales:      # code * per-vector scale: exact in double precision
+                kref, vref = kref * ks[g], vref * vs[g]
             assert np.array_equal(k, kref) and np.array_equal(v, vref)
 
 
@@ -99,6 +122,10 @@ def _brute(p, b, i, h):
     kc, vc = synth.logical_kv_codes(p, b)
     K = kc[g].to(torch.float64).numpy().astype(np.longdouble) * p.k_scale
     V = vc[g].to(torch.float64).numpy().astype(np.longdouble) * p.v_scale
+    if p.k_vs is not None:
+        ks, vs = synth.logical_vscales(p, b)
+        K = K * ks[g].to(torch.float64).numpy().astype(np.longdouble)[:, None]
+        V = V * vs[g].to(torch.float64).numpy().astype(np.longdouble)[:, None]
     q = p.q[b, i, h].to(torch.float64).numpy().astype(np.longdouble)
     allowed = []
     for j in range(L):
@@ -119,11 +146,12 @@ def _brute(p, b, i, h):
     return o.astype(np.float64), float(np.log(Z))
 
 
-@pytest.mark.parametrize("kv_dtype", [DT_F32, DT_BF16, DT_FP8])
+@pytest.mark.parametrize("kv_dtype,vscales", [(DT_F32, False), (DT_BF16, False), (DT_FP8, False),
+                                              (DT_BF8, False), (DT_FP8, True), (DT_BF8, True)])
 @pytest.mark.parametrize("sinks", [False, True])
-def test_brute_force_decode(kv_dtype, sinks):
+def test_brute_force_decode(kv_dtype, vscales, sinks):
     p = synth.make_decode(21, 2, 4, 2, 8, [37, 50], 3, kv_dtype=kv_dtype, sinks=sinks,
-                          softmax_scale=0.3)
+                          softmax_scale=0.3, vscales=vscales)
     o, lse = oracle.attend_full(p)
     for b in range(2):
         for i in range(3):
