@@ -27,7 +27,9 @@
  * p = L - n + i and attends to keys j with j <= p (and, for the block-sparse
  * call, mask[b][mh][p / mask_block][j / mask_block] != 0).  Query head h reads
  * KV head h / (num_q_heads / num_kv_heads).  With s_j = softmax_scale * q.k_j
- * (k_j, v_j dequantised: value * k_scale, value * v_scale):
+ * (k_j, v_j dequantised: code value * k_scale, code value * v_scale, each
+ * also times its (token, head) vector's scale where the cache has per-vector
+ * scales):
  *     m = max(max_j s_j, sink_h),  Z = sum_j e^{s_j - m} + e^{sink_h - m},
  *     o = sum_j e^{s_j - m} v_j / Z,  lse = m + ln Z.
  * No sink means sink_h = -inf.  A row with no allowed key gets o = 0 and
@@ -52,6 +54,13 @@
  *   Q, O     [batch][q_rows][num_q_heads][head_dim] through the given strides,
  *            head_dim contiguous.
  *   lse      optional float [batch][num_q_heads][q_rows] (natural log).
+ *   per-vector scales (optional, 8-bit K/V): float scale of slot t of tile
+ *            (page, kv_head) at k_vscales + page*vscale_stride_page +
+ *            head*vscale_stride_head + t (likewise v_vscales), the 16 slots
+ *            of a tile contiguous (Geramy/LSE README, "K/V storage": fp8 and
+ *            bf8 caches keep an FP32 scale per K and per V vector, 33,280
+ *            bytes per token in its table; the architecture paragraph: FP8/BF8
+ *            loads are decoded with per-vector scales).
  *   block_mask  uint8 [batch][mask_heads][mask_q_blocks][mask_k_blocks];
  *            entries outside that extent count as 0.
  *
@@ -72,7 +81,7 @@
  *                              where required), bad mask geometry.
  *   ATTN_ERR_UNSUPPORTED       a well-formed request this build does not
  *                              implement (head_dim not 64, 128 or 256 --
- *                              256 for decode and append with 16-bit or FP8
+ *                              256 for decode and append with 16-bit or 8-bit
  *                              K/V only --, page_size not 16, unsupported
  *                              dtype combination).
  *   ATTN_ERR_WORKSPACE_TOO_SMALL  decode workspace below the queried size.
@@ -91,7 +100,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 typedef enum {
   ATTN_OK = 0,
@@ -101,8 +110,12 @@ typedef enum {
   ATTN_ERR_DEVICE = 4
 } attn_status;
 
-/* Storage / compute types.  FP8 is OCP e4m3fn (bias 7, max 448, no inf). */
-typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2, ATTN_FP8_E4M3 = 3 } attn_dtype;
+/* Storage / compute types.  FP8 is OCP e4m3fn (bias 7, max 448, no inf); BF8 is
+ * OCP e5m2 (bias 15, max 57344, IEEE infinities and NaNs): the cache formats
+ * "fp8" and "bf8" of the Geramy/LSE README ("K/V storage"). */
+typedef enum {
+  ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2, ATTN_FP8_E4M3 = 3, ATTN_BF8_E5M2 = 4
+} attn_dtype;
 
 typedef struct attn_ctx attn_ctx;
 
@@ -114,15 +127,18 @@ typedef struct {
   int32_t num_pages;            /* pages in the pool */
   int32_t page_size;            /* tokens per page; must be 16 */
   int32_t num_kv_heads;
-  int32_t head_dim;             /* 64, 128, or 256 (decode and append, 16-bit/FP8 K/V) */
+  int32_t head_dim;             /* 64, 128, or 256 (decode and append, 16-/8-bit K/V) */
   int32_t pad0;
   int64_t k_stride_page, k_stride_head;   /* elements */
   int64_t v_stride_page, v_stride_head;   /* elements */
-  float k_scale, v_scale;       /* dequantisation multipliers (1.0 unless FP8) */
+  float k_scale, v_scale;       /* dequantisation multipliers (1.0 unless 8-bit) */
   const int32_t *page_table;    /* [batch][page_table_stride] */
   int32_t page_table_stride;
   int32_t pad1;
   const int32_t *seq_lens;      /* [batch] */
+  const float *k_vscales;       /* nullable: per-vector K scales (8-bit K/V), see layout */
+  const float *v_vscales;       /* nullable: per-vector V scales; both or neither */
+  int64_t vscale_stride_page, vscale_stride_head;   /* floats, multiples of 4 */
 } attn_kv;
 
 /* Queries and outputs. */
@@ -185,7 +201,7 @@ size_t attn_paged_decode_workspace_bytes(const attn_ctx *ctx, const attn_io *io,
                                          const attn_kv *kv, const attn_opts *opts);
 
 /* Decode / verify: q_rows in [1, 8].  Q dtype: F32/F16/BF16 with F32 K/V,
- * equal to the K/V dtype for F16/BF16 K/V, F16 or BF16 with FP8 K/V.
+ * equal to the K/V dtype for F16/BF16 K/V, F16 or BF16 with 8-bit K/V.
  * `workspace` is device memory of at least the queried size (16-byte
  * aligned, contents irrelevant) for the partition partials; it may be reused
  * by consecutive calls on one stream but not by calls that can run
@@ -195,7 +211,8 @@ attn_status attn_paged_decode(attn_ctx *ctx, const attn_io *io, const attn_kv *k
                               void *hip_stream, char **err);
 
 /* Causal prefill (q_rows rows at the end of each sequence, q_rows <= seq_len
- * expected).  K/V F16, BF16 or FP8; Q F16/BF16 (equal to K/V for 16-bit K/V).
+ * expected).  K/V F16, BF16, FP8 or BF8; Q F16/BF16 (equal to K/V for 16-bit
+ * K/V).
  * block_mask must be NULL. */
 attn_status attn_prefill(attn_ctx *ctx, const attn_io *io, const attn_kv *kv,
                          const attn_opts *opts, void *hip_stream, char **err);
@@ -224,10 +241,16 @@ typedef struct {
  * (page_table[b][p / 16], head), its V row to the same slot of the V tile.
  * The stored value is src / scale (k_scale or v_scale; one IEEE
  * single-precision division) rounded to the pool's dtype to nearest, ties to
- * even: F16 and BF16 overflow to infinity, FP8 e4m3fn saturates at +-448, NaN
- * stays NaN (F32 stores the quotient).  Only those slots are written: the
- * pool memory (k_pages / v_pages) must be writable, and the pages for the new
- * positions must already be in the page table.  Base pointers and strides are
+ * even: F16 and BF16 overflow to infinity, FP8 e4m3fn saturates at +-448, BF8
+ * e5m2 saturates finite values at +-57344 and keeps infinities, NaN stays NaN
+ * (F32 stores the quotient).  With per-vector scales (k_vscales/v_vscales set;
+ * k_scale and v_scale must then be 1) each new K or V vector x gets the scale
+ * u = amax / fmax (one single-precision division; amax the largest |x_i| over
+ * its finite entries, fmax 448 for FP8 and 57344 for BF8; u = 1 when the
+ * quotient is 0), written to the vector's scale slot, and its values are
+ * stored as x_i / u rounded as above.  Only those slots are written: the pool
+ * memory (k_pages / v_pages, and the scale pools) must be writable, and the
+ * pages for the new positions must already be in the page table.  Base pointers and strides are
  * 16-byte aligned, head_dim contiguous.  Appends of one call must not target
  * the same slot twice (distinct sequences own distinct pages). */
 attn_status attn_kv_append(attn_ctx *ctx, const attn_kv *kv, const attn_kv_rows *rows,
@@ -235,7 +258,9 @@ attn_status attn_kv_append(attn_ctx *ctx, const attn_kv *kv, const attn_kv_rows 
 
 /* Test hook: gather sequence b's K and V through the page table and
  * dequantise them exactly as the attention kernels do, into FP32 arrays
- * k_out, v_out of [num_kv_heads][seq_len][head_dim] (device memory). */
+ * k_out, v_out of [num_kv_heads][seq_len][head_dim] (device memory): each
+ * value is (code value * per-vector scale) * per-tensor scale, evaluated in
+ * FP32 in that order (the per-vector factor only where the cache has one). */
 attn_status attn_debug_gather_kv(attn_ctx *ctx, const attn_kv *kv, int32_t b, int32_t seq_len,
                                  float *k_out, float *v_out, void *hip_stream, char **err);
 

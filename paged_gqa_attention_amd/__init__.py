@@ -23,12 +23,12 @@ LIB_PATH = os.path.join(_HERE, "libpaged_attn.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARGUMENT, ATTN_ERR_UNSUPPORTED = 0, 1, 2
 ATTN_ERR_WORKSPACE_TOO_SMALL, ATTN_ERR_DEVICE = 3, 4
-ATTN_F32, ATTN_F16, ATTN_BF16, ATTN_FP8_E4M3 = 0, 1, 2, 3
+ATTN_F32, ATTN_F16, ATTN_BF16, ATTN_FP8_E4M3, ATTN_BF8_E5M2 = 0, 1, 2, 3, 4
 
 _DT = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16,
-       torch.float8_e4m3fn: ATTN_FP8_E4M3}
+       torch.float8_e4m3fn: ATTN_FP8_E4M3, torch.float8_e5m2: ATTN_BF8_E5M2}
 
-ABI_VERSION = 2   # include/paged_attn.h ATTN_ABI_VERSION
+ABI_VERSION = 3   # include/paged_attn.h ATTN_ABI_VERSION
 
 EXPORTED = [
     "attn_abi_version", "attn_open", "attn_open_host_only", "attn_close", "attn_free",
@@ -55,6 +55,8 @@ class attn_kv(ctypes.Structure):
         ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
         ("page_table", ctypes.c_void_p), ("page_table_stride", ctypes.c_int32),
         ("pad1", ctypes.c_int32), ("seq_lens", ctypes.c_void_p),
+        ("k_vscales", ctypes.c_void_p), ("v_vscales", ctypes.c_void_p),
+        ("vscale_stride_page", ctypes.c_int64), ("vscale_stride_head", ctypes.c_int64),
     ]
 
 
@@ -205,9 +207,13 @@ def _dtype(t: torch.Tensor) -> int:
 
 
 def make_kv(k_pages: torch.Tensor, v_pages: torch.Tensor, page_table: torch.Tensor,
-            seq_lens: torch.Tensor, k_scale: float = 1.0, v_scale: float = 1.0) -> attn_kv:
+            seq_lens: torch.Tensor, k_scale: float = 1.0, v_scale: float = 1.0,
+            k_vscales: Optional[torch.Tensor] = None,
+            v_vscales: Optional[torch.Tensor] = None) -> attn_kv:
     """K pool [num_pages][Hkv][16][d], V pool [num_pages][Hkv][d][16] (any strides on
-    the first two dims, tiles contiguous), page_table int32 [B][stride], seq_lens int32 [B]."""
+    the first two dims, tiles contiguous), page_table int32 [B][stride], seq_lens int32 [B].
+    Optional per-vector scale pools (8-bit K/V) k_vscales / v_vscales: float32
+    [num_pages][Hkv][16] with the 16 slots contiguous and equal strides."""
     if k_pages.dim() != 4 or v_pages.dim() != 4:
         raise AttnError(ATTN_ERR_INVALID_ARGUMENT, "K/V pools must be 4-D")
     n, hkv, page, d = k_pages.shape
@@ -230,7 +236,22 @@ def make_kv(k_pages: torch.Tensor, v_pages: torch.Tensor, page_table: torch.Tens
     kv.page_table = _ptr(page_table)
     kv.page_table_stride = page_table.stride(0)
     kv.seq_lens = _ptr(seq_lens)
-    kv._keep = (k_pages, v_pages, page_table, seq_lens)
+    if (k_vscales is None) != (v_vscales is None):
+        raise AttnError(ATTN_ERR_INVALID_ARGUMENT, "k_vscales and v_vscales go together")
+    if k_vscales is not None:
+        for t in (k_vscales, v_vscales):
+            if t.dtype != torch.float32 or t.dim() != 3 or t.shape[0] != n or \
+               t.shape[1] != hkv or t.shape[2] != page or t.stride(2) != 1:
+                raise AttnError(ATTN_ERR_INVALID_ARGUMENT, "per-vector scales must be float32 "
+                                "[num_pages][Hkv][16] with contiguous slots")
+        if k_vscales.stride() != v_vscales.stride():
+            raise AttnError(ATTN_ERR_INVALID_ARGUMENT, "k_vscales and v_vscales need equal strides")
+        kv.k_vscales, kv.v_vscales = _ptr(k_vscales), _ptr(v_vscales)
+        kv.vscale_stride_page, kv.vscale_stride_head = k_vscales.stride(0), k_vscales.stride(1)
+    else:
+        kv.k_vscales = kv.v_vscales = None
+        kv.vscale_stride_page = kv.vscale_stride_head = 0
+    kv._keep = (k_pages, v_pages, page_table, seq_lens, k_vscales, v_vscales)
     return kv
 
 
@@ -385,13 +406,15 @@ def decode_workspace(ctx: Context, io: attn_io, kv: attn_kv, opts: attn_opts, de
 
 def paged_decode(ctx: Context, q, k_pages, v_pages, page_table, seq_lens, *, k_scale=1.0,
                  v_scale=1.0, softmax_scale=0.0, sinks=None, out=None, out_dtype=None,
-                 lse=None, num_splits=0, workspace=None, stream=None, rows_per_seq=None):
+                 lse=None, num_splits=0, workspace=None, stream=None, rows_per_seq=None,
+                 k_vscales=None, v_vscales=None):
     """Decode / verify rows ``q`` [B][R][Hq][d]; returns the output tensor.  With
-    ``rows_per_seq`` (int32 [B]) sequence b has only its first rows_per_seq[b] rows."""
+    ``rows_per_seq`` (int32 [B]) sequence b has only its first rows_per_seq[b] rows;
+    ``k_vscales``/``v_vscales`` are per-vector scale pools of an 8-bit cache."""
     o = out if out is not None else torch.empty(q.shape, dtype=out_dtype or q.dtype,
                                                  device=q.device)
     io = make_io(q, o, lse)
-    kv = make_kv(k_pages, v_pages, page_table, seq_lens, k_scale, v_scale)
+    kv = make_kv(k_pages, v_pages, page_table, seq_lens, k_scale, v_scale, k_vscales, v_vscales)
     op = make_opts(softmax_scale, sinks, None, 128, num_splits, rows_per_seq)
     if workspace is None:
         workspace = decode_workspace(ctx, io, kv, op, q.device)
@@ -401,13 +424,15 @@ def paged_decode(ctx: Context, q, k_pages, v_pages, page_table, seq_lens, *, k_s
 
 def prefill(ctx: Context, q, k_pages, v_pages, page_table, seq_lens, *, k_scale=1.0,
             v_scale=1.0, softmax_scale=0.0, sinks=None, out=None, out_dtype=None, lse=None,
-            block_mask=None, mask_block=128, stream=None, rows_per_seq=None):
+            block_mask=None, mask_block=128, stream=None, rows_per_seq=None, k_vscales=None,
+            v_vscales=None):
     """Causal (optionally block-sparse) prefill of ``q`` [B][S_q][Hq][d]; with
-    ``rows_per_seq`` (int32 [B]) sequence b has only its first rows_per_seq[b] rows."""
+    ``rows_per_seq`` (int32 [B]) sequence b has only its first rows_per_seq[b] rows;
+    ``k_vscales``/``v_vscales`` are per-vector scale pools of an 8-bit cache."""
     o = out if out is not None else torch.empty(q.shape, dtype=out_dtype or q.dtype,
                                                  device=q.device)
     io = make_io(q, o, lse)
-    kv = make_kv(k_pages, v_pages, page_table, seq_lens, k_scale, v_scale)
+    kv = make_kv(k_pages, v_pages, page_table, seq_lens, k_scale, v_scale, k_vscales, v_vscales)
     op = make_opts(softmax_scale, sinks, block_mask, mask_block, rows_per_seq=rows_per_seq)
     if block_mask is None:
         attn_prefill(ctx, io, kv, op, stream)

@@ -34,6 +34,7 @@ int elt_bytes(int dt) {
     case ATTN_F16: return 2;
     case ATTN_BF16: return 2;
     case ATTN_FP8_E4M3: return 1;
+    case ATTN_BF8_E5M2: return 1;
   }
   return 0;
 }
@@ -81,6 +82,16 @@ attn_status check_kv(const attn_kv *kv, char **err) {
   }
   if (!(kv->k_scale > 0.f) || !(kv->v_scale > 0.f) || !std::isfinite(kv->k_scale) || !std::isfinite(kv->v_scale))
     return fail(err, ATTN_ERR_INVALID_ARGUMENT, "k_scale and v_scale must be finite and > 0");
+  if ((kv->k_vscales == nullptr) != (kv->v_vscales == nullptr))
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "k_vscales and v_vscales must both be set or both be NULL");
+  if (kv->k_vscales) {
+    if (eb != 1) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "per-vector scales need 8-bit K/V (FP8 or BF8)");
+    if (!aligned16(kv->k_vscales) || !aligned16(kv->v_vscales))
+      return fail(err, ATTN_ERR_INVALID_ARGUMENT, "per-vector scale pools must be 16-byte aligned");
+    if (kv->vscale_stride_page < kPage || kv->vscale_stride_head < kPage ||
+        kv->vscale_stride_page % 4 || kv->vscale_stride_head % 4)
+      return fail(err, ATTN_ERR_INVALID_ARGUMENT, "per-vector scale strides must be >= 16 and multiples of 4 floats");
+  }
   return ATTN_OK;
 }
 
@@ -179,7 +190,8 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
     // workgroups when sequences are shorter than the capacity.
     const int cap_cu = pl->mfma ? kMfmaWgPerCu : kValuWgPerCu;
     int per_cu = ctx->host_only ? cap_cu
-                                : pa::decode_blocks_per_cu(pl->mfma, kv->dtype, io->q_dtype, D, rows);
+                                : pa::decode_blocks_per_cu(pl->mfma, kv->dtype, io->q_dtype, D, rows,
+                                                           kv->k_vscales != nullptr);
     per_cu = std::max(1, std::min(per_cu, cap_cu));
     const int64_t slots = (int64_t)ctx->num_cus * per_cu;
     const int64_t target = std::max<int64_t>(1, slots / groups);
@@ -268,6 +280,8 @@ attn_status prefill_common(attn_ctx *ctx, const attn_io *io, const attn_kv *kv, 
   a.mask = sparse ? opts->block_mask : nullptr;
   a.mask_heads = opts->mask_heads; a.mask_block = opts->mask_block;
   a.mask_nqb = opts->mask_q_blocks; a.mask_nkb = opts->mask_k_blocks;
+  a.k_vs = kv->k_vscales; a.v_vs = kv->v_vscales;
+  a.vs_sp = kv->vscale_stride_page; a.vs_sh = kv->vscale_stride_head;
   a.q_tiles = (int)ceil_div(io->q_rows, 128);
   a.heads_per_wg = (G % 2 == 0) ? 2 : 1;
   // groups dealt over 8 XCDs (padded), each with q_tiles tasks of G/HPW workgroups
@@ -378,6 +392,8 @@ attn_status attn_paged_decode(attn_ctx *ctx, const attn_io *io, const attn_kv *k
   a.o_sb = io->o_stride_b; a.o_sr = io->o_stride_row; a.o_sh = io->o_stride_head;
   a.lse = io->lse;
   a.rows_b = opts->rows_per_seq;
+  a.k_vs = kv->k_vscales; a.v_vs = kv->v_vscales;
+  a.vs_sp = kv->vscale_stride_page; a.vs_sh = kv->vscale_stride_head;
   a.P = pl.P; a.T = pl.T;
   a.row_blocks = pl.row_blocks;
   a.ws_o = reinterpret_cast<float *>(workspace);
@@ -417,6 +433,8 @@ attn_status attn_debug_gather_kv(attn_ctx *ctx, const attn_kv *kv, int32_t b, in
   return launched(pa::launch_debug_gather(kv->k_pages, kv->v_pages, kv->k_stride_page, kv->k_stride_head,
                                           kv->v_stride_page, kv->v_stride_head, kv->dtype,
                                           kv->num_kv_heads, kv->head_dim, kv->k_scale, kv->v_scale,
+                                          kv->k_vscales, kv->v_vscales, kv->vscale_stride_page,
+                                          kv->vscale_stride_head,
                                           kv->page_table + (int64_t)b * kv->page_table_stride, seq_len,
                                           k_out, v_out, (hipStream_t)hip_stream),
                   err, "debug gather launch");
@@ -443,6 +461,8 @@ attn_status attn_kv_append(attn_ctx *ctx, const attn_kv *kv, const attn_kv_rows 
   }
   if (rows->stride_head < kv->head_dim)
     return fail(err, ATTN_ERR_INVALID_ARGUMENT, "rows head stride below head_dim");
+  if (kv->k_vscales && (kv->k_scale != 1.0f || kv->v_scale != 1.0f))
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "an append with per-vector scales needs k_scale = v_scale = 1");
   if (ctx->host_only) return fail(err, ATTN_ERR_DEVICE, "host-only context: nothing enqueued");
   DeviceGuard g(ctx->device);
   if (!g.ok) return fail(err, ATTN_ERR_DEVICE, "cannot select device %d", ctx->device);
@@ -470,6 +490,10 @@ attn_status attn_kv_append(attn_ctx *ctx, const attn_kv *kv, const attn_kv_rows 
   a.D = kv->head_dim;
   a.k_scale = kv->k_scale;
   a.v_scale = kv->v_scale;
+  a.k_vs = const_cast<float *>(kv->k_vscales);
+  a.v_vs = const_cast<float *>(kv->v_vscales);
+  a.vs_sp = kv->vscale_stride_page;
+  a.vs_sh = kv->vscale_stride_head;
   return launched(pa::launch_kv_append(a, (hipStream_t)hip_stream), err, "K/V append launch");
 }
 

@@ -6,7 +6,15 @@
 // L_b = min(seq_lens[b], capacity): page_table[b][p / 16], slot p % 16.  The
 // stored value is src / scale (one IEEE single-precision division), rounded to
 // the storage type to nearest, ties to even; F16/BF16 overflow to infinity,
-// e4m3fn saturates at +-448; NaN stays NaN.
+// e4m3fn saturates at +-448, e5m2 saturates finite values at +-57344 and keeps
+// infinities; NaN stays NaN.
+//
+// With per-vector scales (8-bit storage, template flag VS; Geramy/LSE README,
+// "K/V storage": fp8 and bf8 caches with scales) the scale of each new K or V
+// vector is amax / fmax (amax over its finite entries, fmax the format's
+// largest finite value; 1 if that is 0): the threads of a token row reduce
+// their maxima with lane exchanges, one of them stores the scale, and every
+// element is divided by it before rounding.
 //
 // One workgroup owns the new slots of four consecutive pages of one (sequence,
 // KV head): each thread converts 8 consecutive elements of a token row, stores
@@ -54,6 +62,25 @@ __device__ __forceinline__ uint32_t enc_e4m3(float y) {
   return s | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
 }
 
+// OCP e5m2 (bias 15, largest finite 57344 = 0x7b), finite values saturating,
+// infinities kept
+__device__ __forceinline__ uint32_t enc_e5m2(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t s = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return s | 0x7fu;                   // NaN
+  if (a == 0x7f800000u) return s | 0x7cu;                  // infinity
+  if (a >= 0x47600000u) return s | 0x7bu;                  // >= 57344: saturate
+  if (a >= 0x38800000u) {                                  // normal: >= 2^-14
+    // round the f32 (exponent, 2 leading mantissa bits) to nearest even;
+    // rebias 127 -> 15: subtract 112 << 2
+    const uint32_t t = (a + 0xfffffu + ((a >> 21) & 1u)) >> 21;
+    return s | (t - 448u);
+  }
+  // subnormal: multiples of 2^-16 (exact scaling, then round to nearest even)
+  return s | (uint32_t)__builtin_rintf(__uint_as_float(a) * 65536.0f);
+}
+
 template <int SRC>
 __device__ __forceinline__ void load8(const char *p, float *x) {
   if constexpr (SRC == DT_F32) {
@@ -80,7 +107,28 @@ __device__ __forceinline__ uint32_t encode(float y) {
   if constexpr (KVDT == DT_F32) return __float_as_uint(y);
   else if constexpr (KVDT == DT_BF16) return enc_bf16(y);
   else if constexpr (KVDT == DT_F16) return enc_f16(y);
+  else if constexpr (KVDT == DT_BF8) return enc_e5m2(y);
   else return enc_e4m3(y);
+}
+
+// largest finite value of an 8-bit storage type
+template <int KVDT>
+constexpr float fmax8() { return KVDT == DT_BF8 ? 57344.0f : 448.0f; }
+
+// per-vector scale of the token row whose TPT threads (consecutive lanes,
+// 8 values each) hold x: amax over the finite values / fmax, 1 if that is 0
+template <int KVDT, int TPT>
+__device__ __forceinline__ float vector_scale(const float *x) {
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float v = __builtin_fabsf(x[e]);
+    m = v <= 3.402823466e38f ? __builtin_fmaxf(m, v) : m;   // NaN and inf do not count
+  }
+#pragma unroll
+  for (int k = 1; k < TPT; k <<= 1) m = __builtin_fmaxf(m, shfl_xor(m, k));
+  const float u = m / fmax8<KVDT>();
+  return u == 0.f ? 1.f : u;
 }
 
 // 8 codes -> one store of 8 elements of the storage type
@@ -89,7 +137,7 @@ __device__ __forceinline__ void store8(char *p, const uint32_t *c) {
   if constexpr (KVDT == DT_F32) {
     *reinterpret_cast<u32x4 *>(p) = u32x4{c[0], c[1], c[2], c[3]};
     *reinterpret_cast<u32x4 *>(p + 16) = u32x4{c[4], c[5], c[6], c[7]};
-  } else if constexpr (KVDT == DT_FP8) {
+  } else if constexpr (is8bit(KVDT)) {
     u32x2 w;
     w[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
     w[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
@@ -105,7 +153,7 @@ template <int KVDT>
 __device__ __forceinline__ void store_vec(char *p, const uint32_t *c) {
   if constexpr (KVDT == DT_F32) {
     *reinterpret_cast<u32x4 *>(p) = u32x4{c[0], c[1], c[2], c[3]};
-  } else if constexpr (KVDT == DT_FP8) {
+  } else if constexpr (is8bit(KVDT)) {
     u32x4 w;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -120,11 +168,11 @@ __device__ __forceinline__ void store_vec(char *p, const uint32_t *c) {
 template <int KVDT>
 __device__ __forceinline__ void store1(char *p, uint32_t c) {
   if constexpr (KVDT == DT_F32) *reinterpret_cast<uint32_t *>(p) = c;
-  else if constexpr (KVDT == DT_FP8) *reinterpret_cast<uint8_t *>(p) = (uint8_t)c;
+  else if constexpr (is8bit(KVDT)) *reinterpret_cast<uint8_t *>(p) = (uint8_t)c;
   else *reinterpret_cast<uint16_t *>(p) = (uint16_t)c;
 }
 
-template <int KVDT, int SRC, int D>
+template <int KVDT, int SRC, int D, bool VS>
 __global__ __launch_bounds__(kAppendThreads) void kv_append(AppendArgs a) {
   constexpr int ELT = DtInfo<KVDT>::bytes;
   constexpr int SELT = DtInfo<SRC>::bytes;
@@ -158,11 +206,22 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append(AppendArgs a) {
     float xk[8], xv[8];
     load8<SRC>(ksrc + off, xk);
     load8<SRC>(vsrc + off, xv);
+    float uk = a.k_scale, uv = a.v_scale;
+    if constexpr (VS) {
+      // a slot's TPT threads are consecutive lanes of one wave, all present
+      uk = vector_scale<KVDT, TPT>(xk);
+      uv = vector_scale<KVDT, TPT>(xv);
+      if (part == 0) {
+        const int64_t si = (int64_t)pt[page0 + slot / 16] * a.vs_sp + (int64_t)g * a.vs_sh + slot % 16;
+        a.k_vs[si] = uk;
+        a.v_vs[si] = uv;
+      }
+    }
     uint32_t ck[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      ck[e] = encode<KVDT>(xk[e] / a.k_scale);
-      vstage[slot][part * 8 + e] = encode<KVDT>(xv[e] / a.v_scale);
+      ck[e] = encode<KVDT>(xk[e] / uk);
+      vstage[slot][part * 8 + e] = encode<KVDT>(xv[e] / uv);
     }
     store8<KVDT>(tile(a.k, a.k_sp, a.k_sh, slot) + ((int64_t)(slot % 16) * D + part * 8) * ELT, ck);
   }
@@ -185,32 +244,38 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append(AppendArgs a) {
   }
 }
 
-template <int KV, int SRC>
+template <int KV, int SRC, bool VS>
 hipError_t append_d(const AppendArgs &a, hipStream_t s) {
   auto grid = [&](int pages) { return dim3(((a.n_new + 15) / 16 + 1 + pages - 1) / pages, a.Hkv, a.B); };
-  if (a.D == 64) hipLaunchKernelGGL((kv_append<KV, SRC, 64>), grid(append_pages<64>()), dim3(kAppendThreads), 0, s, a);
-  else if (a.D == 128) hipLaunchKernelGGL((kv_append<KV, SRC, 128>), grid(append_pages<128>()), dim3(kAppendThreads), 0, s, a);
-  else hipLaunchKernelGGL((kv_append<KV, SRC, 256>), grid(append_pages<256>()), dim3(kAppendThreads), 0, s, a);
+  if (a.D == 64) hipLaunchKernelGGL((kv_append<KV, SRC, 64, VS>), grid(append_pages<64>()), dim3(kAppendThreads), 0, s, a);
+  else if (a.D == 128) hipLaunchKernelGGL((kv_append<KV, SRC, 128, VS>), grid(append_pages<128>()), dim3(kAppendThreads), 0, s, a);
+  else hipLaunchKernelGGL((kv_append<KV, SRC, 256, VS>), grid(append_pages<256>()), dim3(kAppendThreads), 0, s, a);
   return hipGetLastError();
 }
 
-template <int KV>
+template <int KV, bool VS>
 hipError_t append_s(const AppendArgs &a, hipStream_t s) {
   switch (a.src_dtype) {
-    case DT_F32: return append_d<KV, DT_F32>(a, s);
-    case DT_F16: return append_d<KV, DT_F16>(a, s);
-    default: return append_d<KV, DT_BF16>(a, s);
+    case DT_F32: return append_d<KV, DT_F32, VS>(a, s);
+    case DT_F16: return append_d<KV, DT_F16, VS>(a, s);
+    default: return append_d<KV, DT_BF16, VS>(a, s);
   }
+}
+
+template <int KV>
+hipError_t append_8(const AppendArgs &a, hipStream_t s) {
+  return a.k_vs ? append_s<KV, true>(a, s) : append_s<KV, false>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_kv_append(const AppendArgs &a, hipStream_t s) {
   switch (a.kv_dtype) {
-    case DT_F32: return append_s<DT_F32>(a, s);
-    case DT_F16: return append_s<DT_F16>(a, s);
-    case DT_BF16: return append_s<DT_BF16>(a, s);
-    default: return append_s<DT_FP8>(a, s);
+    case DT_F32: return append_s<DT_F32, false>(a, s);
+    case DT_F16: return append_s<DT_F16, false>(a, s);
+    case DT_BF16: return append_s<DT_BF16, false>(a, s);
+    case DT_FP8: return append_8<DT_FP8>(a, s);
+    default: return append_8<DT_BF8>(a, s);
   }
 }
 

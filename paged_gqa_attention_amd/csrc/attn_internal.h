@@ -36,6 +36,8 @@ struct DecodeArgs {
   float *ws_o;            // [B][Hkv][rows][P][D]   unnormalised partial outputs
   float *ws_ml;           // [B][Hkv][rows][P][2]   partial max (log2 units) and sum
   const int32_t *rows_b;  // nullable [B]: rows of each sequence (<= R); the rest are skipped
+  const float *k_vs, *v_vs;   // per-vector scales [page][head][16] (8-bit K/V), or null
+  int64_t vs_sp, vs_sh;       // their page / head strides (floats)
 };
 
 struct PrefillArgs {
@@ -61,6 +63,8 @@ struct PrefillArgs {
   int32_t q_tiles;        // ceil(n_q / 128)
   int32_t heads_per_wg;   // 1 or 2 query heads of one group per workgroup
   int32_t num_wg;         // total workgroups
+  const float *k_vs, *v_vs;   // per-vector scales [page][head][16] (8-bit K/V), or null
+  int64_t vs_sp, vs_sh;
 };
 
 // K/V append: new rows [B][n_new][Hkv][D] (source strides) into the paged pool
@@ -77,6 +81,8 @@ struct AppendArgs {
   const int32_t *lens;
   int32_t B, n_new, Hkv, D;
   float k_scale, v_scale;
+  float *k_vs, *v_vs;         // per-vector scale pools (written), or null
+  int64_t vs_sp, vs_sh;
 };
 
 hipError_t launch_kv_append(const AppendArgs &a, hipStream_t s);
@@ -87,15 +93,18 @@ hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t s);
 bool decode_mfma_supported(int kv_dtype, int q_dtype, int D, int rows);
 bool decode_valu_supported(int kv_dtype, int q_dtype, int D);
 // resident workgroups per CU of the partial kernel selected for these arguments
-int decode_blocks_per_cu(bool mfma, int kv_dtype, int q_dtype, int D, int rows);
+// (vs: per-vector scales)
+int decode_blocks_per_cu(bool mfma, int kv_dtype, int q_dtype, int D, int rows, bool vs);
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 bool prefill_supported(int kv_dtype, int q_dtype, int D);
 
 hipError_t launch_debug_gather(const void *k, const void *v, int64_t k_sp, int64_t k_sh,
                                int64_t v_sp, int64_t v_sh, int kv_dtype, int Hkv, int D,
-                               float k_scale, float v_scale, const int32_t *pt_row, int seq_len,
-                               float *k_out, float *v_out, hipStream_t s);
+                               float k_scale, float v_scale, const float *k_vs,
+                               const float *v_vs, int64_t vs_sp, int64_t vs_sh,
+                               const int32_t *pt_row, int seq_len, float *k_out, float *v_out,
+                               hipStream_t s);
 
 // read-only HBM probes (pattern 0: contiguous, 1: 4 KiB tiles in `order`)
 hipError_t launch_read_probe(const void *buf, size_t bytes, int pattern, const int32_t *order,

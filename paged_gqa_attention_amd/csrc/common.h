@@ -7,13 +7,17 @@
 
 namespace pa {
 
-enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3 };
+// storage types; FP8 is OCP e4m3fn, BF8 is OCP e5m2
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3, DT_BF8 = 4 };
 
 template <int DT> struct DtInfo;
 template <> struct DtInfo<DT_F32>  { static constexpr int bytes = 4; };
 template <> struct DtInfo<DT_F16>  { static constexpr int bytes = 2; };
 template <> struct DtInfo<DT_BF16> { static constexpr int bytes = 2; };
 template <> struct DtInfo<DT_FP8>  { static constexpr int bytes = 1; };
+template <> struct DtInfo<DT_BF8>  { static constexpr int bytes = 1; };
+
+__host__ __device__ constexpr bool is8bit(int dt) { return dt == DT_FP8 || dt == DT_BF8; }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -48,25 +52,36 @@ __device__ __forceinline__ float f16_lo(uint32_t w) {
 __device__ __forceinline__ float f16_hi(uint32_t w) {
   return (float)__builtin_bit_cast(f16x2, w)[1];
 }
-// two e4m3fn codes (bytes 0,1 if !HI, else 2,3 of w) to FP32, exact
-template <bool HI>
-__device__ __forceinline__ f32x2 fp8x2_to_f32(uint32_t w) {
-  return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+// Two 8-bit codes of type KV (bytes 0,1 of w if !HI, else 2,3) to FP32,
+// exact.  e4m3fn and e5m2 values are all representable in FP32, bf16 and
+// f16, so every conversion below is exact.
+template <int KV, bool HI>
+__device__ __forceinline__ f32x2 e8x2_to_f32(uint32_t w) {
+  if constexpr (KV == DT_BF8) return __builtin_amdgcn_cvt_pk_f32_bf8(w, HI);
+  else return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
 }
-// two e4m3fn codes to a packed bf16 / f16 pair, exact (scale 1.0)
-template <bool HI>
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+// two codes to a packed bf16 / f16 pair.  The scaled conversions take only the
+// exponent of their FP32 scale operand (measured on gfx950): with 1.0 they are
+// plain exact conversions.
+template <int KV, bool HI>
+__device__ __forceinline__ uint32_t e8x2_to_bf16x2(uint32_t w) {
+  if constexpr (KV == DT_BF8)
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HI));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
-template <bool HI>
-__device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+template <int KV, bool HI>
+__device__ __forceinline__ uint32_t e8x2_to_f16x2(uint32_t w) {
+  if constexpr (KV == DT_BF8)
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, HI));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
 }
 // to the 16-bit MFMA/dot operand type (f16 if F16 else bf16)
-template <bool F16, bool HI>
-__device__ __forceinline__ uint32_t fp8x2_to_16(uint32_t w) {
-  if constexpr (F16) return fp8x2_to_f16x2<HI>(w);
-  else return fp8x2_to_bf16x2<HI>(w);
+template <int KV, bool F16, bool HI>
+__device__ __forceinline__ uint32_t e8x2_to_16(uint32_t w) {
+  if constexpr (F16) return e8x2_to_f16x2<KV, HI>(w);
+  else return e8x2_to_bf16x2<KV, HI>(w);
 }
 
 // element e of a 16-byte chunk of dtype DT, to FP32
@@ -82,7 +97,7 @@ __device__ __forceinline__ float chunk_elem(const u32x4 &c, int e) {
     return (e & 1) ? f16_hi(w) : f16_lo(w);
   } else {
     uint32_t w = c[e >> 2];
-    f32x2 v = (e & 2) ? fp8x2_to_f32<true>(w) : fp8x2_to_f32<false>(w);
+    f32x2 v = (e & 2) ? e8x2_to_f32<DT, true>(w) : e8x2_to_f32<DT, false>(w);
     return (e & 1) ? v[1] : v[0];
   }
 }

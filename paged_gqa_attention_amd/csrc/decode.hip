@@ -20,6 +20,9 @@
 //                S^T = K.Q^T and O^T += V^T.P^T, so every lane's softmax row
 //                matches its accumulator row and V tiles (token-minor pages)
 //                load straight into MFMA operands.
+// With per-vector scales (8-bit K/V, template flag VS) a token's K scale
+// multiplies its scores and its V scale its softmax weights before P.V; the
+// row sums use the unscaled weights.
 #include "attn_internal.h"
 #include "common.h"
 
@@ -149,14 +152,14 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
 //      g = 64c + lane; chunk g is value row g / CPR, tokens (g % CPR) * EPC + e.
 //   After the quad sum every lane knows all rows' scores of its token and
 //   handles the softmax of rows r = qq + 4k.
-template <int KVDT, int QDT, int D, int RB>
+template <int KVDT, int QDT, int D, int RB, bool VS>
 __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
   constexpr int ELT = DtInfo<KVDT>::bytes;
   constexpr int NL = D * ELT / 64;   // 16-byte chunks per lane per page, for K and for V
   constexpr int EPC = 16 / ELT;      // elements per chunk
   constexpr int CPR = ELT;           // V chunks per value row (16 tokens * ELT bytes)
   constexpr int MR = RB / 4;         // softmax rows per lane
-  constexpr int QW = (KVDT == DT_F32) ? 4 : (KVDT == DT_FP8 ? 8 : 4);  // Q words per K chunk
+  constexpr int QW = (KVDT == DT_F32) ? 4 : (is8bit(KVDT) ? 8 : 4);  // Q words per K chunk
 
   // query rows of the workgroup, in the arithmetic's representation:
   // FP32 for FP32 K/V, else the 16-bit Q codes
@@ -249,7 +252,10 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
     return k < 64 ? __builtin_amdgcn_readlane(ids[0], k) : __builtin_amdgcn_readlane(ids[1], k - 64);
   };
 
-  auto load_page = [&](int page_idx, u32x4 *kd, u32x4 *vd) {
+  // per-vector scales: lane n's token (the quad shares it)
+  const float *ksbase = VS ? a.k_vs + (int64_t)kvh * a.vs_sh + n : nullptr;
+  const float *vsbase = VS ? a.v_vs + (int64_t)kvh * a.vs_sh + n : nullptr;
+  auto load_page = [&](int page_idx, u32x4 *kd, u32x4 *vd, float &ksd, float &vsd) {
     const int64_t pid = page_id(page_idx);
     const char *kp = kbase + pid * a.k_sp * ELT + n * (D * ELT) + qq * 16;
     const char *vp = vbase + pid * a.v_sp * ELT + lane * 16;
@@ -258,9 +264,13 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
       kd[c] = ld16(kp + c * 64);
       vd[c] = ld16(vp + c * 1024);
     }
+    if constexpr (VS) {
+      ksd = ksbase[pid * a.vs_sp];
+      vsd = vsbase[pid * a.vs_sp];
+    }
   };
 
-  auto process_page = [&](const int pg, const u32x4 *kc, const u32x4 *vc) {
+  auto process_page = [&](const int pg, const u32x4 *kc, const u32x4 *vc, float ksc, float vsc) {
     // ---- scores of this lane's token for all rows ----
     float s[RB];
 #pragma unroll
@@ -280,11 +290,11 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
         } else if constexpr (KVDT == DT_F16) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc = dot2_f16(qw[e], kc[c][e], acc);
-        } else {  // FP8 K -> 16-bit pairs of Q's type
+        } else {  // 8-bit K -> 16-bit pairs of Q's type
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            uint32_t lo = fp8x2_to_16<QDT != DT_BF16, false>(kc[c][e]);
-            uint32_t hi = fp8x2_to_16<QDT != DT_BF16, true>(kc[c][e]);
+            uint32_t lo = e8x2_to_16<KVDT, QDT != DT_BF16, false>(kc[c][e]);
+            uint32_t hi = e8x2_to_16<KVDT, QDT != DT_BF16, true>(kc[c][e]);
             if constexpr (QDT == DT_BF16) {
               acc = dot2_bf16(qw[2 * e], lo, acc);
               acc = dot2_bf16(qw[2 * e + 1], hi, acc);
@@ -314,11 +324,14 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
     // ---- online softmax for this lane's rows ----
     const int tok = pg * 16 + n;
     const bool page_full = (pg * 16 + 16 <= t1);
+    const float sc_tok = VS ? a.score_scale * ksc : a.score_scale;
+    // a slot past the end may hold any scale: its weight is 0 and stays 0
+    const float v_tok = (VS && tok < t1) ? vsc : 0.f;
 #pragma unroll
     for (int k = 0; k < MR; ++k) {
       const float v = mine[k];
       const bool valid = tok < t1 && tok <= pos_mine[k];
-      const float x = valid ? v * a.score_scale : kNegInf;
+      const float x = valid ? v * sc_tok : kNegInf;
       float mx = x;
       mx = __builtin_fmaxf(mx, dpp<kDppRowRor4>(mx));
       mx = __builtin_fmaxf(mx, dpp<kDppRowRor8>(mx));
@@ -330,7 +343,7 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
       const float pv = fast_exp2(x - m_use);
       l_run[k] = l_run[k] * alpha + pv;
       m_run[k] = m_new;
-      p_lds[wave][n][qq + 4 * k] = pv;
+      p_lds[wave][n][qq + 4 * k] = VS ? pv * v_tok : pv;
       if (n == 0) alpha_lds[wave][qq + 4 * k] = alpha;
     }
     wave_lds_sync();
@@ -365,14 +378,15 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
   // Two page buffers in ping-pong: while one page is processed the other's
   // loads stay in flight (no register copies, which would force a full wait).
   u32x4 kA[NL], vA[NL], kB[NL], vB[NL];
-  if (pg < pg_end) load_page(pg, kA, vA);
-  if (pg + kWaves < pg_end) load_page(pg + kWaves, kB, vB);
+  float ksA = 1.f, vsA = 1.f, ksB = 1.f, vsB = 1.f;
+  if (pg < pg_end) load_page(pg, kA, vA, ksA, vsA);
+  if (pg + kWaves < pg_end) load_page(pg + kWaves, kB, vB, ksB, vsB);
   for (; pg < pg_end; pg += 2 * kWaves) {
-    process_page(pg, kA, vA);
-    if (pg + 2 * kWaves < pg_end) load_page(pg + 2 * kWaves, kA, vA);
+    process_page(pg, kA, vA, ksA, vsA);
+    if (pg + 2 * kWaves < pg_end) load_page(pg + 2 * kWaves, kA, vA, ksA, vsA);
     if (pg + kWaves < pg_end) {
-      process_page(pg + kWaves, kB, vB);
-      if (pg + 3 * kWaves < pg_end) load_page(pg + 3 * kWaves, kB, vB);
+      process_page(pg + kWaves, kB, vB, ksB, vsB);
+      if (pg + 3 * kWaves < pg_end) load_page(pg + 3 * kWaves, kB, vB, ksB, vsB);
     }
   }
 
@@ -463,7 +477,7 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
 // 16-byte read of a token-minor V page.
 template <int KVDT, int QDT>
 struct MfmaT {
-  static constexpr bool f16 = (KVDT == DT_F16) || (KVDT == DT_FP8 && QDT == DT_F16);
+  static constexpr bool f16 = (KVDT == DT_F16) || (is8bit(KVDT) && QDT == DT_F16);
 };
 
 template <bool F16>
@@ -479,18 +493,18 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b, const f3
 // d offset of the 8 elements lane group j supplies for 32-wide d chunk kc
 template <int KVDT>
 __device__ __forceinline__ int dchunk(int kc, int j) {
-  if constexpr (KVDT == DT_FP8) return 64 * (kc >> 1) + 16 * j + 8 * (kc & 1);
+  if constexpr (is8bit(KVDT)) return 64 * (kc >> 1) + 16 * j + 8 * (kc & 1);
   else return 32 * kc + 8 * j;
 }
 
-template <int KVDT, int QDT, int D, int NB>
+template <int KVDT, int QDT, int D, int NB, bool VS>
 __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
   constexpr int ELT = DtInfo<KVDT>::bytes;
   constexpr bool F16 = MfmaT<KVDT, QDT>::f16;
   constexpr int KC = D / 32;           // 32-wide d chunks
   constexpr int MB = D / 16;           // 16-row value blocks
   constexpr int NR = 16 * NB;          // padded rows
-  constexpr int KL = (KVDT == DT_FP8) ? KC / 2 : KC;  // 16-byte K loads per `a`
+  constexpr int KL = is8bit(KVDT) ? KC / 2 : KC;  // 16-byte K loads per `a`
 
   __shared__ float m_w[kWaves][NR];
   __shared__ float l_w[kWaves][NR];
@@ -554,7 +568,9 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
 
   // K rows: A row m = n of MFMA `a` holds token 8*(n/4) + 4a + n%4 (page-pair local)
   // V rows: value row 16*mb + n, tokens 8*j .. 8*j+7 (page j/2, offset 8*(j&1))
-  auto load_pair = [&](int ppi, u32x4 (*kd)[KL], u32x4 *vd16, u32x2 *vd8) {
+  // Per-vector scales: the K and V scales of the lane's score tokens 8j .. 8j+7
+  // (sd[0..1] K, sd[2..3] V).
+  auto load_pair = [&](int ppi, u32x4 (*kd)[KL], u32x4 *vd16, u32x2 *vd8, f32x4 *sd) {
     const int k = (ppi - pp_first) / kWaves;
     const int64_t pid0 = __builtin_amdgcn_readlane(ids0, k);
     const int64_t pid1 = __builtin_amdgcn_readlane(ids1, k);
@@ -565,7 +581,7 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
       const char *kp = kbase + pid * a.k_sp * ELT + (tok & 15) * (D * ELT);
 #pragma unroll
       for (int u = 0; u < KL; ++u) {
-        const int d0 = (KVDT == DT_FP8) ? 64 * u + 16 * j : dchunk<KVDT>(u, j);
+        const int d0 = is8bit(KVDT) ? 64 * u + 16 * j : dchunk<KVDT>(u, j);
         kd[aa][u] = ld16(kp + d0 * ELT);
       }
     }
@@ -574,11 +590,21 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const char *row = vp + (int64_t)(16 * mb + n) * 16 * ELT;
-      if constexpr (KVDT == DT_FP8) vd8[mb] = ld8(row);
+      if constexpr (is8bit(KVDT)) vd8[mb] = ld8(row);
       else vd16[mb] = ld16(row);
     }
+    if constexpr (VS) {
+      const int64_t so = pidv * a.vs_sp + (int64_t)kvh * a.vs_sh + 8 * (j & 1);
+      const f32x4 *kq = reinterpret_cast<const f32x4 *>(a.k_vs + so);
+      const f32x4 *vq = reinterpret_cast<const f32x4 *>(a.v_vs + so);
+      sd[0] = kq[0];
+      sd[1] = kq[1];
+      sd[2] = vq[0];
+      sd[3] = vq[1];
+    }
   };
-  auto process_pair = [&](const int pp, const u32x4 (*kf)[KL], const u32x4 *vf16, const u32x2 *vf8) {
+  auto process_pair = [&](const int pp, const u32x4 (*kf)[KL], const u32x4 *vf16, const u32x2 *vf8,
+                          const f32x4 *sd) {
     // ---- S^T = K Q^T ----
     f32x4 s[NB][2];
 #pragma unroll
@@ -589,17 +615,17 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
     for (int aa = 0; aa < 2; ++aa) {
 #pragma unroll
       for (int u = 0; u < KL; ++u) {
-        if constexpr (KVDT == DT_FP8) {
-          // 16 FP8 codes -> two 8-element 16-bit fragments (chunks kc = 2u, 2u+1)
+        if constexpr (is8bit(KVDT)) {
+          // 16 8-bit codes -> two 8-element 16-bit fragments (chunks kc = 2u, 2u+1)
           u32x4 lo, hi;
 #pragma unroll
           for (int w = 0; w < 2; ++w) {
             const uint32_t x = kf[aa][u][w];
             const uint32_t y = kf[aa][u][w + 2];
-            lo[2 * w] = fp8x2_to_16<F16, false>(x);
-            lo[2 * w + 1] = fp8x2_to_16<F16, true>(x);
-            hi[2 * w] = fp8x2_to_16<F16, false>(y);
-            hi[2 * w + 1] = fp8x2_to_16<F16, true>(y);
+            lo[2 * w] = e8x2_to_16<KVDT, F16, false>(x);
+            lo[2 * w + 1] = e8x2_to_16<KVDT, F16, true>(x);
+            hi[2 * w] = e8x2_to_16<KVDT, F16, false>(y);
+            hi[2 * w + 1] = e8x2_to_16<KVDT, F16, true>(y);
           }
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
@@ -615,6 +641,14 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
 
     // ---- online softmax: lane row 16*nb + n, tokens 8j .. 8j+7 ----
     const int tokb = pp * 32 + 8 * j;
+    // score multipliers and V weights of the 8 tokens (per-vector scales); a
+    // slot past the end may hold any scale: its weight is 0 and stays 0
+    float sk[8], vw[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sk[e] = VS ? a.score_scale * sd[e >> 2][e & 3] : a.score_scale;
+      vw[e] = (VS && tokb + e < t1) ? sd[2 + (e >> 2)][e & 3] : 0.f;
+    }
     u32x4 pf[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -625,7 +659,7 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
         for (int i = 0; i < 4; ++i) {
           const int tok = tokb + 4 * aa + i;
           const bool valid = tok < t1 && tok <= pos[nb];
-          x[4 * aa + i] = valid ? s[nb][aa][i] * a.score_scale : kNegInf;
+          x[4 * aa + i] = valid ? s[nb][aa][i] * sk[4 * aa + i] : kNegInf;
         }
       float mx = max3(x[0], x[1], x[2]);
       mx = max3(mx, x[3], x[4]);
@@ -646,6 +680,10 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
       l_run[nb] = l_run[nb] * alpha + ps;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) oacc[mb][nb] *= alpha;
+      if constexpr (VS) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] *= vw[e];
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         pf[nb][e] = F16 ? pack_f16x2(pv[2 * e], pv[2 * e + 1]) : pack_bf16x2(pv[2 * e], pv[2 * e + 1]);
@@ -656,11 +694,11 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       u32x4 vfr;
-      if constexpr (KVDT == DT_FP8) {
-        vfr[0] = fp8x2_to_16<F16, false>(vf8[mb][0]);
-        vfr[1] = fp8x2_to_16<F16, true>(vf8[mb][0]);
-        vfr[2] = fp8x2_to_16<F16, false>(vf8[mb][1]);
-        vfr[3] = fp8x2_to_16<F16, true>(vf8[mb][1]);
+      if constexpr (is8bit(KVDT)) {
+        vfr[0] = e8x2_to_16<KVDT, F16, false>(vf8[mb][0]);
+        vfr[1] = e8x2_to_16<KVDT, F16, true>(vf8[mb][0]);
+        vfr[2] = e8x2_to_16<KVDT, F16, false>(vf8[mb][1]);
+        vfr[3] = e8x2_to_16<KVDT, F16, true>(vf8[mb][1]);
       } else {
         vfr = vf16[mb];
       }
@@ -684,14 +722,15 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
   u32x4 kA[2][KL], kB[2][KL];
   u32x4 vA16[MB], vB16[MB];
   u32x2 vA8[MB], vB8[MB];
-  if (pp < pp_end) load_pair(pp, kA, vA16, vA8);
-  if (pp + kWaves < pp_end) load_pair(pp + kWaves, kB, vB16, vB8);
+  f32x4 sA[4], sB[4];
+  if (pp < pp_end) load_pair(pp, kA, vA16, vA8, sA);
+  if (pp + kWaves < pp_end) load_pair(pp + kWaves, kB, vB16, vB8, sB);
   for (; pp < pp_end; pp += 2 * kWaves) {
-    process_pair(pp, kA, vA16, vA8);
-    if (pp + 2 * kWaves < pp_end) load_pair(pp + 2 * kWaves, kA, vA16, vA8);
+    process_pair(pp, kA, vA16, vA8, sA);
+    if (pp + 2 * kWaves < pp_end) load_pair(pp + 2 * kWaves, kA, vA16, vA8, sA);
     if (pp + kWaves < pp_end) {
-      process_pair(pp + kWaves, kB, vB16, vB8);
-      if (pp + 3 * kWaves < pp_end) load_pair(pp + 3 * kWaves, kB, vB16, vB8);
+      process_pair(pp + kWaves, kB, vB16, vB8, sB);
+      if (pp + 3 * kWaves < pp_end) load_pair(pp + 3 * kWaves, kB, vB16, vB8, sB);
     }
   }
 
@@ -757,13 +796,15 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
 
 // ==================================================================================
 // Debug gather: K/V of one sequence through the page table, dequantised the
-// way the kernels do it (FP8 through both the FP32 and the 16-bit routes;
-// a disagreement between the two is reported as NaN).
+// way the kernels do it (8-bit codes through both the FP32 and the 16-bit
+// routes; a disagreement between the two is reported as NaN), times the
+// per-vector scale (VS) and then the per-tensor scale, in FP32.
 // ==================================================================================
-template <int KVDT>
+template <int KVDT, bool VS>
 __global__ void debug_gather(const void *k, const void *v, int64_t k_sp, int64_t k_sh,
                              int64_t v_sp, int64_t v_sh, int Hkv, int D, float k_scale,
-                             float v_scale, const int32_t *pt, int seq_len, float *k_out,
+                             float v_scale, const float *k_vs, const float *v_vs, int64_t vs_sp,
+                             int64_t vs_sh, const int32_t *pt, int seq_len, float *k_out,
                              float *v_out) {
   const int64_t total = (int64_t)Hkv * seq_len * D;
   for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
@@ -788,13 +829,18 @@ __global__ void debug_gather(const void *k, const void *v, int64_t k_sp, int64_t
         kv[s] = f16_lo(reinterpret_cast<const uint16_t *>(base[s])[e]);
       } else {
         const uint32_t code = reinterpret_cast<const uint8_t *>(base[s])[e];
-        const float a32 = fp8x2_to_f32<false>(code)[0];
-        const float b16 = bf16_lo(fp8x2_to_bf16x2<false>(code));
-        const float h16 = f16_lo(fp8x2_to_f16x2<false>(code));
+        const float a32 = e8x2_to_f32<KVDT, false>(code)[0];
+        const float b16 = bf16_lo(e8x2_to_bf16x2<KVDT, false>(code));
+        const float h16 = f16_lo(e8x2_to_f16x2<KVDT, false>(code));
         const bool agree = (__float_as_uint(a32) == __float_as_uint(b16)) &&
                            (__float_as_uint(a32) == __float_as_uint(h16));
         kv[s] = (agree || a32 != a32) ? a32 : __builtin_nanf("");
       }
+    }
+    if constexpr (VS) {
+      const int64_t si = pid * vs_sp + g * vs_sh + (t & 15);
+      kv[0] = kv[0] * k_vs[si];
+      kv[1] = kv[1] * v_vs[si];
     }
     k_out[idx] = kv[0] * k_scale;
     v_out[idx] = kv[1] * v_scale;
@@ -811,7 +857,7 @@ bool decode_valu_supported(int kv, int qd, int D) {
   if (kv == DT_F32) return qd == DT_F32 || qd == DT_F16 || qd == DT_BF16;
   if (kv == DT_BF16) return qd == DT_BF16;
   if (kv == DT_F16) return qd == DT_F16;
-  if (kv == DT_FP8) return qd == DT_BF16 || qd == DT_F16;
+  if (is8bit(kv)) return qd == DT_BF16 || qd == DT_F16;
   return false;
 }
 
@@ -820,66 +866,79 @@ bool decode_mfma_supported(int kv, int qd, int D, int rows) {
   if (rows > 64) return false;
   if (kv == DT_BF16) return qd == DT_BF16;
   if (kv == DT_F16) return qd == DT_F16;
-  if (kv == DT_FP8) return qd == DT_BF16 || qd == DT_F16;
+  if (is8bit(kv)) return qd == DT_BF16 || qd == DT_F16;
   return false;
 }
 
-template <int KV, int QD, int D>
+template <int KV, int QD, int D, bool VS>
 static hipError_t valu_rb(const DecodeArgs &a, hipStream_t s) {
   dim3 grid(a.Hkv * a.row_blocks, a.P, a.B);   // KV heads of one page run side by side
   const int rb = (a.rows + a.row_blocks - 1) / a.row_blocks;
-  if (rb <= 4) hipLaunchKernelGGL((decode_valu<KV, QD, D, 4>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((decode_valu<KV, QD, D, 8>), grid, dim3(256), 0, s, a);
+  if (rb <= 4) hipLaunchKernelGGL((decode_valu<KV, QD, D, 4, VS>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((decode_valu<KV, QD, D, 8, VS>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <int KV, int QD>
+template <int KV, int QD, bool VS>
 static hipError_t valu_d(const DecodeArgs &a, hipStream_t s) {
-  if (a.D == 64) return valu_rb<KV, QD, 64>(a, s);
+  if (a.D == 64) return valu_rb<KV, QD, 64, VS>(a, s);
   if constexpr (KV != DT_F32) {
-    if (a.D == 256) return valu_rb<KV, QD, 256>(a, s);
+    if (a.D == 256) return valu_rb<KV, QD, 256, VS>(a, s);
   }
-  return valu_rb<KV, QD, 128>(a, s);
+  return valu_rb<KV, QD, 128, VS>(a, s);
+}
+
+// 8-bit K/V: element format, Q type and per-vector scales
+template <int KV>
+static hipError_t valu_8(const DecodeArgs &a, hipStream_t s) {
+  const bool vs = a.k_vs != nullptr;
+  if (a.q_dtype == DT_BF16) return vs ? valu_d<KV, DT_BF16, true>(a, s) : valu_d<KV, DT_BF16, false>(a, s);
+  return vs ? valu_d<KV, DT_F16, true>(a, s) : valu_d<KV, DT_F16, false>(a, s);
 }
 
 hipError_t launch_decode_valu(const DecodeArgs &a, hipStream_t s) {
   switch (a.kv_dtype) {
     case DT_F32:
-      if (a.q_dtype == DT_F32) return valu_d<DT_F32, DT_F32>(a, s);
-      if (a.q_dtype == DT_BF16) return valu_d<DT_F32, DT_BF16>(a, s);
-      return valu_d<DT_F32, DT_F16>(a, s);
-    case DT_BF16: return valu_d<DT_BF16, DT_BF16>(a, s);
-    case DT_F16: return valu_d<DT_F16, DT_F16>(a, s);
-    default:
-      if (a.q_dtype == DT_BF16) return valu_d<DT_FP8, DT_BF16>(a, s);
-      return valu_d<DT_FP8, DT_F16>(a, s);
+      if (a.q_dtype == DT_F32) return valu_d<DT_F32, DT_F32, false>(a, s);
+      if (a.q_dtype == DT_BF16) return valu_d<DT_F32, DT_BF16, false>(a, s);
+      return valu_d<DT_F32, DT_F16, false>(a, s);
+    case DT_BF16: return valu_d<DT_BF16, DT_BF16, false>(a, s);
+    case DT_F16: return valu_d<DT_F16, DT_F16, false>(a, s);
+    case DT_FP8: return valu_8<DT_FP8>(a, s);
+    default: return valu_8<DT_BF8>(a, s);
   }
 }
 
-template <int KV, int QD, int D>
+template <int KV, int QD, int D, bool VS>
 static hipError_t mfma_nb(const DecodeArgs &a, hipStream_t s) {
   dim3 grid(a.Hkv, a.P, a.B);
   const int nb = (a.rows + 15) / 16;
   switch (nb) {
-    case 1: hipLaunchKernelGGL((decode_mfma<KV, QD, D, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_mfma<KV, QD, D, 2>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((decode_mfma<KV, QD, D, 4>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((decode_mfma<KV, QD, D, 1, VS>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_mfma<KV, QD, D, 2, VS>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((decode_mfma<KV, QD, D, 4, VS>), grid, dim3(256), 0, s, a); break;
   }
   return hipGetLastError();
 }
 
-template <int KV, int QD>
+template <int KV, int QD, bool VS>
 static hipError_t mfma_d(const DecodeArgs &a, hipStream_t s) {
-  return a.D == 64 ? mfma_nb<KV, QD, 64>(a, s) : mfma_nb<KV, QD, 128>(a, s);
+  return a.D == 64 ? mfma_nb<KV, QD, 64, VS>(a, s) : mfma_nb<KV, QD, 128, VS>(a, s);
+}
+
+template <int KV>
+static hipError_t mfma_8(const DecodeArgs &a, hipStream_t s) {
+  const bool vs = a.k_vs != nullptr;
+  if (a.q_dtype == DT_BF16) return vs ? mfma_d<KV, DT_BF16, true>(a, s) : mfma_d<KV, DT_BF16, false>(a, s);
+  return vs ? mfma_d<KV, DT_F16, true>(a, s) : mfma_d<KV, DT_F16, false>(a, s);
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s) {
   switch (a.kv_dtype) {
-    case DT_BF16: return mfma_d<DT_BF16, DT_BF16>(a, s);
-    case DT_F16: return mfma_d<DT_F16, DT_F16>(a, s);
-    default:
-      if (a.q_dtype == DT_BF16) return mfma_d<DT_FP8, DT_BF16>(a, s);
-      return mfma_d<DT_FP8, DT_F16>(a, s);
+    case DT_BF16: return mfma_d<DT_BF16, DT_BF16, false>(a, s);
+    case DT_F16: return mfma_d<DT_F16, DT_F16, false>(a, s);
+    case DT_FP8: return mfma_8<DT_FP8>(a, s);
+    default: return mfma_8<DT_BF8>(a, s);
   }
 }
 
@@ -892,47 +951,53 @@ static int occupancy_of(K kernel) {
   return n > 0 ? n : 1;
 }
 
-template <int KV, int QD, int D>
+template <int KV, int QD, int D, bool VS>
 static int valu_occ(int rows) {
   static int cache[2] = {0, 0};
   const int k = rows <= 4 ? 0 : 1;
   if (!cache[k])
-    cache[k] = k == 0 ? occupancy_of(decode_valu<KV, QD, D, 4>) : occupancy_of(decode_valu<KV, QD, D, 8>);
+    cache[k] = k == 0 ? occupancy_of(decode_valu<KV, QD, D, 4, VS>)
+                      : occupancy_of(decode_valu<KV, QD, D, 8, VS>);
   return cache[k];
 }
 
-template <int KV, int QD, int D>
+template <int KV, int QD, int D, bool VS>
 static int mfma_occ(int rows) {
   static int cache[3] = {0, 0, 0};
   const int nb = (rows + 15) / 16;
   const int k = nb <= 1 ? 0 : nb == 2 ? 1 : 2;
   if (!cache[k])
-    cache[k] = k == 0 ? occupancy_of(decode_mfma<KV, QD, D, 1>)
-             : k == 1 ? occupancy_of(decode_mfma<KV, QD, D, 2>)
-                      : occupancy_of(decode_mfma<KV, QD, D, 4>);
+    cache[k] = k == 0 ? occupancy_of(decode_mfma<KV, QD, D, 1, VS>)
+             : k == 1 ? occupancy_of(decode_mfma<KV, QD, D, 2, VS>)
+                      : occupancy_of(decode_mfma<KV, QD, D, 4, VS>);
   return cache[k];
 }
 
-template <int KV, int QD>
+template <int KV, int QD, bool VS>
 static int occ_d(bool mfma, int D, int rows) {
   if constexpr (KV != DT_F32) {
-    if (mfma) return D == 64 ? mfma_occ<KV, QD, 64>(rows) : mfma_occ<KV, QD, 128>(rows);
-    if (D == 256) return valu_occ<KV, QD, 256>(rows);
+    if (mfma) return D == 64 ? mfma_occ<KV, QD, 64, VS>(rows) : mfma_occ<KV, QD, 128, VS>(rows);
+    if (D == 256) return valu_occ<KV, QD, 256, VS>(rows);
   }
-  return D == 64 ? valu_occ<KV, QD, 64>(rows) : valu_occ<KV, QD, 128>(rows);
+  return D == 64 ? valu_occ<KV, QD, 64, VS>(rows) : valu_occ<KV, QD, 128, VS>(rows);
 }
 
-int decode_blocks_per_cu(bool mfma, int kv, int qd, int D, int rows) {
+template <int KV>
+static int occ_8(bool mfma, int qd, int D, int rows, bool vs) {
+  if (qd == DT_BF16) return vs ? occ_d<KV, DT_BF16, true>(mfma, D, rows) : occ_d<KV, DT_BF16, false>(mfma, D, rows);
+  return vs ? occ_d<KV, DT_F16, true>(mfma, D, rows) : occ_d<KV, DT_F16, false>(mfma, D, rows);
+}
+
+int decode_blocks_per_cu(bool mfma, int kv, int qd, int D, int rows, bool vs) {
   switch (kv) {
     case DT_F32:
-      if (qd == DT_F32) return occ_d<DT_F32, DT_F32>(false, D, rows);
-      if (qd == DT_BF16) return occ_d<DT_F32, DT_BF16>(false, D, rows);
-      return occ_d<DT_F32, DT_F16>(false, D, rows);
-    case DT_BF16: return occ_d<DT_BF16, DT_BF16>(mfma, D, rows);
-    case DT_F16: return occ_d<DT_F16, DT_F16>(mfma, D, rows);
-    default:
-      if (qd == DT_BF16) return occ_d<DT_FP8, DT_BF16>(mfma, D, rows);
-      return occ_d<DT_FP8, DT_F16>(mfma, D, rows);
+      if (qd == DT_F32) return occ_d<DT_F32, DT_F32, false>(false, D, rows);
+      if (qd == DT_BF16) return occ_d<DT_F32, DT_BF16, false>(false, D, rows);
+      return occ_d<DT_F32, DT_F16, false>(false, D, rows);
+    case DT_BF16: return occ_d<DT_BF16, DT_BF16, false>(mfma, D, rows);
+    case DT_F16: return occ_d<DT_F16, DT_F16, false>(mfma, D, rows);
+    case DT_FP8: return occ_8<DT_FP8>(mfma, qd, D, rows, vs);
+    default: return occ_8<DT_BF8>(mfma, qd, D, rows, vs);
   }
 }
 
@@ -946,19 +1011,24 @@ hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t s) {
 
 hipError_t launch_debug_gather(const void *k, const void *v, int64_t k_sp, int64_t k_sh,
                                int64_t v_sp, int64_t v_sh, int kv_dtype, int Hkv, int D,
-                               float k_scale, float v_scale, const int32_t *pt_row, int seq_len,
-                               float *k_out, float *v_out, hipStream_t s) {
+                               float k_scale, float v_scale, const float *k_vs,
+                               const float *v_vs, int64_t vs_sp, int64_t vs_sh,
+                               const int32_t *pt_row, int seq_len, float *k_out, float *v_out,
+                               hipStream_t s) {
   const int64_t total = (int64_t)Hkv * seq_len * D;
   if (total == 0) return hipSuccess;
   const int blocks = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
-#define PA_GATHER(DT)                                                                     \
-  hipLaunchKernelGGL((debug_gather<DT>), dim3(blocks), dim3(256), 0, s, k, v, k_sp, k_sh, \
-                     v_sp, v_sh, Hkv, D, k_scale, v_scale, pt_row, seq_len, k_out, v_out)
+#define PA_GATHER(DT, VS)                                                                     \
+  hipLaunchKernelGGL((debug_gather<DT, VS>), dim3(blocks), dim3(256), 0, s, k, v, k_sp, k_sh, \
+                     v_sp, v_sh, Hkv, D, k_scale, v_scale, k_vs, v_vs, vs_sp, vs_sh, pt_row,  \
+                     seq_len, k_out, v_out)
+  const bool vs = k_vs != nullptr;
   switch (kv_dtype) {
-    case DT_F32: PA_GATHER(DT_F32); break;
-    case DT_F16: PA_GATHER(DT_F16); break;
-    case DT_BF16: PA_GATHER(DT_BF16); break;
-    default: PA_GATHER(DT_FP8); break;
+    case DT_F32: PA_GATHER(DT_F32, false); break;
+    case DT_F16: PA_GATHER(DT_F16, false); break;
+    case DT_BF16: PA_GATHER(DT_BF16, false); break;
+    case DT_FP8: if (vs) PA_GATHER(DT_FP8, true); else PA_GATHER(DT_FP8, false); break;
+    default: if (vs) PA_GATHER(DT_BF8, true); else PA_GATHER(DT_BF8, false); break;
   }
 #undef PA_GATHER
   return hipGetLastError();

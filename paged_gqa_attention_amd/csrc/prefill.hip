@@ -18,6 +18,12 @@
 // paragraph of the Geramy/LSE README).  Sinks are added to the softmax
 // denominator at the end (TokenSpeed-Kernel-AMD page, "Attention").
 //
+// 8-bit K/V (e4m3fn, e5m2) is decoded to the 16-bit operand type while it is
+// staged; with per-vector scales (template flag VS) each value is multiplied
+// by its vector's FP32 scale on the way (Geramy/LSE README, architecture
+// paragraph: FP8/BF8 operand loads staged through shared memory with decoding
+// and per-vector scales), so the tile loop is the same for every format.
+//
 // Workgroup order: (sequence, KV head) groups are dealt to the 8 XCDs; an
 // XCD runs a group's query tiles back to back, heaviest first, with the G/HPW
 // workgroups of one query tile adjacent, so resident workgroups share K/V
@@ -51,12 +57,17 @@ __device__ __forceinline__ int kperm(int k) {
 
 template <int KVDT, int QDT>
 struct Cfg {
-  static constexpr bool f16 = (KVDT == DT_F16) || (KVDT == DT_FP8 && QDT == DT_F16);
+  static constexpr bool f16 = (KVDT == DT_F16) || (is8bit(KVDT) && QDT == DT_F16);
 };
+
+template <bool F16>
+__device__ __forceinline__ uint32_t pack16(float a, float b) {
+  return F16 ? pack_f16x2(a, b) : pack_bf16x2(a, b);
+}
 
 }  // namespace
 
-template <int KVDT, int QDT, int D, int HPW, bool MASK>
+template <int KVDT, int QDT, int D, int HPW, bool MASK, bool VS>
 __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
   constexpr int ELT = DtInfo<KVDT>::bytes;
   constexpr bool F16 = Cfg<KVDT, QDT>::f16;
@@ -77,6 +88,7 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KBUF];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][VBUF];
   __shared__ int tile_list[MASK ? LIST : 1];
+  __shared__ __attribute__((aligned(16))) float vs_lds[VS ? kTileK : 4];   // V scales of a tile
   __shared__ int list_count[MASK ? NW : 1];
 
   // ---- task of this workgroup ----
@@ -157,10 +169,12 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
   uint32_t k_goff[KPT], v_goff[KPT];        // byte offset inside the page tile
   uint32_t k_loff[KPT], v_loff[KPT];        // element offset inside an LDS buffer
   int v_tok0[KPT];                          // first token of the V chunk in its tile
+  int k_slot[KPT];                          // slot of the K chunk's token in its page
 #pragma unroll
   for (int c = 0; c < KPT; ++c) {
     const int ch = tid + c * NT;
     const int key = ch / CPK, part = ch % CPK;
+    k_slot[c] = key & 15;
     k_pg[c] = __builtin_amdgcn_readfirstlane(key >> 4);
     k_goff[c] = (uint32_t)(((key & 15) * D + part * EPC) * ELT);
     k_loff[c] = (uint32_t)(((key & ~31) | kperm(key & 31)) * KSTR + part * EPC);
@@ -172,7 +186,13 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
     v_tok0[c] = 16 * vpg + tg * EPC;
   }
 
+  static_assert(!VS || EPC == 16, "per-vector scales: a V chunk is one page row");
+  static_assert(!VS || NT >= kTileK, "per-vector scales: one thread per key of a tile");
   u32x4 kreg[KPT], vreg[KPT];
+  float ksr[KPT];           // per-vector scale of the K chunk's token
+  float vsr = 0.f;          // V scale of key `tid` of the tile (threads < 64)
+  const float *ks_head = VS ? a.k_vs + (int64_t)kvh * a.vs_sh : nullptr;
+  const float *vs_head = VS ? a.v_vs + (int64_t)kvh * a.vs_sh : nullptr;
   auto gload = [&](int t) {
     t = __builtin_amdgcn_readfirstlane(t);
     int pid[4];
@@ -189,13 +209,27 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
         const char *vpage = vbase + (int64_t)__builtin_amdgcn_readfirstlane(pv) * v_page_bytes;
         kreg[c] = ld16(kpage + k_goff[c]);
         vreg[c] = ld16(vpage + v_goff[c]);
+        if constexpr (VS)
+          ksr[c] = ks_head[(int64_t)__builtin_amdgcn_readfirstlane(pk) * a.vs_sp + k_slot[c]];
       }
+    }
+    if constexpr (VS) {
+      // the tile's 64 V scales, one per thread of the first wave (uniform page)
+      const int k = tid >> 4;
+      const int ps = k == 0 ? pid[0] : k == 1 ? pid[1] : k == 2 ? pid[2] : pid[3];
+      if (tid < kTileK) vsr = vs_head[(int64_t)ps * a.vs_sp + (tid & 15)];
     }
   };
   auto lstore = [&](int t, int buf) {
     const int kbase_tok = t * kTileK;
     // V slots at or past the end may hold anything: zero them (last tile only)
     const bool tail = kbase_tok + kTileK > L;
+    if constexpr (VS) {
+      // V scales -> LDS.  The previous tile's readers are past the loop's
+      // barrier; this barrier makes the new scales visible to every wave.
+      if (tid < kTileK) vs_lds[tid] = vsr;
+      __syncthreads();
+    }
 #pragma unroll
     for (int c = 0; c < KPT; ++c) {
       const int ch = tid + c * NT;
@@ -204,21 +238,42 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
         uint16_t *vdst = &v_lds[buf][v_loff[c]];
         constexpr int NQ = EPC / 8;   // 16-byte LDS words per V chunk
         u32x4 vv[NQ];
-        if constexpr (KVDT == DT_FP8) {
+        if constexpr (is8bit(KVDT) && VS) {
+          // codes -> FP32, times the vector's scale, rounded once to the operand type
+          u32x4 kw[2];
+          const float ks = ksr[c];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const f32x2 x0 = e8x2_to_f32<KVDT, false>(kreg[c][w]);
+            const f32x2 x1 = e8x2_to_f32<KVDT, true>(kreg[c][w]);
+            kw[w >> 1][2 * (w & 1)] = pack16<F16>(x0[0] * ks, x0[1] * ks);
+            kw[w >> 1][2 * (w & 1) + 1] = pack16<F16>(x1[0] * ks, x1[1] * ks);
+          }
+          *reinterpret_cast<u32x4 *>(kdst) = kw[0];
+          *reinterpret_cast<u32x4 *>(kdst + 8) = kw[1];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {   // word w: tokens 4w .. 4w+3 of the page row
+            const f32x2 x0 = e8x2_to_f32<KVDT, false>(vreg[c][w]);
+            const f32x2 x1 = e8x2_to_f32<KVDT, true>(vreg[c][w]);
+            const f32x4 sv = *reinterpret_cast<const f32x4 *>(&vs_lds[v_tok0[c] + 4 * w]);
+            vv[w >> 1][2 * (w & 1)] = pack16<F16>(x0[0] * sv[0], x0[1] * sv[1]);
+            vv[w >> 1][2 * (w & 1) + 1] = pack16<F16>(x1[0] * sv[2], x1[1] * sv[3]);
+          }
+        } else if constexpr (is8bit(KVDT)) {
           u32x4 lo, hi;
 #pragma unroll
           for (int w = 0; w < 2; ++w) {
-            lo[2 * w] = fp8x2_to_16<F16, false>(kreg[c][w]);
-            lo[2 * w + 1] = fp8x2_to_16<F16, true>(kreg[c][w]);
-            hi[2 * w] = fp8x2_to_16<F16, false>(kreg[c][w + 2]);
-            hi[2 * w + 1] = fp8x2_to_16<F16, true>(kreg[c][w + 2]);
+            lo[2 * w] = e8x2_to_16<KVDT, F16, false>(kreg[c][w]);
+            lo[2 * w + 1] = e8x2_to_16<KVDT, F16, true>(kreg[c][w]);
+            hi[2 * w] = e8x2_to_16<KVDT, F16, false>(kreg[c][w + 2]);
+            hi[2 * w + 1] = e8x2_to_16<KVDT, F16, true>(kreg[c][w + 2]);
           }
           *reinterpret_cast<u32x4 *>(kdst) = lo;
           *reinterpret_cast<u32x4 *>(kdst + 8) = hi;
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            vv[w >> 1][2 * (w & 1)] = fp8x2_to_16<F16, false>(vreg[c][w]);
-            vv[w >> 1][2 * (w & 1) + 1] = fp8x2_to_16<F16, true>(vreg[c][w]);
+            vv[w >> 1][2 * (w & 1)] = e8x2_to_16<KVDT, F16, false>(vreg[c][w]);
+            vv[w >> 1][2 * (w & 1) + 1] = e8x2_to_16<KVDT, F16, true>(vreg[c][w]);
           }
         } else {
           *reinterpret_cast<u32x4 *>(kdst) = kreg[c];
@@ -446,36 +501,42 @@ bool prefill_supported(int kv, int qd, int D) {
   if (D != 64 && D != 128) return false;
   if (kv == DT_BF16) return qd == DT_BF16;
   if (kv == DT_F16) return qd == DT_F16;
-  if (kv == DT_FP8) return qd == DT_BF16 || qd == DT_F16;
+  if (is8bit(kv)) return qd == DT_BF16 || qd == DT_F16;
   return false;
 }
 
-template <int KV, int QD, int D, int HPW>
+template <int KV, int QD, int D, int HPW, bool VS>
 static hipError_t prefill_m(const PrefillArgs &a, hipStream_t s) {
   if (a.mask)
-    hipLaunchKernelGGL((prefill_mfma<KV, QD, D, HPW, true>), dim3(a.num_wg), dim3(HPW * 256), 0, s, a);
+    hipLaunchKernelGGL((prefill_mfma<KV, QD, D, HPW, true, VS>), dim3(a.num_wg), dim3(HPW * 256), 0, s, a);
   else
-    hipLaunchKernelGGL((prefill_mfma<KV, QD, D, HPW, false>), dim3(a.num_wg), dim3(HPW * 256), 0, s, a);
+    hipLaunchKernelGGL((prefill_mfma<KV, QD, D, HPW, false, VS>), dim3(a.num_wg), dim3(HPW * 256), 0, s, a);
   return hipGetLastError();
 }
 
-template <int KV, int QD, int D>
+template <int KV, int QD, int D, bool VS>
 static hipError_t prefill_h(const PrefillArgs &a, hipStream_t s) {
-  return a.heads_per_wg == 2 ? prefill_m<KV, QD, D, 2>(a, s) : prefill_m<KV, QD, D, 1>(a, s);
+  return a.heads_per_wg == 2 ? prefill_m<KV, QD, D, 2, VS>(a, s) : prefill_m<KV, QD, D, 1, VS>(a, s);
 }
 
-template <int KV, int QD>
+template <int KV, int QD, bool VS>
 static hipError_t prefill_d(const PrefillArgs &a, hipStream_t s) {
-  return a.D == 64 ? prefill_h<KV, QD, 64>(a, s) : prefill_h<KV, QD, 128>(a, s);
+  return a.D == 64 ? prefill_h<KV, QD, 64, VS>(a, s) : prefill_h<KV, QD, 128, VS>(a, s);
+}
+
+template <int KV>
+static hipError_t prefill_8(const PrefillArgs &a, hipStream_t s) {
+  const bool vs = a.k_vs != nullptr;
+  if (a.q_dtype == DT_BF16) return vs ? prefill_d<KV, DT_BF16, true>(a, s) : prefill_d<KV, DT_BF16, false>(a, s);
+  return vs ? prefill_d<KV, DT_F16, true>(a, s) : prefill_d<KV, DT_F16, false>(a, s);
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {
   switch (a.kv_dtype) {
-    case DT_BF16: return prefill_d<DT_BF16, DT_BF16>(a, s);
-    case DT_F16: return prefill_d<DT_F16, DT_F16>(a, s);
-    default:
-      if (a.q_dtype == DT_BF16) return prefill_d<DT_FP8, DT_BF16>(a, s);
-      return prefill_d<DT_FP8, DT_F16>(a, s);
+    case DT_BF16: return prefill_d<DT_BF16, DT_BF16, false>(a, s);
+    case DT_F16: return prefill_d<DT_F16, DT_F16, false>(a, s);
+    case DT_FP8: return prefill_8<DT_FP8>(a, s);
+    default: return prefill_8<DT_BF8>(a, s);
   }
 }
 

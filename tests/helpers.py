@@ -13,8 +13,10 @@ import paged_gqa_attention_amd as pa
 import synth
 
 # acceptance bars (max abs error against the oracle)
-TOL = {synth.DT_F32: 1e-4, synth.DT_F16: 2e-2, synth.DT_BF16: 2e-2, synth.DT_FP8: 5e-2}
-LSE_TOL = {synth.DT_F32: 1e-4, synth.DT_F16: 4e-3, synth.DT_BF16: 4e-3, synth.DT_FP8: 4e-3}
+TOL = {synth.DT_F32: 1e-4, synth.DT_F16: 2e-2, synth.DT_BF16: 2e-2, synth.DT_FP8: 5e-2,
+       synth.DT_BF8: 5e-2}
+LSE_TOL = {synth.DT_F32: 1e-4, synth.DT_F16: 4e-3, synth.DT_BF16: 4e-3, synth.DT_FP8: 4e-3,
+           synth.DT_BF8: 4e-3}
 
 _ctx = None
 
@@ -39,6 +41,8 @@ class Dev:
         self.sinks = p.sinks.to(dev) if p.sinks is not None else None
         self.mask = p.mask.to(dev) if p.mask is not None else None
         self.rows = p.rows_per_seq.to(dev) if p.rows_per_seq is not None else None
+        self.k_vs = p.k_vs.to(dev) if p.k_vs is not None else None
+        self.v_vs = p.v_vs.to(dev) if p.v_vs is not None else None
         self.o_dtype = synth.TORCH_DTYPE[p.o_dtype]
 
 
@@ -51,11 +55,13 @@ def run(d: Dev, lse: bool = True, num_splits: int = 0, out_dtype=None):
     if p.kind == "decode":
         pa.paged_decode(ctx(), d.q, d.k, d.v, d.pt, d.lens, k_scale=p.k_scale, v_scale=p.v_scale,
                         softmax_scale=p.softmax_scale, sinks=d.sinks, out=o, lse=lse_t,
-                        num_splits=num_splits, rows_per_seq=d.rows)
+                        num_splits=num_splits, rows_per_seq=d.rows, k_vscales=d.k_vs,
+                        v_vscales=d.v_vs)
     else:
         pa.prefill(ctx(), d.q, d.k, d.v, d.pt, d.lens, k_scale=p.k_scale, v_scale=p.v_scale,
                    softmax_scale=p.softmax_scale, sinks=d.sinks, out=o, lse=lse_t,
-                   block_mask=d.mask, mask_block=p.mask_block, rows_per_seq=d.rows)
+                   block_mask=d.mask, mask_block=p.mask_block, rows_per_seq=d.rows,
+                   k_vscales=d.k_vs, v_vscales=d.v_vs)
     torch.cuda.synchronize()
     return (o.to(torch.float64).cpu().numpy(),
             lse_t.to(torch.float64).cpu().numpy() if lse else None)

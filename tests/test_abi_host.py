@@ -34,7 +34,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.attn_abi_version() == 2
+    assert lib.attn_abi_version() == 3
 
 
 def test_open_without_a_gpu_is_a_device_error(lib):
@@ -87,7 +87,8 @@ def _decode_args(B=2, R=1, Hq=8, Hkv=2, d=128, stride=64, dtype=torch.bfloat16, 
     v = FakeTensor((pages, Hkv, d, 16), dtype, 0x200000)
     pt = FakeTensor((B, stride), torch.int32, 0x300000)
     lens = FakeTensor((B,), torch.int32, 0x400000)
-    q = FakeTensor((B, R, Hq, d), torch.bfloat16 if dtype == torch.float8_e4m3fn else dtype, 0x500000)
+    eight = dtype in (torch.float8_e4m3fn, torch.float8_e5m2)
+    q = FakeTensor((B, R, Hq, d), torch.bfloat16 if eight else dtype, 0x500000)
     o = FakeTensor((B, R, Hq, d), q.dtype, 0x600000)
     return pa.make_io(q, o), pa.make_kv(k, v, pt, lens), pa.make_opts()
 
@@ -246,3 +247,59 @@ def test_head_dim_256_support(hctx):
     # head_dim 96 is not built anywhere
     io, kv, op = _decode_args(d=96)
     assert _status(lambda: pa.attn_paged_decode_plan(hctx, io, kv, op)) == pa.ATTN_ERR_UNSUPPORTED
+
+
+def _scales(pages=100, Hkv=2, ptr=0xA00000, strides=None):
+    return FakeTensor((pages, Hkv, 16), torch.float32, ptr, strides)
+
+
+@pytest.mark.parametrize("dtype", [torch.float8_e4m3fn, torch.float8_e5m2])
+def test_per_vector_scales_validate(hctx, dtype):
+    io, _, op = _decode_args(dtype=dtype)
+    k = FakeTensor((100, 2, 16, 128), dtype, 0x100000)
+    v = FakeTensor((100, 2, 128, 16), dtype, 0x200000)
+    pt = FakeTensor((2, 64), torch.int32, 0x300000)
+    lens = FakeTensor((2,), torch.int32, 0x400000)
+    ks, vs = _scales(ptr=0xA00000), _scales(ptr=0xB00000)
+    kv = pa.make_kv(k, v, pt, lens, k_vscales=ks, v_vscales=vs)
+    assert (kv.vscale_stride_page, kv.vscale_stride_head) == (32, 16)
+    P, T, W = pa.attn_paged_decode_plan(hctx, io, kv, op)
+    assert P >= 1 and W > 0
+    plan = lambda kv: _status(lambda: pa.attn_paged_decode_plan(hctx, io, kv, op))
+    kv.v_vscales = None                                           # both or neither
+    assert plan(kv) == pa.ATTN_ERR_INVALID_ARGUMENT
+    kv = pa.make_kv(k, v, pt, lens, k_vscales=ks, v_vscales=vs)
+    kv.k_vscales = 0xA00004                                       # misaligned
+    assert plan(kv) == pa.ATTN_ERR_INVALID_ARGUMENT
+    kv = pa.make_kv(k, v, pt, lens, k_vscales=ks, v_vscales=vs)
+    kv.vscale_stride_head = 8                                     # tiles overlap
+    assert plan(kv) == pa.ATTN_ERR_INVALID_ARGUMENT
+    kv = pa.make_kv(k, v, pt, lens, k_vscales=ks, v_vscales=vs)
+    kv.vscale_stride_page = 34                                    # not 16-byte aligned tiles
+    assert plan(kv) == pa.ATTN_ERR_INVALID_ARGUMENT
+    # per-vector scales belong to 8-bit storage only
+    kb = FakeTensor((100, 2, 16, 128), torch.bfloat16, 0x100000)
+    vb = FakeTensor((100, 2, 128, 16), torch.bfloat16, 0x200000)
+    kv = pa.make_kv(kb, vb, pt, lens, k_vscales=ks, v_vscales=vs)
+    iob, _, _ = _decode_args()
+    assert _status(lambda: pa.attn_paged_decode_plan(hctx, iob, kv, op)) == pa.ATTN_ERR_INVALID_ARGUMENT
+    # prefill validates the same way and then enqueues nothing on a planning-only context
+    kv = pa.make_kv(k, v, pt, lens, k_vscales=ks, v_vscales=vs)
+    q = FakeTensor((1, 256, 8, 128), torch.bfloat16, 0x500000)
+    o = FakeTensor((1, 256, 8, 128), torch.bfloat16, 0x600000)
+    assert _status(lambda: pa.attn_prefill(hctx, pa.make_io(q, o), kv, pa.make_opts(), stream=0)) == \
+        pa.ATTN_ERR_DEVICE
+
+
+def test_per_vector_append_needs_unit_tensor_scales(hctx):
+    k = FakeTensor((100, 2, 16, 64), torch.float8_e5m2, 0x100000)
+    v = FakeTensor((100, 2, 64, 16), torch.float8_e5m2, 0x200000)
+    pt = FakeTensor((2, 8), torch.int32, 0x300000)
+    lens = FakeTensor((2,), torch.int32, 0x400000)
+    kv = pa.make_kv(k, v, pt, lens, k_vscales=_scales(), v_vscales=_scales(ptr=0xB00000))
+    rows = pa.make_rows(FakeTensor((2, 3, 2, 64), torch.bfloat16, 0x700000),
+                        FakeTensor((2, 3, 2, 64), torch.bfloat16, 0x800000))
+    app = lambda: _status(lambda: pa.attn_kv_append(hctx, kv, rows, stream=0))
+    assert app() == pa.ATTN_ERR_DEVICE                            # valid: nothing enqueued
+    kv.v_scale = 2.0
+    assert app() == pa.ATTN_ERR_INVALID_ARGUMENT
