@@ -131,7 +131,7 @@ def test_decode_forced_splits_per_vector(splits):
 def test_decode_ragged_rows_per_vector(dt, R, rps):
     _say("decode ragged", dt, R, rps)
     B = len(rps)
-    p = synth.make_decode(173, B, 16, 4, 128, [900, 400, 1300][:B], R, kv_dtype=dt,
+    p = synth.make_decode(173, B, 16, 4, 128, [900, 400, 1300, 77][:B], R, kv_dtype=dt,
                           vscales=True, rows_per_seq=rps)
     o, l = run(Dev(p))
     check_full(p, o, l, label=f"ragged {dt} {rps}")
@@ -167,6 +167,27 @@ PREFILL_CASES = [
 ]
 
 
+def _prefill_lse_tol(p):
+    """LSE bound of the prefill MFMA path with per-vector scales.  Staging rounds
+    each dequantised K value (code x scale) once to the bf16 operand (relative
+    error <= 2^-9), so a score moves by at most scale * 2^-9 * sum_c |q_c k_c|;
+    the LSE moves by at most the largest such shift, plus 2^-9 for the row sum
+    of the bf16-rounded weights."""
+    if p.k_vs is None:
+        return None
+    worst = 0.0
+    G = p.num_q_heads // p.num_kv_heads
+    for b in range(p.batch):
+        kc, _ = synth.logical_kv_codes(p, b)
+        ks, _ = synth.logical_vscales(p, b)
+        kval = oracle.decode_codes(p.kv_dtype, kc.view(torch.uint8).numpy().reshape(-1))
+        kval = np.abs(kval.reshape(kc.shape) * ks.numpy()[..., None])          # [Hkv][L][d]
+        q = np.abs(p.q[b].double().numpy())                                    # [rows][Hq][d]
+        for h in range(p.num_q_heads):
+            worst = max(worst, float((q[:, h, :] @ kval[h // G].T).max()))
+    return 2.0 ** -9 + p.scale * 2.0 ** -9 * worst + 1e-3
+
+
 @pytest.mark.parametrize("name,kw", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
 def test_prefill_parity(name, kw):
     _say("prefill", name)
@@ -174,7 +195,7 @@ def test_prefill_parity(name, kw):
                            q_rows=kw.get("q_rows"), kv_dtype=kw["dt"], sinks=True,
                            softmax_scale=kw.get("scale", 0.0), vscales=kw.get("vs", False))
     o, l = run(Dev(p))
-    check_full(p, o, l, label=name)
+    check_full(p, o, l, lse_tol=_prefill_lse_tol(p), label=name)
 
 
 def test_prefill_per_vector_f16_queries():
@@ -184,7 +205,7 @@ def test_prefill_per_vector_f16_queries():
     p.q_dtype = DT_F16
     p.o_dtype = DT_F16
     o, l = run(Dev(p))
-    check_full(p, o, l, label="prefill f16 q")
+    check_full(p, o, l, lse_tol=_prefill_lse_tol(p), label="prefill f16 q")
 
 
 @pytest.mark.parametrize("dt", [DT_FP8, DT_BF8])
@@ -193,7 +214,7 @@ def test_blocksparse_per_vector(dt):
     p = synth.make_blocksparse(183, 1, 8, 2, 128, 1100, mask_block=128, keep_prob=0.3,
                                sinks=True, kv_dtype=dt, vscales=True)
     o, l = run(Dev(p))
-    check_full(p, o, l, label=f"blocksparse {dt}")
+    check_full(p, o, l, lse_tol=_prefill_lse_tol(p), label=f"blocksparse {dt}")
 
 
 # ------------------------------------------------------------------ append
