@@ -228,6 +228,10 @@ def append_bench(ctx, B, n_new, Hkv, d, kv_dtype, src_dtype, steps, warmup):
     return ms, nbytes
 
 
+def _dev(t, dev):
+    return None if t is None else t.to(dev)
+
+
 def decode_setup(ctx, p, dev="cuda", num_splits=0):
     import torch
     import paged_gqa_attention_amd as pa
@@ -235,7 +239,7 @@ def decode_setup(ctx, p, dev="cuda", num_splits=0):
     o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     io = pa.make_io(q, o)
     kv = pa.make_kv(p.k_pool.to(dev), p.v_pool.to(dev), p.page_table.to(dev),
-                    p.seq_lens.to(dev), p.k_scale, p.v_scale)
+                    p.seq_lens.to(dev), p.k_scale, p.v_scale, _dev(p.k_vs, dev), _dev(p.v_vs, dev))
     op = pa.make_opts(p.softmax_scale, None if p.sinks is None else p.sinks.to(dev),
                       None, 128, num_splits)
     P, T, W = pa.attn_paged_decode_plan(ctx, io, kv, op)
@@ -251,7 +255,7 @@ def prefill_setup(ctx, p, dev="cuda"):
     o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     io = pa.make_io(q, o)
     kv = pa.make_kv(p.k_pool.to(dev), p.v_pool.to(dev), p.page_table.to(dev),
-                    p.seq_lens.to(dev), p.k_scale, p.v_scale)
+                    p.seq_lens.to(dev), p.k_scale, p.v_scale, _dev(p.k_vs, dev), _dev(p.v_vs, dev))
     mask = None if p.mask is None else p.mask.to(dev)
     op = pa.make_opts(p.softmax_scale, None if p.sinks is None else p.sinks.to(dev), mask,
                       p.mask_block)
@@ -419,6 +423,7 @@ def main():
         "roofline": roof, "cpu_baseline": cpu, "prefill": prefill,
         "read_ceiling": read_ceiling(ctx),
         "kv_append": kv_append_summary(ctx, args),
+        "formats": formats_summary(ctx, args),
     }
     if args.all:
         extra(ctx, args)
@@ -442,6 +447,39 @@ def kv_append_summary(ctx, args):
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
             "fp8_pool_GBs": round(nb8 / (ms8 * 1e-3) / 1e9, 1),
             "decode_step_16x1_rows_d128_us": round(ms1 * 1e3, 2)}
+
+
+def formats_summary(ctx, args):
+    """The 8-bit cache formats on their own workloads: decode B=4 x 65,536 keys,
+    R=4 (MFMA verify path, HBM roofline) and prefill 16 x 8K (MFMA roofline),
+    with per-tensor e4m3fn, per-vector-scaled e4m3fn and per-vector-scaled e5m2."""
+    import torch
+    import synth
+    from paged_gqa_attention_amd import accounting as acc
+    out = {"decode_workload": "B=4, Hq=32, Hkv=8, d=128, 65,536 keys, R=4, bf16 Q/O",
+           "prefill_workload": "B=16, S=8192, Hq=64, Hkv=8, d=64, sinks, bf16 Q/O"}
+    flops = acc.attention_flops(acc.causal_pairs(8192, 8192), 64, 64, 16)
+    for name, dt, vs in (("fp8", synth.DT_FP8, False), ("fp8_vs", synth.DT_FP8, True),
+                         ("bf8_vs", synth.DT_BF8, True)):
+        p = synth.config3(device="cuda", kv_dtype=dt, vscales=vs)
+        call, (P, T), keep = decode_setup(ctx, p, "cuda")
+        ms = time_calls(call, args.steps, args.warmup)
+        b = acc.decode_bytes(p.seq_lens.tolist(), 4, 32, 8, 128, dt, 2, 2, per_vector_scales=vs)
+        gbs = b / (ms * 1e-3) / 1e9
+        del keep, call, p
+        torch.cuda.empty_cache()
+        pp = synth.config4(seq_len=8192, batch=16, device="cuda", kv_dtype=dt, vscales=vs)
+        pcall, pkeep = prefill_setup(ctx, pp, "cuda")
+        pms = time_calls(pcall, max(3, args.steps // 2), max(1, args.warmup // 2))
+        tfs = flops / (pms * 1e-3) / 1e12
+        del pkeep, pcall, pp
+        torch.cuda.empty_cache()
+        out[name] = {"decode_GBs": round(gbs, 1), "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "decode_ms": round(ms, 4), "decode_bytes": b, "splits": P,
+                     "prefill_TFLOPs": round(tfs, 1),
+                     "prefill_mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 4),
+                     "prefill_ms": round(pms, 3)}
+    return out
 
 
 def only_prefill(ctx, args):

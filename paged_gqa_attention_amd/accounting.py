@@ -6,7 +6,7 @@ measured times as a fraction of the MI355X roofline.
 """
 from __future__ import annotations
 
-ELT_BYTES = {0: 4, 1: 2, 2: 2, 3: 1}   # f32, f16, bf16, fp8-e4m3
+ELT_BYTES = {0: 4, 1: 2, 2: 2, 3: 1, 4: 1}   # f32, f16, bf16, fp8-e4m3, bf8-e5m2
 PAGE = 16
 
 
@@ -25,10 +25,12 @@ def kv_bytes_per_token(layers: int, kv_heads: int, head_dim: int, dtype: int,
 
 
 def decode_bytes(lens, q_rows, num_q_heads, num_kv_heads, head_dim, kv_dtype, q_dtype,
-                 o_dtype) -> int:
+                 o_dtype, per_vector_scales: bool = False) -> int:
     """Algorithmic HBM bytes of one paged decode call: every live K/V element
-    once, the query rows, the outputs and the used page-table entries."""
-    kv = sum(int(L) for L in lens) * num_kv_heads * head_dim * ELT_BYTES[kv_dtype] * 2
+    once (with its vector's FP32 scale where the cache has per-vector scales),
+    the query rows, the outputs and the used page-table entries."""
+    per_vec = head_dim * ELT_BYTES[kv_dtype] + (4 if per_vector_scales else 0)
+    kv = sum(int(L) for L in lens) * num_kv_heads * per_vec * 2
     B = len(lens)
     q = B * q_rows * num_q_heads * head_dim * ELT_BYTES[q_dtype]
     o = B * q_rows * num_q_heads * head_dim * ELT_BYTES[o_dtype]

@@ -373,16 +373,18 @@ def config2(seed=202, q_rows=1, lens=None, batch=16, device="cpu"):
                        stride=1024, device=device)
 
 
-def config3(seed=303, batch=4, ctx=65536, device="cpu"):
-    """FP8-e4m3 long decode: B=4, Hq=32, Hkv=8, d=128, 64K context, 4 rows."""
-    return make_decode(seed, batch, 32, 8, 128, [ctx] * batch, 4, kv_dtype=DT_FP8,
-                       q_dtype=DT_BF16, o_dtype=DT_BF16, stride=(ctx + 15) // 16, device=device)
+def config3(seed=303, batch=4, ctx=65536, device="cpu", kv_dtype=DT_FP8, vscales=False):
+    """FP8-e4m3 long decode: B=4, Hq=32, Hkv=8, d=128, 64K context, 4 rows (also
+    with e5m2 storage or per-vector scales)."""
+    return make_decode(seed, batch, 32, 8, 128, [ctx] * batch, 4, kv_dtype=kv_dtype,
+                       q_dtype=DT_BF16, o_dtype=DT_BF16, stride=(ctx + 15) // 16, device=device,
+                       vscales=vscales)
 
 
-def config4(seed=404, seq_len=8192, batch=16, device="cpu"):
-    """Causal prefill with sinks: Hq=64, Hkv=8, d=64, BF16, scale 1/8."""
+def config4(seed=404, seq_len=8192, batch=16, device="cpu", kv_dtype=DT_BF16, vscales=False):
+    """Causal prefill with sinks: Hq=64, Hkv=8, d=64, BF16 (or 8-bit) K/V, scale 1/8."""
     return make_prefill(seed, batch, 64, 8, 64, seq_len, sinks=True, softmax_scale=0.125,
-                        device=device)
+                        device=device, kv_dtype=kv_dtype, vscales=vscales)
 
 
 def config5(seed=505, seq_len=32768, device="cpu"):
