@@ -424,6 +424,7 @@ def main():
         "read_ceiling": read_ceiling(ctx),
         "kv_append": kv_append_summary(ctx, args),
         "formats": formats_summary(ctx, args),
+        "fragments": fragments_summary(ctx, args),
     }
     if args.all:
         extra(ctx, args)
@@ -479,6 +480,53 @@ def formats_summary(ctx, args):
                      "prefill_TFLOPs": round(tfs, 1),
                      "prefill_mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 4),
                      "prefill_ms": round(pms, 3)}
+    return out
+
+
+def fragments_summary(ctx, args, fragment_bytes=256 << 10, arena_bytes=256 << 20):
+    """The headline decode with the K and V pools in 256 KiB fragments placed at
+    shuffled slots of 256 MiB arenas and reached through fragment tables, against
+    the same call over the contiguous pools (same inputs, same plan)."""
+    import torch
+    import paged_gqa_attention_amd as pa
+    import synth
+    from paged_gqa_attention_amd import accounting as acc
+    p = synth.config2(q_rows=1, lens=[16384] * 16, device="cuda")
+    call, (P, T), (io, kv, op, ws) = decode_setup(ctx, p, "cuda")
+    ms0 = time_calls(call, args.steps, args.warmup)
+    page_bytes = p.k_pool[0].numel() * p.k_pool.element_size()
+    per = fragment_bytes // page_bytes                  # pages per fragment (8 at this shape)
+    log2 = per.bit_length() - 1
+    tables, views = [], []
+    g = torch.Generator().manual_seed(21)
+    for pool in (p.k_pool, p.v_pool):
+        n = pool.shape[0]
+        F = (n + per - 1) // per
+        per_arena = arena_bytes // fragment_bytes
+        arenas = -(-F // per_arena)
+        slots = torch.randperm(arenas * per_arena, generator=g)[:F]
+        arena = torch.empty((arenas * per_arena, per) + tuple(pool.shape[1:]), dtype=pool.dtype,
+                            device="cuda")
+        full = F * per
+        src = pool if full == n else torch.cat([pool, pool[: full - n]])
+        arena[slots.cuda()] = src.view((F, per) + tuple(pool.shape[1:]))
+        tables.append(torch.tensor([arena[int(s_)].data_ptr() for s_ in slots], dtype=torch.int64,
+                                   device="cuda"))
+        views.append(arena)
+    kvf = pa.make_kv(views[0][0], views[1][0], kv._keep[2], kv._keep[3], p.k_scale, p.v_scale,
+                     k_fragments=tables[0], v_fragments=tables[1], fragment_pages_log2=log2,
+                     num_pages=p.k_pool.shape[0])
+    callf = lambda: pa.attn_paged_decode(ctx, io, kvf, op, ws)
+    ms1 = time_calls(callf, args.steps, args.warmup)
+    nbytes = acc.decode_bytes(p.seq_lens.tolist(), 1, 32, 8, 128, synth.DT_BF16, synth.DT_BF16,
+                              synth.DT_BF16)
+    out = {"workload": "headline decode (16 x 16,384, bf16, R=1), K/V in 256 KiB fragments of "
+                       "256 MiB arenas, shuffled", "pages_per_fragment": per,
+           "contiguous_ms": round(ms0, 5), "fragmented_ms": round(ms1, 5),
+           "fragmented_GBs": round(nbytes / (ms1 * 1e-3) / 1e9, 1),
+           "overhead_pct": round(100.0 * (ms1 / ms0 - 1.0), 2)}
+    del views, tables, kvf, call, callf, p
+    torch.cuda.empty_cache()
     return out
 
 

@@ -54,6 +54,16 @@
  *   Q, O     [batch][q_rows][num_q_heads][head_dim] through the given strides,
  *            head_dim contiguous.
  *   lse      optional float [batch][num_q_heads][q_rows] (natural log).
+ *   fragments (optional): the K and/or V pool split into fragments of
+ *            2^fragment_pages_log2 pages (Geramy/LSE releases, v0.4.20 "K/V
+ *            memory management": K/V kept in 256 KiB fragments of shared
+ *            256 MiB arenas, grown without moving existing data).  With
+ *            k_fragments set, page p's tile (page, kv_head) is at
+ *            k_fragments[p >> fragment_pages_log2] + (p & (2^log2 - 1)) *
+ *            k_stride_page + head*k_stride_head (elements of the K dtype from
+ *            that device address); k_pages is then ignored.  Likewise
+ *            v_fragments for V.  Fragment addresses are device data (trusted),
+ *            16-byte aligned.  The per-vector scale pools stay unfragmented.
  *   per-vector scales (optional, 8-bit K/V): float scale of slot t of tile
  *            (page, kv_head) at k_vscales + page*vscale_stride_page +
  *            head*vscale_stride_head + t (likewise v_vscales), the 16 slots
@@ -100,7 +110,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 typedef enum {
   ATTN_OK = 0,
@@ -139,6 +149,10 @@ typedef struct {
   const float *k_vscales;       /* nullable: per-vector K scales (8-bit K/V), see layout */
   const float *v_vscales;       /* nullable: per-vector V scales; both or neither */
   int64_t vscale_stride_page, vscale_stride_head;   /* floats, multiples of 4 */
+  const uint64_t *k_fragments;  /* nullable: device array of K fragment addresses */
+  const uint64_t *v_fragments;  /* nullable: device array of V fragment addresses */
+  int32_t fragment_pages_log2;  /* pages per fragment = 2^this, 0..20 */
+  int32_t num_fragments;        /* entries in each fragment array (covers num_pages) */
 } attn_kv;
 
 /* Queries and outputs. */

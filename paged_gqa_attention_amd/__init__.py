@@ -28,7 +28,7 @@ ATTN_F32, ATTN_F16, ATTN_BF16, ATTN_FP8_E4M3, ATTN_BF8_E5M2 = 0, 1, 2, 3, 4
 _DT = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16,
        torch.float8_e4m3fn: ATTN_FP8_E4M3, torch.float8_e5m2: ATTN_BF8_E5M2}
 
-ABI_VERSION = 3   # include/paged_attn.h ATTN_ABI_VERSION
+ABI_VERSION = 4   # include/paged_attn.h ATTN_ABI_VERSION
 
 EXPORTED = [
     "attn_abi_version", "attn_open", "attn_open_host_only", "attn_close", "attn_free",
@@ -57,6 +57,8 @@ class attn_kv(ctypes.Structure):
         ("pad1", ctypes.c_int32), ("seq_lens", ctypes.c_void_p),
         ("k_vscales", ctypes.c_void_p), ("v_vscales", ctypes.c_void_p),
         ("vscale_stride_page", ctypes.c_int64), ("vscale_stride_head", ctypes.c_int64),
+        ("k_fragments", ctypes.c_void_p), ("v_fragments", ctypes.c_void_p),
+        ("fragment_pages_log2", ctypes.c_int32), ("num_fragments", ctypes.c_int32),
     ]
 
 
@@ -209,23 +211,47 @@ def _dtype(t: torch.Tensor) -> int:
 def make_kv(k_pages: torch.Tensor, v_pages: torch.Tensor, page_table: torch.Tensor,
             seq_lens: torch.Tensor, k_scale: float = 1.0, v_scale: float = 1.0,
             k_vscales: Optional[torch.Tensor] = None,
-            v_vscales: Optional[torch.Tensor] = None) -> attn_kv:
+            v_vscales: Optional[torch.Tensor] = None,
+            k_fragments: Optional[torch.Tensor] = None, v_fragments: Optional[torch.Tensor] = None,
+            fragment_pages_log2: int = 0, num_pages: Optional[int] = None) -> attn_kv:
     """K pool [num_pages][Hkv][16][d], V pool [num_pages][Hkv][d][16] (any strides on
     the first two dims, tiles contiguous), page_table int32 [B][stride], seq_lens int32 [B].
     Optional per-vector scale pools (8-bit K/V) k_vscales / v_vscales: float32
-    [num_pages][Hkv][16] with the 16 slots contiguous and equal strides."""
+    [num_pages][Hkv][16] with the 16 slots contiguous and equal strides.
+
+    Fragmented pools: k_fragments / v_fragments are int64 device tensors of
+    fragment addresses (``tensor.data_ptr()`` of each fragment), each fragment
+    holding 2^fragment_pages_log2 pages; k_pages / v_pages then describe one
+    fragment's layout (dtype and strides) and ``num_pages`` gives the pool size."""
     if k_pages.dim() != 4 or v_pages.dim() != 4:
         raise AttnError(ATTN_ERR_INVALID_ARGUMENT, "K/V pools must be 4-D")
     n, hkv, page, d = k_pages.shape
     kv = attn_kv()
     kv.k_pages, kv.v_pages = _ptr(k_pages), _ptr(v_pages)
+    if (k_fragments is None) != (v_fragments is None):
+        raise AttnError(ATTN_ERR_INVALID_ARGUMENT, "k_fragments and v_fragments go together here")
+    if k_fragments is not None:
+        if k_fragments.dtype != torch.int64 or v_fragments.dtype != torch.int64 or \
+           k_fragments.shape != v_fragments.shape or k_fragments.dim() != 1:
+            raise AttnError(ATTN_ERR_INVALID_ARGUMENT, "fragment tables must be int64 [num_fragments]")
+        if num_pages is None or n != 1 << fragment_pages_log2:
+            raise AttnError(ATTN_ERR_INVALID_ARGUMENT, "fragmented pools: k_pages describes one "
+                            "fragment of 2^fragment_pages_log2 pages; give num_pages")
+        kv.k_pages = kv.v_pages = None
+        kv.k_fragments, kv.v_fragments = _ptr(k_fragments), _ptr(v_fragments)
+        kv.fragment_pages_log2 = int(fragment_pages_log2)
+        kv.num_fragments = k_fragments.shape[0]
+        n = int(num_pages)
+    else:
+        kv.k_fragments = kv.v_fragments = None
+        kv.fragment_pages_log2 = kv.num_fragments = 0
     kv.dtype = _dtype(k_pages)
     kv.num_pages, kv.page_size, kv.num_kv_heads, kv.head_dim = n, page, hkv, d
     kv.k_stride_page, kv.k_stride_head = k_pages.stride(0), k_pages.stride(1)
     kv.v_stride_page, kv.v_stride_head = v_pages.stride(0), v_pages.stride(1)
     if (k_pages.stride(2), k_pages.stride(3)) != (d, 1) or \
        (v_pages.stride(2), v_pages.stride(3)) != (page, 1) or \
-       tuple(v_pages.shape) != (n, hkv, d, page) or v_pages.dtype != k_pages.dtype:
+       tuple(v_pages.shape) != (k_pages.shape[0], hkv, d, page) or v_pages.dtype != k_pages.dtype:
         raise AttnError(ATTN_ERR_INVALID_ARGUMENT, "K/V page tiles must be contiguous "
                         "[16][d] (K) and [d][16] (V) of one dtype")
     kv.k_scale, kv.v_scale = float(k_scale), float(v_scale)
@@ -251,7 +277,8 @@ def make_kv(k_pages: torch.Tensor, v_pages: torch.Tensor, page_table: torch.Tens
     else:
         kv.k_vscales = kv.v_vscales = None
         kv.vscale_stride_page = kv.vscale_stride_head = 0
-    kv._keep = (k_pages, v_pages, page_table, seq_lens, k_vscales, v_vscales)
+    kv._keep = (k_pages, v_pages, page_table, seq_lens, k_vscales, v_vscales, k_fragments,
+                v_fragments)
     return kv
 
 
@@ -265,6 +292,7 @@ def make_rows(k: torch.Tensor, v: torch.Tensor) -> attn_kv_rows:
     r.k, r.v, r.dtype = _ptr(k), _ptr(v), _dtype(k)
     r.batch, r.n_new = k.shape[0], k.shape[1]
     r.stride_b, r.stride_row, r.stride_head = k.stride(0), k.stride(1), k.stride(2)
+    r._keep = (k, v)     # the descriptor holds raw pointers: keep the tensors alive with it
     return r
 
 

@@ -60,7 +60,8 @@ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
 attn_status check_kv(const attn_kv *kv, char **err) {
   if (!kv) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "kv is NULL");
-  if (!kv->k_pages || !kv->v_pages) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "K/V pages are NULL");
+  if ((!kv->k_pages && !kv->k_fragments) || (!kv->v_pages && !kv->v_fragments))
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "K/V pages are NULL (and no fragment table is given)");
   if (!kv->page_table || !kv->seq_lens)
     return fail(err, ATTN_ERR_INVALID_ARGUMENT, "page_table / seq_lens is NULL");
   if (elt_bytes(kv->dtype) == 0) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "bad K/V dtype %d", kv->dtype);
@@ -73,6 +74,16 @@ attn_status check_kv(const attn_kv *kv, char **err) {
     return fail(err, ATTN_ERR_UNSUPPORTED, "head_dim %d (only 64, 128 or 256)", kv->head_dim);
   if (!aligned16(kv->k_pages) || !aligned16(kv->v_pages))
     return fail(err, ATTN_ERR_INVALID_ARGUMENT, "K/V pages must be 16-byte aligned");
+  if (kv->k_fragments || kv->v_fragments) {
+    if (kv->fragment_pages_log2 < 0 || kv->fragment_pages_log2 > 20)
+      return fail(err, ATTN_ERR_INVALID_ARGUMENT, "fragment_pages_log2 %d outside [0, 20]", kv->fragment_pages_log2);
+    if ((reinterpret_cast<uintptr_t>(kv->k_fragments) | reinterpret_cast<uintptr_t>(kv->v_fragments)) & 7u)
+      return fail(err, ATTN_ERR_INVALID_ARGUMENT, "fragment tables must be 8-byte aligned");
+    const int64_t need = ceil_div(kv->num_pages, int64_t(1) << kv->fragment_pages_log2);
+    if (kv->num_fragments < need)
+      return fail(err, ATTN_ERR_INVALID_ARGUMENT, "%d fragments do not cover %d pages of 2^%d per fragment",
+                  kv->num_fragments, kv->num_pages, kv->fragment_pages_log2);
+  }
   const int64_t tile = (int64_t)kPage * kv->head_dim;
   const int eb = elt_bytes(kv->dtype);
   const int64_t s[4] = {kv->k_stride_page, kv->k_stride_head, kv->v_stride_page, kv->v_stride_head};
@@ -282,6 +293,8 @@ attn_status prefill_common(attn_ctx *ctx, const attn_io *io, const attn_kv *kv, 
   a.mask_nqb = opts->mask_q_blocks; a.mask_nkb = opts->mask_k_blocks;
   a.k_vs = kv->k_vscales; a.v_vs = kv->v_vscales;
   a.vs_sp = kv->vscale_stride_page; a.vs_sh = kv->vscale_stride_head;
+  a.k_frag = kv->k_fragments; a.v_frag = kv->v_fragments;
+  a.frag_shift = kv->fragment_pages_log2;
   a.q_tiles = (int)ceil_div(io->q_rows, 128);
   a.heads_per_wg = (G % 2 == 0) ? 2 : 1;
   // groups dealt over 8 XCDs (padded), each with q_tiles tasks of G/HPW workgroups
@@ -394,6 +407,8 @@ attn_status attn_paged_decode(attn_ctx *ctx, const attn_io *io, const attn_kv *k
   a.rows_b = opts->rows_per_seq;
   a.k_vs = kv->k_vscales; a.v_vs = kv->v_vscales;
   a.vs_sp = kv->vscale_stride_page; a.vs_sh = kv->vscale_stride_head;
+  a.k_frag = kv->k_fragments; a.v_frag = kv->v_fragments;
+  a.frag_shift = kv->fragment_pages_log2;
   a.P = pl.P; a.T = pl.T;
   a.row_blocks = pl.row_blocks;
   a.ws_o = reinterpret_cast<float *>(workspace);
@@ -434,7 +449,8 @@ attn_status attn_debug_gather_kv(attn_ctx *ctx, const attn_kv *kv, int32_t b, in
                                           kv->v_stride_page, kv->v_stride_head, kv->dtype,
                                           kv->num_kv_heads, kv->head_dim, kv->k_scale, kv->v_scale,
                                           kv->k_vscales, kv->v_vscales, kv->vscale_stride_page,
-                                          kv->vscale_stride_head,
+                                          kv->vscale_stride_head, kv->k_fragments, kv->v_fragments,
+                                          kv->fragment_pages_log2,
                                           kv->page_table + (int64_t)b * kv->page_table_stride, seq_len,
                                           k_out, v_out, (hipStream_t)hip_stream),
                   err, "debug gather launch");
@@ -494,6 +510,9 @@ attn_status attn_kv_append(attn_ctx *ctx, const attn_kv *kv, const attn_kv_rows 
   a.v_vs = const_cast<float *>(kv->v_vscales);
   a.vs_sp = kv->vscale_stride_page;
   a.vs_sh = kv->vscale_stride_head;
+  a.k_frag = kv->k_fragments;
+  a.v_frag = kv->v_fragments;
+  a.frag_shift = kv->fragment_pages_log2;
   return launched(pa::launch_kv_append(a, (hipStream_t)hip_stream), err, "K/V append launch");
 }
 

@@ -192,9 +192,10 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append(AppendArgs a) {
   const char *ksrc = reinterpret_cast<const char *>(a.k_src);
   const char *vsrc = reinterpret_cast<const char *>(a.v_src);
   const int32_t *pt = a.page_table + (int64_t)b * a.pt_stride;
-  auto tile = [&](void *base, int64_t sp, int64_t sh, int slot) {
+  auto tile = [&](void *base, const uint64_t *frags, int64_t sp, int64_t sh, int slot) {
     const int64_t pid = pt[page0 + slot / 16];
-    return reinterpret_cast<char *>(base) + (pid * sp + (int64_t)g * sh) * ELT;
+    return page_addr_lane(reinterpret_cast<char *>(base) + (int64_t)g * sh * ELT, frags,
+                          a.frag_shift, pid, sp * ELT, (int64_t)g * sh * ELT);
   };
 
   // phase 1: token rows -> K tiles (token-major) and V codes -> LDS
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append(AppendArgs a) {
       ck[e] = encode<KVDT>(xk[e] / uk);
       vstage[slot][part * 8 + e] = encode<KVDT>(xv[e] / uv);
     }
-    store8<KVDT>(tile(a.k, a.k_sp, a.k_sh, slot) + ((int64_t)(slot % 16) * D + part * 8) * ELT, ck);
+    store8<KVDT>(tile(a.k, a.k_frag, a.k_sp, a.k_sh, slot) + ((int64_t)(slot % 16) * D + part * 8) * ELT, ck);
   }
   __syncthreads();
   // phase 2: V tiles (token-minor): 16 bytes (VG slots of one component) per
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append(AppendArgs a) {
   for (int idx = threadIdx.x; idx < NS / VG * D; idx += kAppendThreads) {
     const int d = idx / (NS / VG), s0 = (idx % (NS / VG)) * VG;
     if (s0 + VG <= s_lo || s0 >= s_hi) continue;
-    char *vt = tile(a.v, a.v_sp, a.v_sh, s0) + ((int64_t)d * 16 + s0 % 16) * ELT;
+    char *vt = tile(a.v, a.v_frag, a.v_sp, a.v_sh, s0) + ((int64_t)d * 16 + s0 % 16) * ELT;
     if (s0 >= s_lo && s0 + VG <= s_hi) {
       uint32_t c[16];
 #pragma unroll

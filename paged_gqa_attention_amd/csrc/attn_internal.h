@@ -38,6 +38,8 @@ struct DecodeArgs {
   const int32_t *rows_b;  // nullable [B]: rows of each sequence (<= R); the rest are skipped
   const float *k_vs, *v_vs;   // per-vector scales [page][head][16] (8-bit K/V), or null
   int64_t vs_sp, vs_sh;       // their page / head strides (floats)
+  const uint64_t *k_frag, *v_frag;   // fragment tables (device addresses), or null
+  int32_t frag_shift;                // log2(pages per fragment)
 };
 
 struct PrefillArgs {
@@ -65,6 +67,8 @@ struct PrefillArgs {
   int32_t num_wg;         // total workgroups
   const float *k_vs, *v_vs;   // per-vector scales [page][head][16] (8-bit K/V), or null
   int64_t vs_sp, vs_sh;
+  const uint64_t *k_frag, *v_frag;   // fragment tables (device addresses), or null
+  int32_t frag_shift;
 };
 
 // K/V append: new rows [B][n_new][Hkv][D] (source strides) into the paged pool
@@ -83,6 +87,8 @@ struct AppendArgs {
   float k_scale, v_scale;
   float *k_vs, *v_vs;         // per-vector scale pools (written), or null
   int64_t vs_sp, vs_sh;
+  const uint64_t *k_frag, *v_frag;   // fragment tables (device addresses), or null
+  int32_t frag_shift;
 };
 
 hipError_t launch_kv_append(const AppendArgs &a, hipStream_t s);
@@ -103,6 +109,7 @@ hipError_t launch_debug_gather(const void *k, const void *v, int64_t k_sp, int64
                                int64_t v_sp, int64_t v_sh, int kv_dtype, int Hkv, int D,
                                float k_scale, float v_scale, const float *k_vs,
                                const float *v_vs, int64_t vs_sp, int64_t vs_sh,
+                               const uint64_t *k_frag, const uint64_t *v_frag, int frag_shift,
                                const int32_t *pt_row, int seq_len, float *k_out, float *v_out,
                                hipStream_t s);
 

@@ -42,6 +42,35 @@ __device__ __forceinline__ u32x2 ld8(const void *p) {
   return *reinterpret_cast<const u32x2 *>(p);
 }
 
+// ---- page addressing ---------------------------------------------------------------
+
+// Address of the (page pid, head) tile of a pool.  Contiguous pools:
+// base_head + pid * page_bytes, base_head = pool base + head offset.  With a
+// fragment table (frags != null) page pid is page (pid & (2^shift - 1)) of
+// fragment pid >> shift, whose device address the table holds.  pid must be
+// wave-uniform: the table entry is read with a scalar load.
+__device__ __forceinline__ const char *page_addr(const char *base_head, const uint64_t *frags,
+                                                 int shift, int64_t pid, int64_t page_bytes,
+                                                 int64_t head_bytes) {
+  if (frags) {
+    typedef const __attribute__((address_space(4))) uint64_t cu64;
+    const uint64_t f = ((cu64 *)frags)[pid >> shift];
+    return reinterpret_cast<const char *>(f) + head_bytes +
+           (pid & ((int64_t(1) << shift) - 1)) * page_bytes;
+  }
+  return base_head + pid * page_bytes;
+}
+
+// the same for a per-lane page id (vector load of the table entry)
+__device__ __forceinline__ char *page_addr_lane(char *base_head, const uint64_t *frags, int shift,
+                                                int64_t pid, int64_t page_bytes,
+                                                int64_t head_bytes) {
+  if (frags)
+    return reinterpret_cast<char *>(frags[pid >> shift]) + head_bytes +
+           (pid & ((int64_t(1) << shift) - 1)) * page_bytes;
+  return base_head + pid * page_bytes;
+}
+
 // ---- storage -> FP32 -------------------------------------------------------------
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

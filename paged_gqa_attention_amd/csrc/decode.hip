@@ -23,10 +23,18 @@
 // With per-vector scales (8-bit K/V, template flag VS) a token's K scale
 // multiplies its scores and its V scale its softmax weights before P.V; the
 // row sums use the unscaled weights.
+#include <type_traits>
+
 #include "attn_internal.h"
 #include "common.h"
 
 namespace pa {
+
+// Page loops are emitted twice inside each partial kernel, once per
+// addressing mode, so that the contiguous-pool loop carries no trace of the
+// fragment lookup; one uniform branch per workgroup picks the loop.
+using Contiguous = std::false_type;
+using Fragmented = std::true_type;
 
 constexpr int kWaves = 4;
 constexpr float kNegInf = -__builtin_inff();
@@ -255,10 +263,19 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
   // per-vector scales: lane n's token (the quad shares it)
   const float *ksbase = VS ? a.k_vs + (int64_t)kvh * a.vs_sh + n : nullptr;
   const float *vsbase = VS ? a.v_vs + (int64_t)kvh * a.vs_sh + n : nullptr;
-  auto load_page = [&](int page_idx, u32x4 *kd, u32x4 *vd, float &ksd, float &vsd) {
+  auto load_page = [&](auto mode, int page_idx, u32x4 *kd, u32x4 *vd, float &ksd,
+                       float &vsd) __attribute__((always_inline)) {
     const int64_t pid = page_id(page_idx);
-    const char *kp = kbase + pid * a.k_sp * ELT + n * (D * ELT) + qq * 16;
-    const char *vp = vbase + pid * a.v_sp * ELT + lane * 16;
+    const char *kp, *vp;
+    if constexpr (decltype(mode)::value) {
+      kp = page_addr(kbase, a.k_frag, a.frag_shift, pid, a.k_sp * ELT, (int64_t)kvh * a.k_sh * ELT);
+      vp = page_addr(vbase, a.v_frag, a.frag_shift, pid, a.v_sp * ELT, (int64_t)kvh * a.v_sh * ELT);
+    } else {
+      kp = kbase + pid * a.k_sp * ELT;
+      vp = vbase + pid * a.v_sp * ELT;
+    }
+    kp += n * (D * ELT) + qq * 16;
+    vp += lane * 16;
 #pragma unroll
     for (int c = 0; c < NL; ++c) {
       kd[c] = ld16(kp + c * 64);
@@ -270,7 +287,8 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
     }
   };
 
-  auto process_page = [&](const int pg, const u32x4 *kc, const u32x4 *vc, float ksc, float vsc) {
+  auto process_page = [&](const int pg, const u32x4 *kc, const u32x4 *vc, float ksc,
+                          float vsc) __attribute__((always_inline)) {
     // ---- scores of this lane's token for all rows ----
     float s[RB];
 #pragma unroll
@@ -379,16 +397,20 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
   // loads stay in flight (no register copies, which would force a full wait).
   u32x4 kA[NL], vA[NL], kB[NL], vB[NL];
   float ksA = 1.f, vsA = 1.f, ksB = 1.f, vsB = 1.f;
-  if (pg < pg_end) load_page(pg, kA, vA, ksA, vsA);
-  if (pg + kWaves < pg_end) load_page(pg + kWaves, kB, vB, ksB, vsB);
-  for (; pg < pg_end; pg += 2 * kWaves) {
-    process_page(pg, kA, vA, ksA, vsA);
-    if (pg + 2 * kWaves < pg_end) load_page(pg + 2 * kWaves, kA, vA, ksA, vsA);
-    if (pg + kWaves < pg_end) {
-      process_page(pg + kWaves, kB, vB, ksB, vsB);
-      if (pg + 3 * kWaves < pg_end) load_page(pg + 3 * kWaves, kB, vB, ksB, vsB);
+  auto pages = [&](auto mode) __attribute__((always_inline)) {
+    if (pg < pg_end) load_page(mode, pg, kA, vA, ksA, vsA);
+    if (pg + kWaves < pg_end) load_page(mode, pg + kWaves, kB, vB, ksB, vsB);
+    for (; pg < pg_end; pg += 2 * kWaves) {
+      process_page(pg, kA, vA, ksA, vsA);
+      if (pg + 2 * kWaves < pg_end) load_page(mode, pg + 2 * kWaves, kA, vA, ksA, vsA);
+      if (pg + kWaves < pg_end) {
+        process_page(pg + kWaves, kB, vB, ksB, vsB);
+        if (pg + 3 * kWaves < pg_end) load_page(mode, pg + 3 * kWaves, kB, vB, ksB, vsB);
+      }
     }
-  }
+  };
+  if (a.k_frag || a.v_frag) pages(Fragmented{});
+  else pages(Contiguous{});
 
   // ---- wave totals: l over the 16 token lanes of a row, o over the token groups ----
 #pragma unroll
@@ -570,15 +592,29 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
   // V rows: value row 16*mb + n, tokens 8*j .. 8*j+7 (page j/2, offset 8*(j&1))
   // Per-vector scales: the K and V scales of the lane's score tokens 8j .. 8j+7
   // (sd[0..1] K, sd[2..3] V).
-  auto load_pair = [&](int ppi, u32x4 (*kd)[KL], u32x4 *vd16, u32x2 *vd8, f32x4 *sd) {
+  auto load_pair = [&](auto mode, int ppi, u32x4 (*kd)[KL], u32x4 *vd16, u32x2 *vd8,
+                       f32x4 *sd) __attribute__((always_inline)) {
     const int k = (ppi - pp_first) / kWaves;
     const int64_t pid0 = __builtin_amdgcn_readlane(ids0, k);
     const int64_t pid1 = __builtin_amdgcn_readlane(ids1, k);
+    // the pair's two page tiles of K and V (page ids are wave-uniform)
+    const char *kpg0, *kpg1, *vpg0, *vpg1;
+    if constexpr (decltype(mode)::value) {
+      const int64_t kh = (int64_t)kvh * a.k_sh * ELT, vh = (int64_t)kvh * a.v_sh * ELT;
+      kpg0 = page_addr(kbase, a.k_frag, a.frag_shift, pid0, a.k_sp * ELT, kh);
+      kpg1 = page_addr(kbase, a.k_frag, a.frag_shift, pid1, a.k_sp * ELT, kh);
+      vpg0 = page_addr(vbase, a.v_frag, a.frag_shift, pid0, a.v_sp * ELT, vh);
+      vpg1 = page_addr(vbase, a.v_frag, a.frag_shift, pid1, a.v_sp * ELT, vh);
+    } else {
+      kpg0 = kbase + pid0 * a.k_sp * ELT;
+      kpg1 = kbase + pid1 * a.k_sp * ELT;
+      vpg0 = vbase + pid0 * a.v_sp * ELT;
+      vpg1 = vbase + pid1 * a.v_sp * ELT;
+    }
 #pragma unroll
     for (int aa = 0; aa < 2; ++aa) {
       const int tok = 8 * (n >> 2) + 4 * aa + (n & 3);
-      const int64_t pid = tok < 16 ? pid0 : pid1;
-      const char *kp = kbase + pid * a.k_sp * ELT + (tok & 15) * (D * ELT);
+      const char *kp = (tok < 16 ? kpg0 : kpg1) + (tok & 15) * (D * ELT);
 #pragma unroll
       for (int u = 0; u < KL; ++u) {
         const int d0 = is8bit(KVDT) ? 64 * u + 16 * j : dchunk<KVDT>(u, j);
@@ -586,7 +622,7 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
       }
     }
     const int64_t pidv = (j >> 1) ? pid1 : pid0;
-    const char *vp = vbase + pidv * a.v_sp * ELT + (8 * (j & 1)) * ELT;
+    const char *vp = ((j >> 1) ? vpg1 : vpg0) + (8 * (j & 1)) * ELT;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const char *row = vp + (int64_t)(16 * mb + n) * 16 * ELT;
@@ -604,7 +640,7 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
     }
   };
   auto process_pair = [&](const int pp, const u32x4 (*kf)[KL], const u32x4 *vf16, const u32x2 *vf8,
-                          const f32x4 *sd) {
+                          const f32x4 *sd) __attribute__((always_inline)) {
     // ---- S^T = K Q^T ----
     f32x4 s[NB][2];
 #pragma unroll
@@ -723,16 +759,20 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
   u32x4 vA16[MB], vB16[MB];
   u32x2 vA8[MB], vB8[MB];
   f32x4 sA[4], sB[4];
-  if (pp < pp_end) load_pair(pp, kA, vA16, vA8, sA);
-  if (pp + kWaves < pp_end) load_pair(pp + kWaves, kB, vB16, vB8, sB);
-  for (; pp < pp_end; pp += 2 * kWaves) {
-    process_pair(pp, kA, vA16, vA8, sA);
-    if (pp + 2 * kWaves < pp_end) load_pair(pp + 2 * kWaves, kA, vA16, vA8, sA);
-    if (pp + kWaves < pp_end) {
-      process_pair(pp + kWaves, kB, vB16, vB8, sB);
-      if (pp + 3 * kWaves < pp_end) load_pair(pp + 3 * kWaves, kB, vB16, vB8, sB);
+  auto pairs = [&](auto mode) __attribute__((always_inline)) {
+    if (pp < pp_end) load_pair(mode, pp, kA, vA16, vA8, sA);
+    if (pp + kWaves < pp_end) load_pair(mode, pp + kWaves, kB, vB16, vB8, sB);
+    for (; pp < pp_end; pp += 2 * kWaves) {
+      process_pair(pp, kA, vA16, vA8, sA);
+      if (pp + 2 * kWaves < pp_end) load_pair(mode, pp + 2 * kWaves, kA, vA16, vA8, sA);
+      if (pp + kWaves < pp_end) {
+        process_pair(pp + kWaves, kB, vB16, vB8, sB);
+        if (pp + 3 * kWaves < pp_end) load_pair(mode, pp + 3 * kWaves, kB, vB16, vB8, sB);
+      }
     }
-  }
+  };
+  if (a.k_frag || a.v_frag) pairs(Fragmented{});
+  else pairs(Contiguous{});
 
   // ---- wave totals ----
 #pragma unroll
@@ -804,8 +844,10 @@ template <int KVDT, bool VS>
 __global__ void debug_gather(const void *k, const void *v, int64_t k_sp, int64_t k_sh,
                              int64_t v_sp, int64_t v_sh, int Hkv, int D, float k_scale,
                              float v_scale, const float *k_vs, const float *v_vs, int64_t vs_sp,
-                             int64_t vs_sh, const int32_t *pt, int seq_len, float *k_out,
+                             int64_t vs_sh, const uint64_t *k_frag, const uint64_t *v_frag,
+                             int frag_shift, const int32_t *pt, int seq_len, float *k_out,
                              float *v_out) {
+  constexpr int ELT = DtInfo<KVDT>::bytes;
   const int64_t total = (int64_t)Hkv * seq_len * D;
   for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * blockDim.x) {
@@ -813,11 +855,16 @@ __global__ void debug_gather(const void *k, const void *v, int64_t k_sp, int64_t
     const int t = (idx / D) % seq_len;
     const int g = idx / ((int64_t)D * seq_len);
     const int64_t pid = pt[t >> 4];
-    const int64_t ki = pid * k_sp + g * k_sh + (t & 15) * D + d;
-    const int64_t vi = pid * v_sp + g * v_sh + (int64_t)d * 16 + (t & 15);
+    // element offsets inside the (page, head) tiles, from the tiles' addresses
+    const int64_t ki = (t & 15) * D + d;
+    const int64_t vi = (int64_t)d * 16 + (t & 15);
     float kv[2];
     const int64_t src[2] = {ki, vi};
-    const void *base[2] = {k, v};
+    char *kh = const_cast<char *>(reinterpret_cast<const char *>(k)) + (int64_t)g * k_sh * ELT;
+    char *vh = const_cast<char *>(reinterpret_cast<const char *>(v)) + (int64_t)g * v_sh * ELT;
+    const void *base[2] = {
+        page_addr_lane(kh, k_frag, frag_shift, pid, k_sp * ELT, (int64_t)g * k_sh * ELT),
+        page_addr_lane(vh, v_frag, frag_shift, pid, v_sp * ELT, (int64_t)g * v_sh * ELT)};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int64_t e = src[s];
@@ -1013,6 +1060,7 @@ hipError_t launch_debug_gather(const void *k, const void *v, int64_t k_sp, int64
                                int64_t v_sp, int64_t v_sh, int kv_dtype, int Hkv, int D,
                                float k_scale, float v_scale, const float *k_vs,
                                const float *v_vs, int64_t vs_sp, int64_t vs_sh,
+                               const uint64_t *k_frag, const uint64_t *v_frag, int frag_shift,
                                const int32_t *pt_row, int seq_len, float *k_out, float *v_out,
                                hipStream_t s) {
   const int64_t total = (int64_t)Hkv * seq_len * D;
@@ -1020,8 +1068,8 @@ hipError_t launch_debug_gather(const void *k, const void *v, int64_t k_sp, int64
   const int blocks = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
 #define PA_GATHER(DT, VS)                                                                     \
   hipLaunchKernelGGL((debug_gather<DT, VS>), dim3(blocks), dim3(256), 0, s, k, v, k_sp, k_sh, \
-                     v_sp, v_sh, Hkv, D, k_scale, v_scale, k_vs, v_vs, vs_sp, vs_sh, pt_row,  \
-                     seq_len, k_out, v_out)
+                     v_sp, v_sh, Hkv, D, k_scale, v_scale, k_vs, v_vs, vs_sp, vs_sh, k_frag, \
+                     v_frag, frag_shift, pt_row, seq_len, k_out, v_out)
   const bool vs = k_vs != nullptr;
   switch (kv_dtype) {
     case DT_F32: PA_GATHER(DT_F32, false); break;

@@ -205,8 +205,12 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
         const int kp = k_pg[c], vp = v_pg[c];
         const int pk = kp == 0 ? pid[0] : kp == 1 ? pid[1] : kp == 2 ? pid[2] : pid[3];
         const int pv = vp == 0 ? pid[0] : vp == 1 ? pid[1] : vp == 2 ? pid[2] : pid[3];
-        const char *kpage = kbase + (int64_t)__builtin_amdgcn_readfirstlane(pk) * k_page_bytes;
-        const char *vpage = vbase + (int64_t)__builtin_amdgcn_readfirstlane(pv) * v_page_bytes;
+        const char *kpage = page_addr(kbase, a.k_frag, a.frag_shift,
+                                      __builtin_amdgcn_readfirstlane(pk), k_page_bytes,
+                                      (int64_t)kvh * a.k_sh * ELT);
+        const char *vpage = page_addr(vbase, a.v_frag, a.frag_shift,
+                                      __builtin_amdgcn_readfirstlane(pv), v_page_bytes,
+                                      (int64_t)kvh * a.v_sh * ELT);
         kreg[c] = ld16(kpage + k_goff[c]);
         vreg[c] = ld16(vpage + v_goff[c]);
         if constexpr (VS)

@@ -34,7 +34,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.attn_abi_version() == 3
+    assert lib.attn_abi_version() == 4
 
 
 def test_open_without_a_gpu_is_a_device_error(lib):
@@ -303,3 +303,57 @@ def test_per_vector_append_needs_unit_tensor_scales(hctx):
     assert app() == pa.ATTN_ERR_DEVICE                            # valid: nothing enqueued
     kv.v_scale = 2.0
     assert app() == pa.ATTN_ERR_INVALID_ARGUMENT
+
+
+def test_fragment_tables_validate(hctx):
+    io, _, op = _decode_args()
+    kf = FakeTensor((8, 2, 16, 128), torch.bfloat16, 0x100000)       # one fragment of 8 pages
+    vf = FakeTensor((8, 2, 128, 16), torch.bfloat16, 0x200000)
+    pt = FakeTensor((2, 64), torch.int32, 0x300000)
+    lens = FakeTensor((2,), torch.int32, 0x400000)
+    tk = FakeTensor((13,), torch.int64, 0xC00000)
+    tv = FakeTensor((13,), torch.int64, 0xD00000)
+    mk = lambda **kw: pa.make_kv(kf, vf, pt, lens, k_fragments=tk, v_fragments=tv,
+                                 fragment_pages_log2=3, num_pages=100, **kw)
+    kv = mk()
+    assert kv.k_pages is None and kv.num_pages == 100 and kv.num_fragments == 13
+    P, T, W = pa.attn_paged_decode_plan(hctx, io, kv, op)
+    assert P >= 1
+    plan = lambda kv: _status(lambda: pa.attn_paged_decode_plan(hctx, io, kv, op))
+    kv = mk()
+    kv.num_fragments = 12                                         # 12 x 8 < 100 pages
+    assert plan(kv) == pa.ATTN_ERR_INVALID_ARGUMENT
+    kv = mk()
+    kv.fragment_pages_log2 = 21
+    assert plan(kv) == pa.ATTN_ERR_INVALID_ARGUMENT
+    kv = mk()
+    kv.k_fragments = 0xC00004                                     # table misaligned
+    assert plan(kv) == pa.ATTN_ERR_INVALID_ARGUMENT
+    kv = mk()
+    kv.k_fragments = None                                         # K then needs its pool
+    assert plan(kv) == pa.ATTN_ERR_INVALID_ARGUMENT
+    # the append and the gather take fragmented pools too
+    rows = pa.make_rows(FakeTensor((2, 3, 2, 128), torch.bfloat16, 0x700000),
+                        FakeTensor((2, 3, 2, 128), torch.bfloat16, 0x800000))
+    assert _status(lambda: pa.attn_kv_append(hctx, mk(), rows, stream=0)) == pa.ATTN_ERR_DEVICE
+    with pytest.raises(pa.AttnError):                             # a fragment view of 8 pages
+        pa.make_kv(kf, vf, pt, lens, k_fragments=tk, v_fragments=tv, fragment_pages_log2=2,
+                   num_pages=100)
+
+
+def test_descriptors_keep_their_tensors_alive():
+    """A descriptor holds raw pointers: the tensors it was made from must live as
+    long as it does (else a caching allocator can hand their memory to the next
+    allocation before the call runs)."""
+    import gc
+    import weakref
+    k = torch.zeros((2, 3, 2, 64), dtype=torch.bfloat16)
+    v = torch.zeros((2, 3, 2, 64), dtype=torch.bfloat16)
+    wk, wv = weakref.ref(k), weakref.ref(v)
+    rows = pa.make_rows(k, v)
+    del k, v
+    gc.collect()
+    assert wk() is not None and wv() is not None
+    del rows
+    gc.collect()
+    assert wk() is None and wv() is None
