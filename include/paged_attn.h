@@ -91,9 +91,9 @@
  *                              where required), bad mask geometry.
  *   ATTN_ERR_UNSUPPORTED       a well-formed request this build does not
  *                              implement (head_dim not 64, 128 or 256 --
- *                              256 for decode and append with 16-bit or 8-bit
- *                              K/V only --, page_size not 16, unsupported
- *                              dtype combination).
+ *                              256 with 16-bit or 8-bit K/V only --,
+ *                              page_size not 16, unsupported dtype
+ *                              combination).
  *   ATTN_ERR_WORKSPACE_TOO_SMALL  decode workspace below the queried size.
  *   ATTN_ERR_DEVICE            no usable gfx950 device, or a HIP error while
  *                              enqueuing (its text in *err).
@@ -137,7 +137,7 @@ typedef struct {
   int32_t num_pages;            /* pages in the pool */
   int32_t page_size;            /* tokens per page; must be 16 */
   int32_t num_kv_heads;
-  int32_t head_dim;             /* 64, 128, or 256 (decode and append, 16-/8-bit K/V) */
+  int32_t head_dim;             /* 64, 128, or 256 (256: 16-bit or 8-bit K/V) */
   int32_t pad0;
   int64_t k_stride_page, k_stride_head;   /* elements */
   int64_t v_stride_page, v_stride_head;   /* elements */

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpaged_attn.so")
-SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "probe.hip", "append.hip"]
+SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "prefill_wide.hip", "probe.hip", "append.hip"]
 ARCH = "gfx950"
 
 

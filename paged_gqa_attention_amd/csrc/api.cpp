@@ -296,7 +296,8 @@ attn_status prefill_common(attn_ctx *ctx, const attn_io *io, const attn_kv *kv, 
   a.k_frag = kv->k_fragments; a.v_frag = kv->v_fragments;
   a.frag_shift = kv->fragment_pages_log2;
   a.q_tiles = (int)ceil_div(io->q_rows, 128);
-  a.heads_per_wg = (G % 2 == 0) ? 2 : 1;
+  // head_dim 256 runs one query head per workgroup (16 rows per wave)
+  a.heads_per_wg = (kv->head_dim == 256 || G % 2) ? 1 : 2;
   // groups dealt over 8 XCDs (padded), each with q_tiles tasks of G/HPW workgroups
   const int64_t groups = (int64_t)a.B * a.Hkv;
   const int64_t nwg = round_up(groups, 8) * a.q_tiles * (G / a.heads_per_wg);

@@ -103,6 +103,7 @@ bool decode_valu_supported(int kv_dtype, int q_dtype, int D);
 int decode_blocks_per_cu(bool mfma, int kv_dtype, int q_dtype, int D, int rows, bool vs);
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_prefill_wide(const PrefillArgs &a, hipStream_t s);   // head_dim 256
 bool prefill_supported(int kv_dtype, int q_dtype, int D);
 
 hipError_t launch_debug_gather(const void *k, const void *v, int64_t k_sp, int64_t k_sh,

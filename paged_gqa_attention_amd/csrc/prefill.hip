@@ -502,7 +502,7 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
 }
 
 bool prefill_supported(int kv, int qd, int D) {
-  if (D != 64 && D != 128) return false;
+  if (D != 64 && D != 128 && D != 256) return false;
   if (kv == DT_BF16) return qd == DT_BF16;
   if (kv == DT_F16) return qd == DT_F16;
   if (is8bit(kv)) return qd == DT_BF16 || qd == DT_F16;
@@ -536,6 +536,7 @@ static hipError_t prefill_8(const PrefillArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {
+  if (a.D == 256) return launch_prefill_wide(a, s);
   switch (a.kv_dtype) {
     case DT_BF16: return prefill_d<DT_BF16, DT_BF16, false>(a, s);
     case DT_F16: return prefill_d<DT_F16, DT_F16, false>(a, s);

@@ -234,7 +234,7 @@ def test_head_dim_256_support(hctx):
     assert P >= 1 and W > 0
     io, kv, op = _decode_args(B=2, R=1, Hq=8, Hkv=2, d=256, stride=64, dtype=torch.float32)
     assert _status(lambda: pa.attn_paged_decode_plan(hctx, io, kv, op)) == pa.ATTN_ERR_UNSUPPORTED
-    # prefill is not built for head_dim 256
+    # prefill at head_dim 256 validates (and a planning-only context enqueues nothing)
     q = FakeTensor((1, 64, 8, 256), torch.bfloat16, 0x500000)
     o = FakeTensor((1, 64, 8, 256), torch.bfloat16, 0x600000)
     k = FakeTensor((100, 2, 16, 256), torch.bfloat16, 0x100000)
@@ -243,7 +243,7 @@ def test_head_dim_256_support(hctx):
     lens = FakeTensor((1,), torch.int32, 0x400000)
     kv = pa.make_kv(k, v, pt, lens)
     assert _status(lambda: pa.attn_prefill(hctx, pa.make_io(q, o), kv, pa.make_opts(), stream=0)) == \
-        pa.ATTN_ERR_UNSUPPORTED
+        pa.ATTN_ERR_DEVICE
     # head_dim 96 is not built anywhere
     io, kv, op = _decode_args(d=96)
     assert _status(lambda: pa.attn_paged_decode_plan(hctx, io, kv, op)) == pa.ATTN_ERR_UNSUPPORTED

@@ -164,6 +164,8 @@ PREFILL_CASES = [
     ("bf8vs_d64_g3", dict(B=1, Hq=6, Hkv=2, d=64, S=129, dt=DT_BF8, vs=True)),
     ("bf8vs_d128_chunked", dict(B=2, Hq=8, Hkv=2, d=128, S=700, q_rows=150, dt=DT_BF8, vs=True)),
     ("fp8vs_tiny", dict(B=2, Hq=4, Hkv=2, d=64, S=5, dt=DT_FP8, vs=True)),
+    ("bf8vs_d256", dict(B=1, Hq=8, Hkv=2, d=256, S=250, dt=DT_BF8, vs=True)),
+    ("bf8_d256", dict(B=1, Hq=4, Hkv=2, d=256, S=170, dt=DT_BF8)),
 ]
 
 

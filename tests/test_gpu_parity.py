@@ -216,6 +216,13 @@ PREFILL_CASES = [
     ("d64_chunked", dict(B=2, Hq=8, Hkv=2, d=64, S=700, q_rows=150, sinks=True)),
     ("d64_tiny", dict(B=2, Hq=4, Hkv=2, d=64, S=5, sinks=True)),
     ("d64_fp32_out", dict(B=1, Hq=4, Hkv=2, d=64, S=150, sinks=True, o=DT_F32)),
+    # head_dim 256: the 16-rows-per-wave kernel, 32-key tiles
+    ("d256_g2_sink", dict(B=2, Hq=8, Hkv=4, d=256, S=300, sinks=True)),
+    ("d256_g4_f16", dict(B=1, Hq=8, Hkv=2, d=256, S=129, sinks=True, dt=DT_F16)),
+    ("d256_fp8", dict(B=1, Hq=4, Hkv=2, d=256, S=200, sinks=True, dt=DT_FP8)),
+    ("d256_chunked", dict(B=2, Hq=4, Hkv=1, d=256, S=400, q_rows=90, sinks=True)),
+    ("d256_tiny", dict(B=2, Hq=4, Hkv=2, d=256, S=5, sinks=True)),
+    ("d256_fp32_out", dict(B=1, Hq=4, Hkv=4, d=256, S=140, sinks=False, o=DT_F32)),
 ]
 
 
@@ -253,6 +260,7 @@ BS_CASES = [
     ("d128_blk128", dict(S=1000, Hq=8, Hkv=2, d=128, blk=128, mh=1, keep=0.3)),
     ("d64_blk64_perhead", dict(S=700, Hq=8, Hkv=2, d=64, blk=64, mh=2, keep=0.4, sinks=True)),
     ("d64_blk256", dict(S=900, Hq=4, Hkv=2, d=64, blk=256, mh=1, keep=0.5)),
+    ("d256_blk64_perhead", dict(S=600, Hq=4, Hkv=2, d=256, blk=64, mh=2, keep=0.4, sinks=True)),
 ]
 
 
@@ -390,6 +398,35 @@ def test_prefill_ragged_rows(masked):
     p.rows_per_seq = torch.tensor(rows, dtype=torch.int32)
     o, lse = run(Dev(p))
     check_full(p, o, lse)
+
+
+@pytest.mark.parametrize("masked", [False, True])
+def test_prefill_ragged_rows_d256(masked):
+    _say(f"ragged prefill d256 masked={masked}")
+    if masked:
+        p = synth.make_blocksparse(94, 3, 4, 2, 256, 320, mask_block=64, mask_heads=1, keep_prob=0.4)
+        rows = [320, 0, 77]
+    else:
+        p = synth.make_prefill(95, 3, 4, 2, 256, 350, q_rows=200, lens=[300, 350, 210])
+        rows = [200, 33, 129]
+    p.rows_per_seq = torch.tensor(rows, dtype=torch.int32)
+    o, lse = run(Dev(p))
+    check_full(p, o, lse)
+
+
+def test_prefill_d256_row_matches_decode():
+    """A prefill row at head_dim 256 equals the single-row decode at its position."""
+    _say("prefill d256 row = decode")
+    p = synth.make_prefill(96, 1, 4, 2, 256, 200, sinks=True)
+    o, _ = run(Dev(p))
+    import copy
+    i = 137
+    q = copy.copy(p)
+    q.kind, q.q_rows = "decode", 1
+    q.q = p.q[:, i:i + 1].contiguous()
+    q.seq_lens = torch.tensor([i + 1], dtype=torch.int32)
+    od, _ = run(Dev(q))
+    assert np.max(np.abs(o[0, i] - od[0, 0])) <= 2e-2
 
 
 # ---------------------------------------------------------------- head_dim 256 (decode)
