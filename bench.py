@@ -425,6 +425,7 @@ def main():
         "kv_append": kv_append_summary(ctx, args),
         "formats": formats_summary(ctx, args),
         "fragments": fragments_summary(ctx, args),
+        "head_dim_256": wide_summary(ctx, args),
     }
     if args.all:
         extra(ctx, args)
@@ -526,6 +527,38 @@ def fragments_summary(ctx, args, fragment_bytes=256 << 10, arena_bytes=256 << 20
            "fragmented_GBs": round(nbytes / (ms1 * 1e-3) / 1e9, 1),
            "overhead_pct": round(100.0 * (ms1 / ms0 - 1.0), 2)}
     del views, tables, kvf, call, callf, p
+    torch.cuda.empty_cache()
+    return out
+
+
+def wide_summary(ctx, args):
+    """head_dim 256, the model layout of four KV heads of 256 (16 query heads):
+    decode 16 x 16,384 keys at R = 1 and R = 4 (HBM roofline), causal prefill
+    with sinks 4 x 8,192 (MFMA roofline); bf16."""
+    import torch
+    import synth
+    from paged_gqa_attention_amd import accounting as acc
+    out = {"decode_workload": "B=16, Hq=16, Hkv=4, d=256, 16,384 keys, bf16",
+           "prefill_workload": "B=4, S=8192, Hq=16, Hkv=4, d=256, sinks, bf16"}
+    for R in (1, 4):
+        p = synth.make_decode(606, 16, 16, 4, 256, [16384] * 16, R, kv_dtype=synth.DT_BF16,
+                              stride=1024, device="cuda")
+        call, (P, T), keep = decode_setup(ctx, p, "cuda")
+        ms = time_calls(call, args.steps, args.warmup)
+        b = acc.decode_bytes(p.seq_lens.tolist(), R, 16, 4, 256, 2, 2, 2)
+        gbs = b / (ms * 1e-3) / 1e9
+        out[f"decode_R{R}"] = {"ms": round(ms, 4), "GBs": round(gbs, 1),
+                               "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "splits": P}
+        del keep, call, p
+        torch.cuda.empty_cache()
+    pp = synth.make_prefill(607, 4, 16, 4, 256, 8192, sinks=True, device="cuda")
+    pcall, pkeep = prefill_setup(ctx, pp, "cuda")
+    pms = time_calls(pcall, max(3, args.steps // 2), max(1, args.warmup // 2))
+    flops = acc.attention_flops(acc.causal_pairs(8192, 8192), 16, 256, 4)
+    tfs = flops / (pms * 1e-3) / 1e12
+    out["prefill"] = {"ms": round(pms, 3), "TFLOPs": round(tfs, 1),
+                      "mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 4), "flops_per_call": flops}
+    del pkeep, pcall, pp
     torch.cuda.empty_cache()
     return out
 

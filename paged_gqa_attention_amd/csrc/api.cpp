@@ -140,6 +140,7 @@ attn_status check_ctx(const attn_ctx *ctx, char **err) {
 
 struct DecodePlan {
   bool mfma;
+  bool wide;              // head_dim 256 with more than 8 rows per KV head
   int rows, rb, row_blocks, P, T;
   size_t ws_bytes, ws_o_bytes, ws_ml_bytes;
 };
@@ -148,6 +149,7 @@ constexpr int kTGran = 128;   // partition granularity (tokens)
 constexpr int kTMax = 8192;   // partition size limit (page ids a wave preloads)
 constexpr int kValuWgPerCu = 2;   // decode_valu workgroups per CU the planner counts on
 constexpr int kMfmaWgPerCu = 1;   // decode_mfma workgroups per CU the planner counts on
+constexpr int kWideWgPerCu = 2;   // head_dim 256 verify workgroups per CU
 
 attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *kv, const attn_opts *opts,
                         DecodePlan *pl, char **err) {
@@ -169,7 +171,8 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
   // these arguments; otherwise the VALU kernel runs them in blocks of 8 rows
   pl->mfma = kv->dtype != ATTN_F32 && rows > 8 &&
              pa::decode_mfma_supported(kv->dtype, io->q_dtype, D, rows);
-  if (pl->mfma) {
+  pl->wide = !pl->mfma && rows > 8 && pa::decode_wide_supported(kv->dtype, io->q_dtype, D, rows);
+  if (pl->mfma || pl->wide) {
     pl->rb = rows;
     pl->row_blocks = 1;
   } else {
@@ -179,8 +182,9 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
     pl->row_blocks = (int)ceil_div(rows, pl->rb);
   }
   // LDS the partial kernel needs for its rows (merge buffer + softmax state)
-  const size_t lds = pl->mfma ? (size_t)round_up(rows, 16) * (D + 4) * 4 + 2 * 4 * 64 * 4
-                              : (size_t)pl->rb * D * 4 + 4 * 16 * pl->rb * 4 + 3 * 4 * pl->rb * 4;
+  const size_t lds = pl->wide ? (size_t)2 * 32 * (256 + 8) * 2 + (size_t)2 * 256 * (32 + 8) * 2 + 128
+                 : pl->mfma ? (size_t)round_up(rows, 16) * (D + 4) * 4 + 2 * 4 * 64 * 4
+                            : (size_t)pl->rb * D * 4 + 4 * 16 * pl->rb * 4 + 3 * 4 * pl->rb * 4;
   if (lds > ctx->lds_per_block)
     return fail(err, ATTN_ERR_UNSUPPORTED, "decode needs %zu bytes of LDS, the device has %zu", lds, ctx->lds_per_block);
 
@@ -188,7 +192,7 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
   // workgroups covers every (sequence, KV head, row block) once; a second,
   // partly filled round would run at a fraction of the occupancy.
   const int64_t cap = (int64_t)kv->page_table_stride * kPage;
-  const int rows_per_wg = pl->mfma ? rows : pl->rb;
+  const int rows_per_wg = (pl->mfma || pl->wide) ? rows : pl->rb;
   const int64_t tmin = round_up(std::max<int64_t>(256, 64 * (int64_t)rows_per_wg), kTGran);
   int64_t T;
   if (opts->num_splits > 0) {
@@ -199,10 +203,11 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
     // kernel) or kMfmaWgPerCu (MFMA kernel) per CU: that many already reach
     // the HBM read rate, and the longer partitions leave fewer idle
     // workgroups when sequences are shorter than the capacity.
-    const int cap_cu = pl->mfma ? kMfmaWgPerCu : kValuWgPerCu;
+    const int cap_cu = pl->wide ? kWideWgPerCu : pl->mfma ? kMfmaWgPerCu : kValuWgPerCu;
     int per_cu = ctx->host_only ? cap_cu
-                                : pa::decode_blocks_per_cu(pl->mfma, kv->dtype, io->q_dtype, D, rows,
-                                                           kv->k_vscales != nullptr);
+                 : pl->wide ? pa::decode_wide_blocks_per_cu(kv->dtype, io->q_dtype, kv->k_vscales != nullptr)
+                            : pa::decode_blocks_per_cu(pl->mfma, kv->dtype, io->q_dtype, D, rows,
+                                                       kv->k_vscales != nullptr);
     per_cu = std::max(1, std::min(per_cu, cap_cu));
     const int64_t slots = (int64_t)ctx->num_cus * per_cu;
     const int64_t target = std::max<int64_t>(1, slots / groups);
@@ -418,8 +423,9 @@ attn_status attn_paged_decode(attn_ctx *ctx, const attn_io *io, const attn_kv *k
   DeviceGuard g(ctx->device);
   if (!g.ok) return fail(err, ATTN_ERR_DEVICE, "cannot select device %d", ctx->device);
   hipStream_t s = (hipStream_t)hip_stream;
-  st = launched(pl.mfma ? pa::launch_decode_mfma(a, s) : pa::launch_decode_valu(a, s), err,
-                "decode partial launch");
+  st = launched(pl.wide ? pa::launch_decode_wide(a, s)
+                : pl.mfma ? pa::launch_decode_mfma(a, s) : pa::launch_decode_valu(a, s),
+                err, "decode partial launch");
   if (st != ATTN_OK) return st;
   return launched(pa::launch_decode_merge(a, s), err, "decode merge launch");
 }

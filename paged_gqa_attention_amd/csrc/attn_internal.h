@@ -104,6 +104,10 @@ int decode_blocks_per_cu(bool mfma, int kv_dtype, int q_dtype, int D, int rows, 
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_prefill_wide(const PrefillArgs &a, hipStream_t s);   // head_dim 256
+// head_dim 256 multi-row verify partial (up to 64 rows per KV head)
+hipError_t launch_decode_wide(const DecodeArgs &a, hipStream_t s);
+bool decode_wide_supported(int kv_dtype, int q_dtype, int D, int rows);
+int decode_wide_blocks_per_cu(int kv_dtype, int q_dtype, bool vs);
 bool prefill_supported(int kv_dtype, int q_dtype, int D);
 
 hipError_t launch_debug_gather(const void *k, const void *v, int64_t k_sp, int64_t k_sh,

@@ -209,11 +209,11 @@ __device__ __forceinline__ float sum_xor16(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// 3-input maximum in one instruction (operands are never NaN where it is used)
+// 3-input maximum.  Plain code, not inline asm: its operands are often MFMA
+// results, and the compiler inserts the wait states a VALU read of an MFMA
+// result needs only for instructions it can see (it forms v_max3_f32 itself).
 __device__ __forceinline__ float max3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
 }
 
 }  // namespace pa

@@ -20,6 +20,16 @@
 // (Geramy/LSE releases, v0.4.14: masked key windows skipped; TokenSpeed-
 // Kernel-AMD page, "Attention": sinks in the denominator; LSE README,
 // FlashPrefill V2 paragraph: attention on kept blocks only).
+//
+// The same kernel, in its decode mode (DEC), is the multi-row verify partial
+// at head_dim 256: a workgroup of up to 4 waves owns the G.R rows of one KV
+// head (16 per wave) and one KV partition, so each K/V tile is read from HBM
+// once for all rows (Geramy/LSE releases, v0.4.21: K/V reads shared across
+// query heads and verify rows; v0.4.19/v0.4.20: partitions merged by a
+// log-sum-exp merge, which the decode merge kernel does); each wave writes its
+// rows' unnormalised partial output, max and sum.
+#include <type_traits>
+
 #include "attn_internal.h"
 #include "common.h"
 
@@ -31,9 +41,8 @@ constexpr int kXcds = 8;
 constexpr int kD = 256;
 constexpr int kTileK = 32;     // keys per tile (two pages)
 constexpr int kRowsW = 16;     // query rows per wave
-constexpr int kWaves = 8;
-constexpr int kTileQ = kRowsW * kWaves;
-constexpr int kThreads = kWaves * 64;
+template <bool DEC> constexpr int waves() { return DEC ? 4 : 8; }
+constexpr int kTileQ = kRowsW * 8;       // prefill rows per workgroup
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLazy = 8.0f;  // rescale only when the max grows by more than 2^8
 
@@ -62,8 +71,16 @@ __device__ __forceinline__ int wide_row(int t) {
 
 }  // namespace
 
-template <int KVDT, int QDT, bool MASK, bool VS>
-__global__ __launch_bounds__(kThreads) void prefill_wide(PrefillArgs a) {
+// Arguments of either mode: prefill (DEC false) or the decode partial.
+template <bool DEC> struct WideArgs;
+template <> struct WideArgs<false> { typedef PrefillArgs T; };
+template <> struct WideArgs<true> { typedef DecodeArgs T; };
+
+template <int KVDT, int QDT, bool MASK, bool VS, bool DEC>
+__global__ __launch_bounds__(waves<DEC>() * 64) void attn_wide(typename WideArgs<DEC>::T a) {
+  constexpr int kWaves = waves<DEC>();
+  constexpr int kThreads = kWaves * 64;
+  static_assert(!(DEC && MASK), "decode takes no block mask");
   constexpr int ELT = DtInfo<KVDT>::bytes;
   constexpr bool F16 = (KVDT == DT_F16) || (is8bit(KVDT) && QDT == DT_F16);
   constexpr int KSTR = kD + 8;            // K LDS row stride (16-bit elements)
@@ -84,44 +101,76 @@ __global__ __launch_bounds__(kThreads) void prefill_wide(PrefillArgs a) {
   __shared__ int list_count[MASK ? kWaves : 1];
   __shared__ __attribute__((aligned(16))) float vs_lds[VS ? kTileK : 4];
 
-  // ---- task: (sequence, KV head) groups dealt to the XCDs, heaviest tile first ----
-  const int x = blockIdx.x;
-  const int xcd = x % kXcds, slot = x / kXcds;
-  const int task_local = slot / a.G, hp = slot % a.G;
-  const int gi = (task_local / a.q_tiles) * kXcds + xcd;
-  const int qt = a.q_tiles - 1 - task_local % a.q_tiles;
-  if (gi >= a.B * a.Hkv) return;
-  const int b = gi / a.Hkv, kvh = gi % a.Hkv;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = kvh * a.G + hp;
-  const int L = min(a.lens[b], a.capacity);
-  const int nq = seq_rows(a.rows_b, b, a.n_q);
-  if (qt * kTileQ >= nq) return;
-  const int off = L - nq;
-  const int q0 = qt * kTileQ + wave * kRowsW;
   const int nl = lane & 15, g = lane >> 4;
-  const int npages = (L + kPage - 1) / kPage;
 
-  const int tile_last = min(qt * kTileQ + kTileQ, nq) - 1;
-  const int wave_last = min(q0 + kRowsW, nq) - 1;
-  const bool wave_has_rows = q0 < nq;
-  const int key_end = min(L, off + tile_last + 1);
-  const int nt = key_end > 0 ? (key_end + kTileK - 1) / kTileK : 0;
-  const int wave_key_end = wave_has_rows ? min(L, off + wave_last + 1) : 0;
-  const int wave_first_pos = off + q0;
-  const int row = q0 + nl;
-  const int pos_row = row < nq ? off + row : -1;
+  // ---- task and the rows of this wave ----
+  // prefill: (sequence, KV head) groups dealt to the XCDs, heaviest tile first;
+  //   the wave owns rows q0 .. q0+15 of query head h, row at position off + row.
+  // decode: one KV partition [k_lo, k_hi) of one (sequence, KV head); the wave
+  //   owns rows 16 wave .. +15 of the group's G.R rows (r -> head r / R, verify
+  //   row r % R at position L - n_b + r % R).
+  int b, kvh, h, L, k_lo, k_hi, pos_row, wave_first_pos, wave_key_end, nt;
+  bool wave_has_rows, row_ok;
+  int64_t q_off;         // element offset of this lane's query row
+  int qt = 0, off = 0, nq = 0, tile_last = 0, part = 0;
+  if constexpr (!DEC) {
+    const int x = blockIdx.x;
+    const int xcd = x % kXcds, slot = x / kXcds;
+    const int task_local = slot / a.G, hp = slot % a.G;
+    const int gi = (task_local / a.q_tiles) * kXcds + xcd;
+    qt = a.q_tiles - 1 - task_local % a.q_tiles;
+    if (gi >= a.B * a.Hkv) return;
+    b = gi / a.Hkv;
+    kvh = gi % a.Hkv;
+    h = kvh * a.G + hp;
+    L = min(a.lens[b], a.capacity);
+    nq = seq_rows(a.rows_b, b, a.n_q);
+    if (qt * kTileQ >= nq) return;
+    off = L - nq;
+    const int q0 = qt * kTileQ + wave * kRowsW;
+    tile_last = min(qt * kTileQ + kTileQ, nq) - 1;
+    const int wave_last = min(q0 + kRowsW, nq) - 1;
+    wave_has_rows = q0 < nq;
+    k_lo = 0;
+    k_hi = min(L, off + tile_last + 1);
+    wave_key_end = wave_has_rows ? min(L, off + wave_last + 1) : 0;
+    wave_first_pos = off + q0;
+    const int row = q0 + nl;
+    row_ok = row < nq;
+    pos_row = row_ok ? off + row : -1;
+    q_off = (int64_t)b * a.q_sb + (int64_t)(row_ok ? row : 0) * a.q_sr + (int64_t)h * a.q_sh;
+  } else {
+    kvh = blockIdx.x;
+    part = blockIdx.y;
+    b = blockIdx.z;
+    L = min(a.lens[b], a.capacity);
+    k_lo = part * a.T;
+    if (k_lo >= L) return;                     // empty partition: never merged
+    k_hi = min(L, k_lo + a.T);
+    const int nrows = seq_rows(a.rows_b, b, a.R);
+    const int r = kRowsW * wave + nl;
+    row_ok = r < a.rows;
+    const int i = row_ok ? r % a.R : 0;
+    h = kvh * a.G + (row_ok ? r / a.R : 0);
+    pos_row = (row_ok && i < nrows) ? L - nrows + i : -1;
+    wave_has_rows = kRowsW * wave < a.rows;
+    // the wave's smallest position (rows are head-major, so any of its first R)
+    wave_first_pos = L - nrows;
+    wave_key_end = k_hi;
+    q_off = (int64_t)b * a.q_sb + (int64_t)i * a.q_sr + (int64_t)h * a.q_sh;
+  }
+  const int key_end = k_hi;
+  nt = key_end > k_lo ? (key_end - k_lo + kTileK - 1) / kTileK : 0;
+  const int npages = (L + kPage - 1) / kPage;
 
   // ---- Q^T fragments: B[k = d][n = row]; lane (row nl, d 32c + 8g .. +8) ----
   u32x4 qf[kD / 32];
   {
-    const bool ok = row < nq;
-    const char *qrow = reinterpret_cast<const char *>(a.q) +
-                       ((int64_t)b * a.q_sb + (int64_t)(ok ? row : 0) * a.q_sr +
-                        (int64_t)h * a.q_sh) * 2;
+    const bool ok = row_ok;
+    const char *qrow = reinterpret_cast<const char *>(a.q) + q_off * 2;
 #pragma unroll
     for (int c = 0; c < kD / 32; ++c) {
       const u32x4 v = ld16(qrow + (32 * c + 8 * g) * 2);
@@ -139,10 +188,11 @@ __global__ __launch_bounds__(kThreads) void prefill_wide(PrefillArgs a) {
   const char *kbase = reinterpret_cast<const char *>(a.k) + k_head;
   const char *vbase = reinterpret_cast<const char *>(a.v) + v_head;
   const int64_t k_page_bytes = a.k_sp * ELT, v_page_bytes = a.v_sp * ELT;
-  const int mh = (MASK && a.mask_heads != 1) ? kvh : 0;
-  const uint8_t *mrow = MASK ? a.mask + ((int64_t)b * a.mask_heads + mh) *
-                                          (int64_t)a.mask_nqb * a.mask_nkb
-                             : nullptr;
+  const uint8_t *mrow = nullptr;
+  if constexpr (MASK) {
+    const int mh = a.mask_heads != 1 ? kvh : 0;
+    mrow = a.mask + ((int64_t)b * a.mask_heads + mh) * (int64_t)a.mask_nqb * a.mask_nkb;
+  }
 
   // ---- staging: each wave's 64 consecutive chunks of a K or V tile lie in
   // one page; page bases are wave-uniform, per-thread offsets fixed ----
@@ -170,10 +220,12 @@ __global__ __launch_bounds__(kThreads) void prefill_wide(PrefillArgs a) {
   float vsr = 0.f;     // V scale of key `tid` of the tile (threads < 32)
   const float *ks_head = VS ? a.k_vs + (int64_t)kvh * a.vs_sh : nullptr;
   const float *vs_head = VS ? a.v_vs + (int64_t)kvh * a.vs_sh : nullptr;
+  // tile t covers keys k_lo + 32 t .. +31 (k_lo is a multiple of 32)
+  const int pg_lo = k_lo / kPage;
   auto gload = [&](int t) {
     t = __builtin_amdgcn_readfirstlane(t);
-    const int pid0 = pt[min(2 * t, npages - 1)];
-    const int pid1 = pt[min(2 * t + 1, npages - 1)];
+    const int pid0 = pt[min(pg_lo + 2 * t, npages - 1)];
+    const int pid1 = pt[min(pg_lo + 2 * t + 1, npages - 1)];
 #pragma unroll
     for (int c = 0; c < KPT; ++c) {
       const int pk = __builtin_amdgcn_readfirstlane(k_pg[c] == 0 ? pid0 : pid1);
@@ -189,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wide(PrefillArgs a) {
     }
   };
   auto lstore = [&](int t, int buf) {
-    const int kbase_tok = t * kTileK;
+    const int kbase_tok = k_lo + t * kTileK;
     const bool tail = kbase_tok + kTileK > L;   // V slots at or past the end: zero them
     if constexpr (VS) {
       if (tid < kTileK) vs_lds[tid] = vsr;
@@ -262,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wide(PrefillArgs a) {
   // ---- per-tile work of one wave ----
   const float sc = a.score_scale;
   auto compute = [&](int t, int buf) {
-    const int kt0 = t * kTileK;
+    const int kt0 = k_lo + t * kTileK;
     if (!wave_has_rows || kt0 >= wave_key_end) return;
     bool keep = true;
     if constexpr (MASK) {
@@ -289,11 +341,11 @@ __global__ __launch_bounds__(kThreads) void prefill_wide(PrefillArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = s[e >> 2][e & 3];
 
-    const bool diag = (kt0 + kTileK - 1 > wave_first_pos) || (kt0 + kTileK > L);
+    const bool diag = (kt0 + kTileK - 1 > wave_first_pos) || (kt0 + kTileK > key_end);
     bool need_mask = diag;
     if constexpr (MASK) need_mask = need_mask || __builtin_amdgcn_ballot_w64(!keep) != 0;
     if (need_mask) {
-      const int lim = keep ? min(pos_row, L - 1) : -1;
+      const int lim = keep ? min(pos_row, key_end - 1) : -1;
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = (kt0 + 8 * g + e <= lim) ? x[e] : kNegInf;
     }
@@ -348,7 +400,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wide(PrefillArgs a) {
         if (t + 1 < nt) lstore(t + 1, buf ^ 1);
         __syncthreads();
       }
-    } else {
+    } else if constexpr (MASK) {
       const int first_row = qt * kTileQ;
       const int qb_lo = max(0, off + first_row) / a.mask_block;
       const int qb_hi = max(0, off + tile_last) / a.mask_block;
@@ -395,10 +447,26 @@ __global__ __launch_bounds__(kThreads) void prefill_wide(PrefillArgs a) {
     }
   }
 
-  // ---- epilogue: sink, normalisation, output ----
   if (!wave_has_rows) return;
-  const float sink = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
   const float l = sum_xor32(sum_xor16(l_run));
+  if constexpr (DEC) {
+    // ---- decode: this partition's unnormalised output, max and sum ----
+    if (!row_ok) return;
+    const int r = kRowsW * wave + nl;
+    const int64_t slot_i = (((int64_t)b * a.Hkv + kvh) * a.rows + r) * a.P + part;
+    float *wo = a.ws_o + slot_i * kD;
+#pragma unroll
+    for (int db = 0; db < kD / 16; ++db)
+      *reinterpret_cast<f32x4 *>(wo + 16 * db + 4 * g) = oacc[db];
+    if (g == 0) {
+      a.ws_ml[slot_i * 2 + 0] = m_run;
+      a.ws_ml[slot_i * 2 + 1] = l;
+    }
+    return;
+  } else {
+  // ---- epilogue: sink, normalisation, output ----
+  const int row = qt * kTileQ + wave * kRowsW + nl;
+  const float sink = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
   const float M = __builtin_fmaxf(m_run, sink);
   float scale_o = 0.f, lse = kNegInf;
   if (M != kNegInf) {
@@ -427,37 +495,88 @@ __global__ __launch_bounds__(kThreads) void prefill_wide(PrefillArgs a) {
     }
     if (a.lse && g == 0) a.lse[((int64_t)b * a.Hq + h) * a.n_q + row] = lse;
   }
+  }
 }
 
 namespace {
 
 template <int KV, int QD, bool VS>
 hipError_t wide_m(const PrefillArgs &a, hipStream_t s) {
+  constexpr int NT = waves<false>() * 64;
   if (a.mask)
-    hipLaunchKernelGGL((prefill_wide<KV, QD, true, VS>), dim3(a.num_wg), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_wide<KV, QD, true, VS, false>), dim3(a.num_wg), dim3(NT), 0, s, a);
   else
-    hipLaunchKernelGGL((prefill_wide<KV, QD, false, VS>), dim3(a.num_wg), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_wide<KV, QD, false, VS, false>), dim3(a.num_wg), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
-template <int KV>
-hipError_t wide_8(const PrefillArgs &a, hipStream_t s) {
+template <int KV, int QD, bool VS>
+hipError_t wide_dec(const DecodeArgs &a, hipStream_t s) {
+  constexpr int NT = waves<true>() * 64;
+  hipLaunchKernelGGL((attn_wide<KV, QD, false, VS, true>), dim3(a.Hkv, a.P, a.B), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+// dtype dispatch shared by both modes: f(KV, QD, VS) as integral constants
+template <int KV, typename F>
+hipError_t wide_dispatch8(bool vs, int qd, F &&f) {
+  using K = std::integral_constant<int, KV>;
+  using QB = std::integral_constant<int, DT_BF16>;
+  using QF = std::integral_constant<int, DT_F16>;
+  if (qd == DT_BF16) return vs ? f(K{}, QB{}, std::true_type{}) : f(K{}, QB{}, std::false_type{});
+  return vs ? f(K{}, QF{}, std::true_type{}) : f(K{}, QF{}, std::false_type{});
+}
+
+template <typename Args, typename F>
+hipError_t wide_dispatch(const Args &a, F &&f) {
+  using B16 = std::integral_constant<int, DT_BF16>;
+  using H16 = std::integral_constant<int, DT_F16>;
   const bool vs = a.k_vs != nullptr;
-  if (a.q_dtype == DT_BF16) return vs ? wide_m<KV, DT_BF16, true>(a, s) : wide_m<KV, DT_BF16, false>(a, s);
-  return vs ? wide_m<KV, DT_F16, true>(a, s) : wide_m<KV, DT_F16, false>(a, s);
+  switch (a.kv_dtype) {
+    case DT_BF16: return f(B16{}, B16{}, std::false_type{});
+    case DT_F16: return f(H16{}, H16{}, std::false_type{});
+    case DT_FP8: return wide_dispatch8<DT_FP8>(vs, a.q_dtype, f);
+    default: return wide_dispatch8<DT_BF8>(vs, a.q_dtype, f);
+  }
 }
 
 }  // namespace
 
-int prefill_wide_rows_per_wg() { return kTileQ; }
-
 hipError_t launch_prefill_wide(const PrefillArgs &a, hipStream_t s) {
-  switch (a.kv_dtype) {
-    case DT_BF16: return wide_m<DT_BF16, DT_BF16, false>(a, s);
-    case DT_F16: return wide_m<DT_F16, DT_F16, false>(a, s);
-    case DT_FP8: return wide_8<DT_FP8>(a, s);
-    default: return wide_8<DT_BF8>(a, s);
-  }
+  return wide_dispatch(a, [&](auto kv, auto qd, auto vs) {
+    return wide_m<decltype(kv)::value, decltype(qd)::value, decltype(vs)::value>(a, s);
+  });
+}
+
+hipError_t launch_decode_wide(const DecodeArgs &a, hipStream_t s) {
+  return wide_dispatch(a, [&](auto kv, auto qd, auto vs) {
+    return wide_dec<decltype(kv)::value, decltype(qd)::value, decltype(vs)::value>(a, s);
+  });
+}
+
+int decode_wide_blocks_per_cu(int kv, int qd, bool vs) {
+  int n = 0;
+  DecodeArgs dummy{};
+  dummy.kv_dtype = kv;
+  dummy.q_dtype = qd;
+  dummy.k_vs = vs ? reinterpret_cast<const float *>(16) : nullptr;
+  wide_dispatch(dummy, [&](auto kvc, auto qdc, auto vsc) {
+    constexpr int KV = decltype(kvc)::value, QD = decltype(qdc)::value;
+    constexpr bool VS = decltype(vsc)::value;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_wide<KV, QD, false, VS, true>,
+                                                     waves<true>() * 64, 0) != hipSuccess)
+      n = 1;
+    return hipSuccess;
+  });
+  return n > 0 ? n : 1;
+}
+
+bool decode_wide_supported(int kv, int qd, int D, int rows) {
+  if (D != 256 || rows > 4 * kRowsW) return false;
+  if (kv == DT_BF16) return qd == DT_BF16;
+  if (kv == DT_F16) return qd == DT_F16;
+  if (is8bit(kv)) return qd == DT_BF16 || qd == DT_F16;
+  return false;
 }
 
 }  // namespace pa

@@ -108,6 +108,8 @@ CASES = [
     ("f32_r1", dict(kind="d", B=2, Hq=8, Hkv=2, d=128, lens=[300, 700], R=1, dt=DT_F32), 4),
     ("fp8vs_r4", dict(kind="d", B=2, Hq=32, Hkv=8, d=128, lens=[1500, 777], R=4, dt=DT_FP8, vs=True), 3),
     ("bf8_r1_d256", dict(kind="d", B=2, Hq=8, Hkv=2, d=256, lens=[700, 45], R=1, dt=DT_BF8), 1),
+    ("fp8vs_r4_d256_wide", dict(kind="d", B=2, Hq=8, Hkv=2, d=256, lens=[700, 45], R=4, dt=DT_FP8, vs=True), 2),
+    ("prefill_bf16_d256", dict(kind="p", B=1, Hq=4, Hkv=2, d=256, S=200, dt=DT_BF16), 3),
     ("prefill_bf16_d64", dict(kind="p", B=2, Hq=8, Hkv=2, d=64, S=300, dt=DT_BF16), 2),
     ("prefill_fp8vs_d128", dict(kind="p", B=1, Hq=8, Hkv=2, d=128, S=333, dt=DT_FP8, vs=True), 5),
     ("sparse_bf8_d128", dict(kind="s", B=1, Hq=8, Hkv=2, d=128, S=1100, dt=DT_BF8), 3),

@@ -11,7 +11,7 @@ import torch
 import oracle
 import paged_gqa_attention_amd as pa
 import synth
-from synth import DT_BF16, DT_F16, DT_F32, DT_FP8
+from synth import DT_BF16, DT_BF8, DT_F16, DT_F32, DT_FP8
 
 pytestmark = pytest.mark.gpu
 
@@ -414,6 +414,19 @@ def test_prefill_ragged_rows_d256(masked):
     check_full(p, o, lse)
 
 
+@pytest.mark.parametrize("d,Hq,Hkv,S", [(64, 8, 2, 300), (256, 4, 2, 200)])
+def test_prefill_replay_deterministic(d, Hq, Hkv, S):
+    """Repeated calls give the same bits (a VALU read of an unfinished MFMA
+    result would not)."""
+    _say(f"prefill replay d={d}")
+    p = synth.make_prefill(98, 1, Hq, Hkv, d, S, sinks=True)
+    dev = Dev(p)
+    o0, l0 = run(dev)
+    for _ in range(4):
+        o1, l1 = run(dev)
+        assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
 def test_prefill_d256_row_matches_decode():
     """A prefill row at head_dim 256 equals the single-row decode at its position."""
     _say("prefill d256 row = decode")
@@ -432,10 +445,12 @@ def test_prefill_d256_row_matches_decode():
 # ---------------------------------------------------------------- head_dim 256 (decode)
 
 @pytest.mark.parametrize("kv_dtype,R,G", [
-    (DT_BF16, 1, 4),      # 4 rows per KV head
-    (DT_F16, 2, 4),       # 8 rows
-    (DT_FP8, 4, 4),       # 16 rows: the VALU kernel in two blocks of 8
-    (DT_BF16, 8, 6),      # 48 rows: six blocks
+    (DT_BF16, 1, 4),      # 4 rows per KV head: the VALU kernel
+    (DT_F16, 2, 4),       # 8 rows: the VALU kernel
+    (DT_FP8, 4, 4),       # 16 rows: the wide MFMA kernel, one wave of rows
+    (DT_BF16, 8, 6),      # 48 rows: three waves
+    (DT_F16, 8, 8),       # 64 rows: four waves
+    (DT_BF16, 3, 3),      # 9 rows: one partly filled wave
 ])
 def test_decode_head_dim_256(kv_dtype, R, G):
     _say(f"d256 decode kv={kv_dtype} R={R} G={G}")
@@ -445,6 +460,18 @@ def test_decode_head_dim_256(kv_dtype, R, G):
     check_full(p, o, lse)
     o2, _ = run(Dev(p), num_splits=7)
     check_full(p, o2, None)
+
+
+@pytest.mark.parametrize("kv_dtype,R,rps", [(DT_BF16, 4, [4, 1, 0]), (DT_BF8, 8, [8, 3, 6])])
+def test_decode_head_dim_256_ragged(kv_dtype, R, rps):
+    """Ragged verify rows on the wide kernel (16 and 32 rows per KV head)."""
+    _say(f"d256 ragged kv={kv_dtype} R={R} rps={rps}")
+    p = synth.make_decode(97, 3, 8, 2, 256, [900, 300, 1700], R, kv_dtype=kv_dtype, sinks=True,
+                          rows_per_seq=rps)
+    o, lse = run(Dev(p))
+    check_full(p, o, lse)
+    o2, l2 = run(Dev(p), num_splits=5)
+    check_full(p, o2, l2)
 
 
 def test_gather_head_dim_256():
