@@ -278,8 +278,8 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
     vp += lane * 16;
 #pragma unroll
     for (int c = 0; c < NL; ++c) {
-      kd[c] = ld16(kp + c * 64);
-      vd[c] = ld16(vp + c * 1024);
+      kd[c] = ld16_nt(kp + c * 64);       // streamed once: non-temporal
+      vd[c] = ld16_nt(vp + c * 1024);
     }
     if constexpr (VS) {
       ksd = ksbase[pid * a.vs_sp];
@@ -618,7 +618,7 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
 #pragma unroll
       for (int u = 0; u < KL; ++u) {
         const int d0 = is8bit(KVDT) ? 64 * u + 16 * j : dchunk<KVDT>(u, j);
-        kd[aa][u] = ld16(kp + d0 * ELT);
+        kd[aa][u] = ld16_nt(kp + d0 * ELT);   // streamed once: non-temporal
       }
     }
     const int64_t pidv = (j >> 1) ? pid1 : pid0;
@@ -626,8 +626,8 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const char *row = vp + (int64_t)(16 * mb + n) * 16 * ELT;
-      if constexpr (is8bit(KVDT)) vd8[mb] = ld8(row);
-      else vd16[mb] = ld16(row);
+      if constexpr (is8bit(KVDT)) vd8[mb] = ld8_nt(row);
+      else vd16[mb] = ld16_nt(row);
     }
     if constexpr (VS) {
       const int64_t so = pidv * a.vs_sp + (int64_t)kvh * a.vs_sh + 8 * (j & 1);

@@ -232,8 +232,10 @@ __global__ __launch_bounds__(waves<DEC>() * 64) void attn_wide(typename WideArgs
       const int pv = __builtin_amdgcn_readfirstlane(v_pg[c] == 0 ? pid0 : pid1);
       const char *kpage = page_addr(kbase, a.k_frag, a.frag_shift, pk, k_page_bytes, k_head);
       const char *vpage = page_addr(vbase, a.v_frag, a.frag_shift, pv, v_page_bytes, v_head);
-      kreg[c] = ld16(kpage + k_goff[c]);
-      vreg[c] = ld16(vpage + v_goff[c]);
+      // decode streams each tile once (non-temporal); prefill tiles are
+      // re-read by the other heads' workgroups through L2
+      kreg[c] = DEC ? ld16_nt(kpage + k_goff[c]) : ld16(kpage + k_goff[c]);
+      vreg[c] = DEC ? ld16_nt(vpage + v_goff[c]) : ld16(vpage + v_goff[c]);
       if constexpr (VS) ksr[c] = ks_head[(int64_t)pk * a.vs_sp + k_slot[c]];
     }
     if constexpr (VS) {

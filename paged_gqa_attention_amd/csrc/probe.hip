@@ -1,8 +1,9 @@
 // Read-only HBM probes: the practical read ceiling that the decode kernels are
 // compared with.  Pattern 0 streams a buffer contiguously; pattern 1 reads
 // whole 4 KiB tiles in a caller-given order, the access pattern of a paged
-// K/V cache whose (page, head) tiles are scattered over the pool.  Every
-// load's data feeds a data-dependent store, so no load can be removed.
+// K/V cache whose (page, head) tiles are scattered over the pool.  Both use
+// non-temporal loads, as the decode kernels do for their once-read K/V.
+// Every load's data feeds a data-dependent store, so no load can be removed.
 #include "attn_internal.h"
 #include "common.h"
 
@@ -20,10 +21,11 @@ __global__ __launch_bounds__(kProbeThreads) void probe_contig(const u32x4 *src, 
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
+    const u32x4 v0 = ld16_nt(src + i), v1 = ld16_nt(src + i + stride);
+    const u32x4 v2 = ld16_nt(src + i + 2 * stride), v3 = ld16_nt(src + i + 3 * stride);
     acc ^= v0 ^ v1 ^ v2 ^ v3;
   }
-  for (; i < n16; i += stride) acc ^= src[i];
+  for (; i < n16; i += stride) acc ^= ld16_nt(src + i);
   const uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
   if (x == kNever) *sink = x;
 }
@@ -43,7 +45,7 @@ __global__ __launch_bounds__(kProbeThreads) void probe_tiles(const char *pool, c
     for (int d = 0; d < kDepth; ++d) {
       const char *a = pool + (size_t)order[t + d * nwaves] * 4096 + lane * 16;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) v[d][c] = *reinterpret_cast<const u32x4 *>(a + c * 1024);
+      for (int c = 0; c < 4; ++c) v[d][c] = ld16_nt(a + c * 1024);
     }
 #pragma unroll
     for (int d = 0; d < kDepth; ++d)
@@ -53,7 +55,7 @@ __global__ __launch_bounds__(kProbeThreads) void probe_tiles(const char *pool, c
   for (; t < ntiles; t += nwaves) {
     const char *a = pool + (size_t)order[t] * 4096 + lane * 16;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc ^= *reinterpret_cast<const u32x4 *>(a + c * 1024);
+    for (int c = 0; c < 4; ++c) acc ^= ld16_nt(a + c * 1024);
   }
   const uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
   if (x == kNever) *sink = x;
