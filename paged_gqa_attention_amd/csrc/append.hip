@@ -135,16 +135,16 @@ __device__ __forceinline__ float vector_scale(const float *x) {
 template <int KVDT>
 __device__ __forceinline__ void store8(char *p, const uint32_t *c) {
   if constexpr (KVDT == DT_F32) {
-    *reinterpret_cast<u32x4 *>(p) = u32x4{c[0], c[1], c[2], c[3]};
-    *reinterpret_cast<u32x4 *>(p + 16) = u32x4{c[4], c[5], c[6], c[7]};
+    gstore<u32x4>(p, u32x4{c[0], c[1], c[2], c[3]});
+    gstore<u32x4>(p + 16, u32x4{c[4], c[5], c[6], c[7]});
   } else if constexpr (is8bit(KVDT)) {
     u32x2 w;
     w[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
     w[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-    *reinterpret_cast<u32x2 *>(p) = w;
+    gstore<u32x2>(p, w);
   } else {
-    *reinterpret_cast<u32x4 *>(p) = u32x4{c[0] | (c[1] << 16), c[2] | (c[3] << 16),
-                                          c[4] | (c[5] << 16), c[6] | (c[7] << 16)};
+    gstore<u32x4>(p, u32x4{c[0] | (c[1] << 16), c[2] | (c[3] << 16),
+                           c[4] | (c[5] << 16), c[6] | (c[7] << 16)});
   }
 }
 
@@ -152,24 +152,24 @@ __device__ __forceinline__ void store8(char *p, const uint32_t *c) {
 template <int KVDT>
 __device__ __forceinline__ void store_vec(char *p, const uint32_t *c) {
   if constexpr (KVDT == DT_F32) {
-    *reinterpret_cast<u32x4 *>(p) = u32x4{c[0], c[1], c[2], c[3]};
+    gstore<u32x4>(p, u32x4{c[0], c[1], c[2], c[3]});
   } else if constexpr (is8bit(KVDT)) {
     u32x4 w;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       w[q] = c[4 * q] | (c[4 * q + 1] << 8) | (c[4 * q + 2] << 16) | (c[4 * q + 3] << 24);
-    *reinterpret_cast<u32x4 *>(p) = w;
+    gstore<u32x4>(p, w);
   } else {
-    *reinterpret_cast<u32x4 *>(p) = u32x4{c[0] | (c[1] << 16), c[2] | (c[3] << 16),
-                                          c[4] | (c[5] << 16), c[6] | (c[7] << 16)};
+    gstore<u32x4>(p, u32x4{c[0] | (c[1] << 16), c[2] | (c[3] << 16),
+                           c[4] | (c[5] << 16), c[6] | (c[7] << 16)});
   }
 }
 
 template <int KVDT>
 __device__ __forceinline__ void store1(char *p, uint32_t c) {
-  if constexpr (KVDT == DT_F32) *reinterpret_cast<uint32_t *>(p) = c;
-  else if constexpr (is8bit(KVDT)) *reinterpret_cast<uint8_t *>(p) = (uint8_t)c;
-  else *reinterpret_cast<uint16_t *>(p) = (uint16_t)c;
+  if constexpr (KVDT == DT_F32) gstore<uint32_t>(p, c);
+  else if constexpr (is8bit(KVDT)) gstore<uint8_t>(p, (uint8_t)c);
+  else gstore<uint16_t>(p, (uint16_t)c);
 }
 
 template <int KVDT, int SRC, int D, bool VS>

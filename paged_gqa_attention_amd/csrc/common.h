@@ -34,21 +34,33 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kPage = 16;
 
 // ---- 16-byte global loads ------------------------------------------------------
+// The pointers are cast to the global address space: a pointer built from a
+// fragment table entry is otherwise generic, and generic (flat) loads also
+// count on the LDS counter, so every wait for an LDS read would wait for
+// them too.
+
+typedef const __attribute__((address_space(1))) u32x4 gu32x4;
+typedef const __attribute__((address_space(1))) u32x2 gu32x2;
 
 __device__ __forceinline__ u32x4 ld16(const void *p) {
-  return *reinterpret_cast<const u32x4 *>(p);
+  return *(gu32x4 *)p;
 }
 __device__ __forceinline__ u32x2 ld8(const void *p) {
-  return *reinterpret_cast<const u32x2 *>(p);
+  return *(gu32x2 *)p;
+}
+// a store through a global address space pointer (not a flat store)
+template <typename T>
+__device__ __forceinline__ void gstore(void *p, T v) {
+  *(__attribute__((address_space(1))) T *)p = v;
 }
 // Non-temporal loads, for data a kernel reads exactly once (the K/V a decode
 // partition streams): they do not allocate in the caches, which measured
 // 6.1 against 5.4 TB/s for the paged decode stream on MI355X.
 __device__ __forceinline__ u32x4 ld16_nt(const void *p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return __builtin_nontemporal_load((gu32x4 *)p);
 }
 __device__ __forceinline__ u32x2 ld8_nt(const void *p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+  return __builtin_nontemporal_load((gu32x2 *)p);
 }
 
 // ---- page addressing ---------------------------------------------------------------
