@@ -102,8 +102,9 @@ def test_plan_headline_decode(hctx):
     io, kv, op = _decode_args(B=16, R=1, Hq=32, Hkv=8, d=128, stride=1024)
     P, T, W = pa.attn_paged_decode_plan(hctx, io, kv, op)
     assert P * T >= 1024 * 16 and T % 128 == 0
-    # one round of two partial workgroups per CU (the VALU path's planning target)
-    assert 16 * 8 * P <= 2 * 256 and 16 * 8 * (P + 1) > 2 * 256
+    # the VALU path: at least one round of two partial workgroups per CU, and
+    # partitions of at most 1,024 tokens (16 per sequence at a 16K capacity)
+    assert 16 * 8 * P >= 2 * 256 and T <= 1024 and P == 16
     assert W >= 16 * 8 * 4 * P * (128 + 2) * 4
 
 
