@@ -580,14 +580,16 @@ def extra(ctx, args):
     import synth
     from paged_gqa_attention_amd import accounting as acc
     dev = "cuda"
-    for R in (1, 4, 8):
-        p = synth.config2(q_rows=R, device=dev)
-        call, (P, T), keep = decode_setup(ctx, p, dev)
-        ms = time_calls(call, args.steps, args.warmup)
-        b = acc.decode_bytes(p.seq_lens.tolist(), R, 32, 8, 128, 2, 2, 2)
-        print(json.dumps({"workload": f"decode/verify B=16 L~U[8K,16K] R={R}", "ms": round(ms, 4),
-                          "GB/s": round(b / ms / 1e6, 1), "splits": P}), file=sys.stderr, flush=True)
-        del keep, call, p
+    for lens, tag in ((None, "L~U[8K,16K]"), ([16384] * 16, "L=16384")):
+        for R in (1, 4, 8):
+            p = synth.config2(q_rows=R, lens=lens, device=dev)
+            call, (P, T), keep = decode_setup(ctx, p, dev)
+            ms = time_calls(call, args.steps, args.warmup)
+            b = acc.decode_bytes(p.seq_lens.tolist(), R, 32, 8, 128, 2, 2, 2)
+            print(json.dumps({"workload": f"decode/verify B=16 {tag} R={R}", "ms": round(ms, 4),
+                              "GB/s": round(b / ms / 1e6, 1), "splits": P}), file=sys.stderr,
+                  flush=True)
+            del keep, call, p
     p = synth.config3(device=dev)
     call, (P, T), keep = decode_setup(ctx, p, dev)
     ms = time_calls(call, args.steps, args.warmup)
