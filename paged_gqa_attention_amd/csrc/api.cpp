@@ -195,7 +195,9 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
   // kernel then cuts further, to partitions of at most kValuTAuto tokens.
   const int64_t cap = (int64_t)kv->page_table_stride * kPage;
   const int rows_per_wg = (pl->mfma || pl->wide) ? rows : pl->rb;
-  const int64_t tmin = round_up(std::max<int64_t>(256, 64 * (int64_t)rows_per_wg), kTGran);
+  // at least 32 tokens per row of a workgroup: a partition's FP32 partials (written
+  // once, read back by the merge) stay within 1/16 of its K/V bytes at 16-bit K/V
+  const int64_t tmin = round_up(std::max<int64_t>(256, 32 * (int64_t)rows_per_wg), kTGran);
   int64_t T;
   if (opts->num_splits > 0) {
     T = round_up(ceil_div(cap, opts->num_splits), kTGran);
