@@ -108,6 +108,15 @@ def test_plan_headline_decode(hctx):
     assert W >= 16 * 8 * 4 * P * (128 + 2) * 4
 
 
+def test_plan_few_groups_fill_the_cus(hctx):
+    # one KV head of the headline at R=8: 16 groups of 32 rows (the MFMA path at
+    # one workgroup per CU) -> 16 partitions of 1,024 tokens (32 per row), so
+    # 256 partial workgroups; a floor of 64 tokens per row would give 128
+    io, kv, op = _decode_args(B=16, R=8, Hq=4, Hkv=1, d=128, stride=1024)
+    P, T, W = pa.attn_paged_decode_plan(hctx, io, kv, op)
+    assert (P, T) == (16, 1024) and 16 * P == 256
+
+
 def test_plan_forced_splits(hctx):
     io, kv, op = _decode_args(stride=64)
     op.num_splits = 3
