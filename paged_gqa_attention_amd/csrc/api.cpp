@@ -183,7 +183,7 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
     pl->row_blocks = (int)ceil_div(rows, pl->rb);
   }
   // LDS the partial kernel needs for its rows (merge buffer + softmax state)
-  const size_t lds = pl->wide ? (size_t)2 * 32 * (256 + 8) * 2 + (size_t)2 * 256 * (32 + 8) * 2 + 128
+  const size_t lds = pl->wide ? (size_t)2 * 32 * (256 + 16) * 2 + (size_t)2 * 256 * 32 * 2 + 128
                  : pl->mfma ? (size_t)round_up(rows, 16) * (D + 4) * 4 + 2 * 4 * 64 * 4
                             : (size_t)pl->rb * D * 4 + 4 * 16 * pl->rb * 4 + 3 * 4 * pl->rb * 4;
   if (lds > ctx->lds_per_block)

@@ -83,10 +83,14 @@ __global__ __launch_bounds__(waves<DEC>() * 64) void attn_wide(typename WideArgs
   static_assert(!(DEC && MASK), "decode takes no block mask");
   constexpr int ELT = DtInfo<KVDT>::bytes;
   constexpr bool F16 = (KVDT == DT_F16) || (is8bit(KVDT) && QDT == DT_F16);
-  constexpr int KSTR = kD + 8;            // K LDS row stride (16-bit elements)
-  constexpr int VSTR = kTileK + 8;        // V^T LDS row stride
+  // The 32 lanes an LDS read serves together (16 rows x 2 chunks of an MFMA
+  // operand) must hit 32 distinct 16-byte chunks of the 512-byte bank window:
+  // K rows are padded to 544 bytes (32 mod 512); V^T rows are unpadded and
+  // chunk j of row d sits at j ^ (2 ((d / 8) mod 2)), which keeps pairs
+  // (2i, 2i + 1) adjacent.
+  constexpr int KSTR = kD + 16;           // K LDS row stride (16-bit elements)
   constexpr int KBUF = kTileK * KSTR;
-  constexpr int VBUF = kD * VSTR;
+  constexpr int VBUF = kD * kTileK;
   constexpr int CPK = kD * ELT / 16;      // 16-byte chunks per stored K row
   constexpr int KCH = kTileK * CPK;       // chunks per K tile (= per V tile)
   constexpr int KPT = KCH / kThreads;     // chunks per thread (exact)
@@ -211,7 +215,8 @@ __global__ __launch_bounds__(waves<DEC>() * 64) void attn_wide(typename WideArgs
     const int d = cc / ELT, tg = cc % ELT;          // value row, token group
     v_pg[c] = __builtin_amdgcn_readfirstlane(vpg);
     v_goff[c] = (uint32_t)(cc * 16);
-    v_loff[c] = (uint32_t)(d * VSTR + 16 * vpg + tg * EPC);
+    const int vj = (16 * vpg + tg * EPC) / 8;
+    v_loff[c] = (uint32_t)(d * kTileK + ((vj ^ (((d >> 3) & 1) << 1)) << 3));
     v_tok0[c] = 16 * vpg + tg * EPC;
   }
 
@@ -384,7 +389,7 @@ __global__ __launch_bounds__(waves<DEC>() * 64) void attn_wide(typename WideArgs
     // O^T[db] += V^T[16 value rows, 32 keys] P^T[32 keys, 16 rows]
 #pragma unroll
     for (int db = 0; db < kD / 16; ++db) {
-      const u32x4 va = *reinterpret_cast<const u32x4 *>(vl + (16 * db + nl) * VSTR + 8 * g);
+      const u32x4 va = *reinterpret_cast<const u32x4 *>(vl + (16 * db + nl) * kTileK + ((g ^ (((nl >> 3) & 1) << 1)) << 3));
       oacc[db] = mfma16<F16>(va, pf, oacc[db]);
     }
   };
