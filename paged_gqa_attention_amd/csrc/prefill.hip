@@ -3,8 +3,9 @@
 //
 // A workgroup owns a 128-row query tile of HPW (1 or 2) query heads of one
 // KV group; each wave owns 32 rows of one head.  64-key K/V tiles are
-// gathered through the page table into LDS (double buffered) and shared by
-// all waves.  Per wave and tile:
+// gathered through the page table into LDS (two tiles staged per barrier,
+// into one pair of buffers while the other pair is read; one tile per
+// barrier with a block mask) and shared by all waves.  Per wave and tile:
 //     S^T = K Q^T        (32x32x16 MFMA, FP32 accumulators)
 //     online softmax     (FP32, one row per lane column, lazy rescaling)
 //     O^T += V^T P^T     (P rounded to the MFMA operand type)
@@ -85,10 +86,15 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
   constexpr int EPC = 16 / ELT;         // stored elements per chunk
   constexpr int LIST = 1024;            // tiles per mask window
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KBUF];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][VBUF];
+  // LDS buffers: without a block mask the loop stages two tiles per barrier
+  // (two pairs of buffers), with one it stages one (two buffers)
+  constexpr int NBUF = MASK ? 2 : 4;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[NBUF][KBUF];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[NBUF][VBUF];
   __shared__ int tile_list[MASK ? LIST : 1];
-  __shared__ __attribute__((aligned(16))) float vs_lds[VS ? kTileK : 4];   // V scales of a tile
+  // V scales of a tile, one slot per buffer parity (two tiles are staged
+  // between barriers without a block mask)
+  __shared__ __attribute__((aligned(16))) float vs_lds[2][VS ? kTileK : 4];
   __shared__ int list_count[MASK ? NW : 1];
 
   // ---- task of this workgroup ----
@@ -229,9 +235,9 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
     // V slots at or past the end may hold anything: zero them (last tile only)
     const bool tail = kbase_tok + kTileK > L;
     if constexpr (VS) {
-      // V scales -> LDS.  The previous tile's readers are past the loop's
+      // V scales -> LDS.  The previous readers of this slot are past a
       // barrier; this barrier makes the new scales visible to every wave.
-      if (tid < kTileK) vs_lds[tid] = vsr;
+      if (tid < kTileK) vs_lds[buf & 1][tid] = vsr;
       __syncthreads();
     }
 #pragma unroll
@@ -259,7 +265,7 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
           for (int w = 0; w < 4; ++w) {   // word w: tokens 4w .. 4w+3 of the page row
             const f32x2 x0 = e8x2_to_f32<KVDT, false>(vreg[c][w]);
             const f32x2 x1 = e8x2_to_f32<KVDT, true>(vreg[c][w]);
-            const f32x4 sv = *reinterpret_cast<const f32x4 *>(&vs_lds[v_tok0[c] + 4 * w]);
+            const f32x4 sv = *reinterpret_cast<const f32x4 *>(&vs_lds[buf & 1][v_tok0[c] + 4 * w]);
             vv[w >> 1][2 * (w & 1)] = pack16<F16>(x0[0] * sv[0], x0[1] * sv[1]);
             vv[w >> 1][2 * (w & 1) + 1] = pack16<F16>(x1[0] * sv[2], x1[1] * sv[3]);
           }
@@ -401,17 +407,28 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
         }
   };
 
-  // ---- tile loop (double-buffered LDS, one barrier per tile) ----
+  // ---- tile loop (LDS buffers as above; one barrier per two tiles without a
+  // block mask, per tile with one) ----
   if (nt > 0) {
     if constexpr (!MASK) {
+      // two tiles per barrier: tiles t, t + 1 in buffer pair (t & 2), while
+      // t + 2, t + 3 are staged into the other pair, whose last readers
+      // passed the previous barrier (about 2% over one tile per barrier)
       gload(0);
       lstore(0, 0);
+      if (nt > 1) {
+        gload(1);
+        lstore(1, 1);
+      }
       __syncthreads();
-      for (int t = 0; t < nt; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < nt) gload(t + 1);
-        compute(t, buf);
-        if (t + 1 < nt) lstore(t + 1, buf ^ 1);
+      for (int t = 0; t < nt; t += 2) {
+        const int pb = t & 2;
+        if (t + 2 < nt) gload(t + 2);
+        compute(t, pb);
+        if (t + 2 < nt) lstore(t + 2, pb ^ 2);
+        if (t + 3 < nt) gload(t + 3);
+        if (t + 1 < nt) compute(t + 1, pb + 1);
+        if (t + 3 < nt) lstore(t + 3, (pb ^ 2) + 1);
         __syncthreads();
       }
     } else {
