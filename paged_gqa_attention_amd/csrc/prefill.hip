@@ -4,8 +4,8 @@
 // A workgroup owns a 128-row query tile of HPW (1 or 2) query heads of one
 // KV group; each wave owns 32 rows of one head.  64-key K/V tiles are
 // gathered through the page table into LDS (two tiles staged per barrier,
-// into one pair of buffers while the other pair is read; one tile per
-// barrier with a block mask) and shared by all waves.  Per wave and tile:
+// into one pair of buffers while the other pair is read) and shared by all
+// waves.  Per wave and tile:
 //     S^T = K Q^T        (32x32x16 MFMA, FP32 accumulators)
 //     online softmax     (FP32, one row per lane column, lazy rescaling)
 //     O^T += V^T P^T     (P rounded to the MFMA operand type)
@@ -86,14 +86,13 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
   constexpr int EPC = 16 / ELT;         // stored elements per chunk
   constexpr int LIST = 1024;            // tiles per mask window
 
-  // LDS buffers: without a block mask the loop stages two tiles per barrier
-  // (two pairs of buffers), with one it stages one (two buffers)
-  constexpr int NBUF = MASK ? 2 : 4;
+  // LDS buffers: the loop stages two tiles per barrier (two pairs of buffers)
+  constexpr int NBUF = 4;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[NBUF][KBUF];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[NBUF][VBUF];
   __shared__ int tile_list[MASK ? LIST : 1];
   // V scales of a tile, one slot per buffer parity (two tiles are staged
-  // between barriers without a block mask)
+  // between barriers)
   __shared__ __attribute__((aligned(16))) float vs_lds[2][VS ? kTileK : 4];
   __shared__ int list_count[MASK ? NW : 1];
 
@@ -407,8 +406,7 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
         }
   };
 
-  // ---- tile loop (LDS buffers as above; one barrier per two tiles without a
-  // block mask, per tile with one) ----
+  // ---- tile loop (LDS buffers as above; one barrier per two tiles) ----
   if (nt > 0) {
     if constexpr (!MASK) {
       // two tiles per barrier: tiles t, t + 1 in buffer pair (t & 2), while
@@ -463,17 +461,23 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
         }
         const int cnt = base;
         if (cnt == 0) continue;
-        gload(tile_list[0]);
-        lstore(tile_list[0], 0);
+        // the listed tiles, two per barrier as in the unmasked loop
+        auto tl = [&](int i) { return __builtin_amdgcn_readfirstlane(tile_list[i]); };
+        gload(tl(0));
+        lstore(tl(0), 0);
+        if (cnt > 1) {
+          gload(tl(1));
+          lstore(tl(1), 1);
+        }
         __syncthreads();
-        for (int idx = 0; idx < cnt; ++idx) {
-          const int buf = idx & 1;
-          const int t = __builtin_amdgcn_readfirstlane(tile_list[idx]);
-          const bool more = idx + 1 < cnt;
-          const int tn = more ? __builtin_amdgcn_readfirstlane(tile_list[idx + 1]) : 0;
-          if (more) gload(tn);
-          compute(t, buf);
-          if (more) lstore(tn, buf ^ 1);
+        for (int idx = 0; idx < cnt; idx += 2) {
+          const int pb = idx & 2;
+          if (idx + 2 < cnt) gload(tl(idx + 2));
+          compute(tl(idx), pb);
+          if (idx + 2 < cnt) lstore(tl(idx + 2), pb ^ 2);
+          if (idx + 3 < cnt) gload(tl(idx + 3));
+          if (idx + 1 < cnt) compute(tl(idx + 1), pb + 1);
+          if (idx + 3 < cnt) lstore(tl(idx + 3), (pb ^ 2) + 1);
           __syncthreads();
         }
       }
