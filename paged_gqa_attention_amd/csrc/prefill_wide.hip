@@ -99,11 +99,14 @@ __global__ __launch_bounds__(waves<DEC>() * 64) void attn_wide(typename WideArgs
   static_assert(KCH % kThreads == 0, "whole chunks per thread");
   static_assert(64 % CPK == 0 || CPK % 64 == 0, "a wave's K chunks lie in one page");
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KBUF];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][VBUF];
+  // prefill stages two tiles per barrier (two pairs of buffers); decode keeps
+  // one tile per barrier, so that two of its workgroups fit per CU
+  constexpr int NBUF = DEC ? 2 : 4;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[NBUF][KBUF];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[NBUF][VBUF];
   __shared__ int tile_list[MASK ? LIST : 1];
   __shared__ int list_count[MASK ? kWaves : 1];
-  __shared__ __attribute__((aligned(16))) float vs_lds[VS ? kTileK : 4];
+  __shared__ __attribute__((aligned(16))) float vs_lds[2][VS ? kTileK : 4];   // per buffer parity
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -251,7 +254,7 @@ __global__ __launch_bounds__(waves<DEC>() * 64) void attn_wide(typename WideArgs
     const int kbase_tok = k_lo + t * kTileK;
     const bool tail = kbase_tok + kTileK > L;   // V slots at or past the end: zero them
     if constexpr (VS) {
-      if (tid < kTileK) vs_lds[tid] = vsr;
+      if (tid < kTileK) vs_lds[buf & 1][tid] = vsr;
       __syncthreads();
     }
 #pragma unroll
@@ -276,7 +279,7 @@ __global__ __launch_bounds__(waves<DEC>() * 64) void attn_wide(typename WideArgs
         for (int w = 0; w < 4; ++w) {   // word w: tokens 4w .. 4w+3 of the page row
           const f32x2 x0 = e8x2_to_f32<KVDT, false>(vreg[c][w]);
           const f32x2 x1 = e8x2_to_f32<KVDT, true>(vreg[c][w]);
-          const f32x4 sv = *reinterpret_cast<const f32x4 *>(&vs_lds[v_tok0[c] + 4 * w]);
+          const f32x4 sv = *reinterpret_cast<const f32x4 *>(&vs_lds[buf & 1][v_tok0[c] + 4 * w]);
           vv[w >> 1][2 * (w & 1)] = pack16w<F16>(x0[0] * sv[0], x0[1] * sv[1]);
           vv[w >> 1][2 * (w & 1) + 1] = pack16w<F16>(x1[0] * sv[2], x1[1] * sv[3]);
         }
@@ -394,9 +397,32 @@ __global__ __launch_bounds__(waves<DEC>() * 64) void attn_wide(typename WideArgs
     }
   };
 
-  // ---- tile loop (double-buffered LDS, one barrier per tile) ----
+  // ---- tile loop: prefill two tiles per barrier (tiles i, i + 1 read from one
+  // buffer pair while i + 2, i + 3 are staged into the other, whose last
+  // readers passed the previous barrier); decode one tile per barrier ----
+  auto run_pairs = [&](auto tl, int cnt) __attribute__((always_inline)) {
+    gload(tl(0));
+    lstore(tl(0), 0);
+    if (cnt > 1) {
+      gload(tl(1));
+      lstore(tl(1), 1);
+    }
+    __syncthreads();
+    for (int i = 0; i < cnt; i += 2) {
+      const int pb = i & 2;
+      if (i + 2 < cnt) gload(tl(i + 2));
+      compute(tl(i), pb);
+      if (i + 2 < cnt) lstore(tl(i + 2), pb ^ 2);
+      if (i + 3 < cnt) gload(tl(i + 3));
+      if (i + 1 < cnt) compute(tl(i + 1), pb + 1);
+      if (i + 3 < cnt) lstore(tl(i + 3), (pb ^ 2) + 1);
+      __syncthreads();
+    }
+  };
   if (nt > 0) {
-    if constexpr (!MASK) {
+    if constexpr (!MASK && !DEC) {
+      run_pairs([](int i) { return i; }, nt);
+    } else if constexpr (!MASK) {
       gload(0);
       lstore(0, 0);
       __syncthreads();
@@ -437,19 +463,7 @@ __global__ __launch_bounds__(waves<DEC>() * 64) void attn_wide(typename WideArgs
         }
         const int cnt = base;
         if (cnt == 0) continue;
-        gload(tile_list[0]);
-        lstore(tile_list[0], 0);
-        __syncthreads();
-        for (int idx = 0; idx < cnt; ++idx) {
-          const int buf = idx & 1;
-          const int t = __builtin_amdgcn_readfirstlane(tile_list[idx]);
-          const bool more = idx + 1 < cnt;
-          const int tn = more ? __builtin_amdgcn_readfirstlane(tile_list[idx + 1]) : 0;
-          if (more) gload(tn);
-          compute(t, buf);
-          if (more) lstore(tn, buf ^ 1);
-          __syncthreads();
-        }
+        run_pairs([&](int i) { return __builtin_amdgcn_readfirstlane(tile_list[i]); }, cnt);
       }
     }
   }
