@@ -223,6 +223,14 @@ PREFILL_CASES = [
     ("d256_chunked", dict(B=2, Hq=4, Hkv=1, d=256, S=400, q_rows=90, sinks=True)),
     ("d256_tiny", dict(B=2, Hq=4, Hkv=2, d=256, S=5, sinks=True)),
     ("d256_fp32_out", dict(B=1, Hq=4, Hkv=4, d=256, S=140, sinks=False, o=DT_F32)),
+    # tile counts around the two-tiles-per-barrier staging: 1, 2, 3 and 4
+    # 64-key tiles (d 64/128), 3 and 5 32-key tiles (d 256)
+    ("d64_one_tile", dict(B=1, Hq=4, Hkv=2, d=64, S=64, sinks=True)),
+    ("d64_two_tiles", dict(B=1, Hq=4, Hkv=2, d=64, S=128, sinks=True)),
+    ("d64_three_tiles", dict(B=1, Hq=4, Hkv=2, d=64, S=129, sinks=True)),
+    ("d128_four_tiles", dict(B=1, Hq=4, Hkv=2, d=128, S=256, sinks=True)),
+    ("d256_three_tiles", dict(B=1, Hq=4, Hkv=2, d=256, S=96, sinks=True)),
+    ("d256_five_tiles", dict(B=1, Hq=4, Hkv=2, d=256, S=150, sinks=True)),
 ]
 
 
