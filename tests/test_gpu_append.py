@@ -15,7 +15,7 @@ sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
 import oracle  # noqa: E402
 import paged_gqa_attention_amd as pa  # noqa: E402
 import synth  # noqa: E402
-from synth import DT_BF16, DT_F16, DT_F32, DT_FP8  # noqa: E402
+from synth import DT_BF16, DT_BF8, DT_F16, DT_F32, DT_FP8  # noqa: E402
 from helpers import Dev, check_full, ctx, run  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -119,3 +119,48 @@ def test_append_head_dim_256(kv_dtype):
     _, _, got, exp = _append_case(740 + kv_dtype, kv_dtype, DT_F32, 256, [70, 300, 16], 37, 24)
     for gt, ex in zip(got, exp):
         assert np.array_equal(gt, ex)
+
+
+def _encoder_probe_values(kv_dtype) -> np.ndarray:
+    """Every finite code value of the format, the midpoints between neighbours
+    (ties, which go to the even code), the midpoints one FP32 ulp either side,
+    values past the largest finite code, infinities, NaN, zeros and FP32
+    denormals, with both signs."""
+    t = torch.float8_e4m3fn if kv_dtype == DT_FP8 else torch.float8_e5m2
+    v = torch.arange(256, dtype=torch.uint8).view(t).to(torch.float64).numpy()
+    v = np.unique(v[np.isfinite(v) & (v >= 0)])
+    mids = ((v[:-1] + v[1:]) / 2).astype(np.float32)
+    up = np.nextafter(mids, np.float32(np.inf))
+    dn = np.nextafter(mids, np.float32(0))
+    big = np.float32(v[-1])
+    extra = np.array([big * 1.01, big * 1.0625, big * 1.125, big * 1.2, 1e30, np.inf, np.nan,
+                      1e-40, 1e-45, 0.0], dtype=np.float32)
+    pos = np.concatenate([v.astype(np.float32), mids, up, dn, extra])
+    return np.concatenate([pos, -pos]).astype(np.float32)
+
+
+@pytest.mark.parametrize("kv_dtype", [DT_FP8, DT_BF8])
+def test_append_encoder_dense(kv_dtype):
+    """The 8-bit encoders against the oracle's, bit for bit, on every code
+    value, every tie and its neighbours (unit scales, FP32 source rows)."""
+    _say("encoder dense", kv_dtype)
+    vals = _encoder_probe_values(kv_dtype)
+    B, n_new, hkv, d = 2, 24, 2, 64
+    slots = B * n_new * hkv * d
+    assert vals.size <= slots
+    g = np.random.default_rng(kv_dtype)
+    kf = np.resize(vals, slots)
+    vf = np.resize(vals[g.permutation(vals.size)], slots)
+    knew = torch.from_numpy(kf.reshape(B, n_new, hkv, d).copy())
+    vnew = torch.from_numpy(vf.reshape(B, n_new, hkv, d).copy())
+    p = synth.make_decode(750 + kv_dtype, B, 4 * hkv, hkv, d, [40, 24], 1, kv_dtype=kv_dtype,
+                          stride=5)
+    k0, v0 = synth.pool_codes(p.k_pool), synth.pool_codes(p.v_pool)
+    kexp, vexp = oracle.kv_append(kv_dtype, k0, v0, p.page_table.numpy(), p.seq_lens.numpy(),
+                                  knew.numpy(), vnew.numpy(), 1.0, 1.0)
+    dev = Dev(p)
+    kv = pa.make_kv(dev.k, dev.v, dev.pt, dev.lens, 1.0, 1.0)
+    pa.attn_kv_append(ctx(), kv, pa.make_rows(knew.cuda(), vnew.cuda()))
+    torch.cuda.synchronize()
+    assert np.array_equal(synth.pool_codes(dev.k), kexp)
+    assert np.array_equal(synth.pool_codes(dev.v), vexp)
