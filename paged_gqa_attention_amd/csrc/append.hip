@@ -47,38 +47,21 @@ __device__ __forceinline__ uint32_t enc_f16(float y) {
 
 // OCP e4m3fn (bias 7, largest finite 448 = 0x7e), saturating
 __device__ __forceinline__ uint32_t enc_e4m3(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t s = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  if (a > 0x7f800000u) return s | 0x7fu;                   // NaN
-  if (a >= 0x43e00000u) return s | 0x7eu;                  // >= 448 (and inf): saturate
-  if (a >= 0x3c800000u) {                                  // normal: >= 2^-6
-    // round the f32 (exponent, 3 leading mantissa bits) to nearest even;
-    // rebias 127 -> 7: subtract 120 << 3
-    const uint32_t t = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
-    return s | (t - 960u);
-  }
-  // subnormal: multiples of 2^-9 (exact scaling, then round to nearest even)
-  return s | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  // the hardware conversion rounds to nearest even, subnormals included;
+  // finite magnitudes above the largest code (and infinities) are clamped to
+  // it first.  NaN is written as sign | 0x7f (the conversion sets other bits).
+  const float c = __builtin_fabsf(y) > 448.f ? __builtin_copysignf(448.f, y) : y;
+  const uint32_t code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xffu;
+  return y != y ? (((__float_as_uint(y) >> 24) & 0x80u) | 0x7fu) : code;
 }
 
 // OCP e5m2 (bias 15, largest finite 57344 = 0x7b), finite values saturating,
-// infinities kept
+// infinities kept; the same conversion scheme as e4m3fn
 __device__ __forceinline__ uint32_t enc_e5m2(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t s = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  if (a > 0x7f800000u) return s | 0x7fu;                   // NaN
-  if (a == 0x7f800000u) return s | 0x7cu;                  // infinity
-  if (a >= 0x47600000u) return s | 0x7bu;                  // >= 57344: saturate
-  if (a >= 0x38800000u) {                                  // normal: >= 2^-14
-    // round the f32 (exponent, 2 leading mantissa bits) to nearest even;
-    // rebias 127 -> 15: subtract 112 << 2
-    const uint32_t t = (a + 0xfffffu + ((a >> 21) & 1u)) >> 21;
-    return s | (t - 448u);
-  }
-  // subnormal: multiples of 2^-16 (exact scaling, then round to nearest even)
-  return s | (uint32_t)__builtin_rintf(__uint_as_float(a) * 65536.0f);
+  const float a = __builtin_fabsf(y);
+  const float c = (a > 57344.f && a != __builtin_inff()) ? __builtin_copysignf(57344.f, y) : y;
+  const uint32_t code = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c, c, 0, false) & 0xffu;
+  return y != y ? (((__float_as_uint(y) >> 24) & 0x80u) | 0x7fu) : code;
 }
 
 template <int SRC>
