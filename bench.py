@@ -22,7 +22,8 @@ stderr (not part of the JSON line).
 
 ``--only`` runs one workload without the CPU baseline, for profiling under
 rocprofv3 (``copy`` is a 1 GiB device-to-device copy whose counter readings
-calibrate HBM byte counts).  ``--pmc-summary`` turns two rocprofv3 ``--pmc``
+calibrate HBM byte counts; ``append`` and ``d256`` print the ``kv_append`` and
+``head_dim_256`` objects of the main line).  ``--pmc-summary`` turns two rocprofv3 ``--pmc``
 CSV outputs (FETCH_SIZE, then WRITE_SIZE, each over the three ``--only`` runs)
 into profiles/hbm_counters.json, which fills ``roofline.traffic``.
 """
@@ -333,7 +334,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--all", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "copy"])
+    ap.add_argument("--only", choices=["decode", "prefill", "copy", "append", "d256"])
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--counter-summary", metavar="DIR")
     args = ap.parse_args()
@@ -370,6 +371,12 @@ def main():
     # ---------------- decode @16K (the headline) ----------------
     if args.only == "prefill":
         return only_prefill(ctx, args)
+    if args.only == "append":
+        print(json.dumps(kv_append_summary(ctx, args)), flush=True)
+        return
+    if args.only == "d256":
+        print(json.dumps(wide_summary(ctx, args)), flush=True)
+        return
     t_gen = time.perf_counter()
     p = synth.config2(q_rows=1, lens=[16384] * 16, device=dev)
     call, (P, T), keep = decode_setup(ctx, p, dev)
