@@ -632,6 +632,18 @@ def extra(ctx, args):
                               "GB/s": round(b / ms / 1e6, 1), "splits": P}), file=sys.stderr,
                   flush=True)
             del keep, call, p
+    # sequences far shorter than the page table's capacity (16 x 4,096 tokens in
+    # 65,536-token tables): the kernels size partitions from the longest one
+    for R in (1, 4):
+        p = synth.make_decode(208, 16, 32, 8, 128, [4096] * 16, R, kv_dtype=synth.DT_BF16,
+                              stride=4096, device=dev)
+        call, (P, T), keep = decode_setup(ctx, p, dev)
+        ms = time_calls(call, args.steps, args.warmup)
+        b = acc.decode_bytes(p.seq_lens.tolist(), R, 32, 8, 128, 2, 2, 2)
+        print(json.dumps({"workload": f"decode/verify B=16 L=4096 in 64K tables R={R}",
+                          "ms": round(ms, 4), "GB/s": round(b / ms / 1e6, 1),
+                          "planned_splits": P}), file=sys.stderr, flush=True)
+        del keep, call, p
     p = synth.config3(device=dev)
     call, (P, T), keep = decode_setup(ctx, p, dev)
     ms = time_calls(call, args.steps, args.warmup)

@@ -142,6 +142,7 @@ struct DecodePlan {
   bool mfma;
   bool wide;              // head_dim 256 with more than 8 rows per KV head
   int rows, rb, row_blocks, P, T;
+  int t_dyn, t_target, t_min, t_cap;   // the device-side partition rule (DecodeArgs)
   size_t ws_bytes, ws_o_bytes, ws_ml_bytes;
 };
 
@@ -199,6 +200,10 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
   // once, read back by the merge) stay within 1/16 of its K/V bytes at 16-bit K/V
   const int64_t tmin = round_up(std::max<int64_t>(256, 32 * (int64_t)rows_per_wg), kTGran);
   int64_t T;
+  pl->t_dyn = 0;
+  pl->t_target = 1;
+  pl->t_min = (int)tmin;
+  pl->t_cap = kTMax;
   if (opts->num_splits > 0) {
     T = round_up(ceil_div(cap, opts->num_splits), kTGran);
   } else {
@@ -223,6 +228,12 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
     // U[8K,16K] +6%, U[4K,32K] +20%, 32 x U[2K,16K] +28%; all 16K equal;
     // 4 x 64K -2.5%.
     if (!pl->mfma && !pl->wide) T = std::min(T, std::max(tmin, kValuTAuto));
+    // the kernels apply the same rule to the batch's longest sequence, so
+    // that sequences far shorter than the capacity still fill the CUs
+    pl->t_dyn = 1;
+    pl->t_target = (int)std::min<int64_t>(target, INT32_MAX);
+    pl->t_cap = (int)std::min<int64_t>(kTMax, (!pl->mfma && !pl->wide) ? std::max(tmin, kValuTAuto)
+                                                                         : kTMax);
   }
   // a wave preloads the page ids of its pages: at most 8192 tokens per partition
   T = std::min<int64_t>(T, kTMax);
@@ -427,6 +438,7 @@ attn_status attn_paged_decode(attn_ctx *ctx, const attn_io *io, const attn_kv *k
   a.k_frag = kv->k_fragments; a.v_frag = kv->v_fragments;
   a.frag_shift = kv->fragment_pages_log2;
   a.P = pl.P; a.T = pl.T;
+  a.t_dyn = pl.t_dyn; a.t_target = pl.t_target; a.t_min = pl.t_min; a.t_cap = pl.t_cap;
   a.row_blocks = pl.row_blocks;
   a.ws_o = reinterpret_cast<float *>(workspace);
   a.ws_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + pl.ws_o_bytes);

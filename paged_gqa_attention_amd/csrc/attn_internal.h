@@ -40,7 +40,43 @@ struct DecodeArgs {
   int64_t vs_sp, vs_sh;       // their page / head strides (floats)
   const uint64_t *k_frag, *v_frag;   // fragment tables (device addresses), or null
   int32_t frag_shift;                // log2(pages per fragment)
+  // partition size from the batch's longest sequence (t_dyn = 1): the plan's
+  // rule with that length in place of the capacity (see decode_tokens)
+  int32_t t_dyn, t_target, t_min, t_cap;
 };
+
+// Tokens per partition of this call.  The plan sees only the page table's
+// capacity; its rule -- T = max(t_min, ceil(len / t_target) rounded up to 128),
+// at most t_cap -- is applied here to the longest sequence of the batch, and T
+// is kept large enough that no sequence needs more than the P partitions the
+// grid has.  With the longest sequence at the capacity this is the plan's T.
+// Every lane of the calling wave must be active.
+__device__ __forceinline__ int decode_tokens(const DecodeArgs &a) {
+  if (!a.t_dyn) return a.T;
+  // the longest sequence: scalar loads of the lengths (wave-uniform), 16 at a time
+  typedef const __attribute__((address_space(4))) int32_t ci32;
+  const ci32 *lens = (const ci32 *)a.lens;
+  int m = 0;
+  int b = 0;
+  for (; b + 16 <= a.B; b += 16) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) m = max(m, lens[b + k]);
+  }
+  for (; b < a.B; ++b) m = max(m, lens[b]);
+  m = min(m, a.capacity);
+  const int t = max(a.t_min, ((m + a.t_target - 1) / a.t_target + 127) & ~127);
+  return max(min(t, a.t_cap), ((m + a.P - 1) / a.P + 127) & ~127);
+}
+
+// A lower bound of decode_tokens from one sequence's own length (the longest
+// one is at least as long): partition p of a sequence of length L is empty if
+// p * decode_tokens_lo(a, L) >= L, which a workgroup can tell before the
+// reduction over the batch.
+__device__ __forceinline__ int decode_tokens_lo(const DecodeArgs &a, int L) {
+  if (!a.t_dyn) return a.T;
+  const int l = max(L, 0);
+  return min(a.t_cap, max(a.t_min, ((l + a.t_target - 1) / a.t_target + 127) & ~127));
+}
 
 struct PrefillArgs {
   const void *q;

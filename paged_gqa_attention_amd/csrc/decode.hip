@@ -66,11 +66,12 @@ __device__ __forceinline__ void wave_scales(const float (*m_w)[NR], int wave, in
 // Log-sum-exp merge of the partitions + sink, one wave per output row
 // ==================================================================================
 template <int D>
-__device__ __forceinline__ void merge_row(const DecodeArgs &a, int b, int kvh, int rr, int lane) {
+__device__ __forceinline__ void merge_row(const DecodeArgs &a, int T, int b, int kvh, int rr,
+                                          int lane) {
   constexpr int DPL = D / 64;
   constexpr int CH = 8;                  // partitions whose outputs are loaded at once
   const int L = min(a.lens[b], a.capacity);
-  const int Pl = (L + a.T - 1) / a.T;    // live partitions
+  const int Pl = (L + T - 1) / T;        // live partitions
   const int h = kvh * a.G + rr / a.R, i = rr % a.R;
   const int64_t base = (((int64_t)b * a.Hkv + kvh) * a.rows + rr) * a.P;
   const float sink = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
@@ -145,7 +146,8 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rr = blockIdx.x * kWaves + wave, kvh = blockIdx.y, b = blockIdx.z;
   // rows past a sequence's own row count are not part of the output
-  if (rr < a.rows && rr % a.R < seq_rows(a.rows_b, b, a.R)) merge_row<D>(a, b, kvh, rr, lane);
+  const int T = decode_tokens(a);
+  if (rr < a.rows && rr % a.R < seq_rows(a.rows_b, b, a.R)) merge_row<D>(a, T, b, kvh, rr, lane);
 }
 
 // ==================================================================================
@@ -184,9 +186,11 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
   const int kvh = blockIdx.x / a.row_blocks, rb = blockIdx.x % a.row_blocks;
   const int p = blockIdx.y, b = blockIdx.z;
   const int L = min(a.lens[b], a.capacity);
-  const int t0 = p * a.T;
-  if (t0 >= L) return;  // empty partition: the merge never reads it
-  const int t1 = min(L, t0 + a.T);
+  if (p * decode_tokens_lo(a, L) >= L) return;   // empty partition: the merge never reads it
+  const int T = decode_tokens(a);
+  const int t0 = p * T;
+  if (t0 >= L) return;
+  const int t1 = min(L, t0 + T);
   const int n = lane >> 2, qq = lane & 3;
   const int tg = lane % CPR;
 
@@ -536,9 +540,11 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
   const int wave = uniform_int(threadIdx.x >> 6);
   const int kvh = blockIdx.x, p = blockIdx.y, b = blockIdx.z;
   const int L = min(a.lens[b], a.capacity);
-  const int t0 = p * a.T;
+  if (p * decode_tokens_lo(a, L) >= L) return;   // empty partition
+  const int T = decode_tokens(a);
+  const int t0 = p * T;
   if (t0 >= L) return;
-  const int t1 = min(L, t0 + a.T);
+  const int t1 = min(L, t0 + T);
   const int n = lane & 15, j = lane >> 4;
 
   // ---- Q^T fragments: B[k = d][n = row] ----

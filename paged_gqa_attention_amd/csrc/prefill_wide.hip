@@ -154,9 +154,11 @@ __global__ __launch_bounds__(waves<DEC>() * 64) void attn_wide(typename WideArgs
     part = blockIdx.y;
     b = blockIdx.z;
     L = min(a.lens[b], a.capacity);
-    k_lo = part * a.T;
+    if (part * decode_tokens_lo(a, L) >= L) return;   // empty partition: never merged
+    const int T = decode_tokens(a);
+    k_lo = part * T;
     if (k_lo >= L) return;                     // empty partition: never merged
-    k_hi = min(L, k_lo + a.T);
+    k_hi = min(L, k_lo + T);
     const int nrows = seq_rows(a.rows_b, b, a.R);
     const int r = kRowsW * wave + nl;
     row_ok = r < a.rows;
