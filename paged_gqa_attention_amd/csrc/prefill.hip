@@ -66,6 +66,12 @@ __device__ __forceinline__ uint32_t pack16(float a, float b) {
   return F16 ? pack_f16x2(a, b) : pack_bf16x2(a, b);
 }
 
+// max(a, b) as a median with +inf: one instruction, where fmaxf first
+// quiets both operands (two more)
+__device__ __forceinline__ float max2(float a, float b) {
+  return __builtin_amdgcn_fmed3f(a, b, __builtin_inff());
+}
+
 }  // namespace
 
 template <int KVDT, int QDT, int D, int HPW, bool MASK, bool VS>
@@ -152,6 +158,9 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m_run = kNegInf, l_run = 0.f;
+  // derived from m_run, updated only when it changes: the exponent offset
+  // (0 while no score was seen) and the raw-score threshold of the next rescale
+  float neg_m = 0.f, grow_at = kNegInf;
 
   const int32_t *pt = a.page_table + (int64_t)b * a.pt_stride;
   const char *kbase = reinterpret_cast<const char *>(a.k) + (int64_t)kvh * a.k_sh * ELT;
@@ -356,29 +365,33 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
 
     // online softmax (lazy rescaling) for row nl; the two lane halves hold
     // keys 16g' + 8hh + ... of each 32-key block
-    // row max as a tree of 3-input maxima (32 values -> 11 -> 4 -> 1)
-    float t1[11];
+    // row max as a tree of 3-input maxima (32 values -> 10 + 2 -> 4 -> 1)
+    float t1[10];
 #pragma unroll
     for (int k = 0; k < 10; ++k) {
       const int a0 = 3 * k, a1 = 3 * k + 1, a2 = 3 * k + 2;
       t1[k] = max3(s[a0 >> 4][a0 & 15], s[a1 >> 4][a1 & 15], s[a2 >> 4][a2 & 15]);
     }
-    t1[10] = __builtin_fmaxf(s[1][14], s[1][15]);
-    float mx = max3(max3(t1[0], t1[1], t1[2]), max3(t1[3], t1[4], t1[5]),
-                    max3(t1[6], t1[7], max3(t1[8], t1[9], t1[10])));
-    mx = max_xor32(mx);
-    const float mxs = mx * sc;
-    const bool grow = mxs > m_run + kLazy;
+    float mx = max2(max3(max3(t1[0], t1[1], t1[2]), max3(t1[3], t1[4], t1[5]),
+                         max3(t1[6], t1[7], t1[8])),
+                    max3(t1[9], s[1][14], s[1][15]));
+    {
+      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    // rescale when the scaled max exceeds m_run by more than kLazy (sc > 0)
+    const bool grow = mx > grow_at;
     if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float m_new = grow ? mxs : m_run;
+      const float m_new = grow ? mx * sc : m_run;
       const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
       l_run *= alpha;
       m_run = m_new;
+      neg_m = (m_run == kNegInf) ? 0.f : -m_run;
+      grow_at = (m_run + kLazy) / sc;
     }
-    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-    float lsum[4] = {0.f, 0.f, 0.f, 0.f};   // independent chains of the row sum
+    float la = l_run, lb = 0.f;   // two chains of the row sum
     u32x4 pf[2][2];   // [mb][kk]: P^T fragment, keys 32mb + 16kk + 8hh .. +8
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -386,13 +399,14 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(__builtin_fmaf(s[mb][8 * kk + 2 * e], sc, -m_use));
-          const float p1 = fast_exp2(__builtin_fmaf(s[mb][8 * kk + 2 * e + 1], sc, -m_use));
+          const float p0 = fast_exp2(__builtin_fmaf(s[mb][8 * kk + 2 * e], sc, neg_m));
+          const float p1 = fast_exp2(__builtin_fmaf(s[mb][8 * kk + 2 * e + 1], sc, neg_m));
           const uint32_t w = F16 ? pack_f16x2(p0, p1) : pack_bf16x2(p0, p1);
           pf[mb][kk][e] = w;
-          lsum[e] = F16 ? dot2_f16(w, 0x3C003C00u, lsum[e]) : dot2_bf16(w, 0x3F803F80u, lsum[e]);
+          if (e & 1) lb = F16 ? dot2_f16(w, 0x3C003C00u, lb) : dot2_bf16(w, 0x3F803F80u, lb);
+          else la = F16 ? dot2_f16(w, 0x3C003C00u, la) : dot2_bf16(w, 0x3F803F80u, la);
         }
-    l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+    l_run = la + lb;
 
     // O^T[db] += V^T[32 rows, 16 keys] P^T[16 keys, 32 rows]
 #pragma unroll
