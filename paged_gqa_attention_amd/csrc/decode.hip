@@ -170,12 +170,19 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
   constexpr int CPR = ELT;           // V chunks per value row (16 tokens * ELT bytes)
   constexpr int MR = RB / 4;         // softmax rows per lane
   constexpr int QW = (KVDT == DT_F32) ? 4 : (is8bit(KVDT) ? 8 : 4);  // Q words per K chunk
+  // 8-bit V without per-vector scales: P.V as f16 dot products.  Every e4m3fn
+  // and e5m2 value is exact in f16 and f16 x f16 products are exact in FP32,
+  // so the only rounding added is that of the weights to f16 (2^-11 relative;
+  // the row sums use the same rounded weights).  It halves the vector
+  // instructions of P.V, which bound this kernel at 8-bit K/V.
+  constexpr bool PV16 = is8bit(KVDT) && !VS;
 
   // query rows of the workgroup, in the arithmetic's representation:
   // FP32 for FP32 K/V, else the 16-bit Q codes
   constexpr int QE = (KVDT == DT_F32) ? 4 : 2;
   __shared__ __attribute__((aligned(16))) char q_lds[RB * D * QE];
-  __shared__ float p_lds[kWaves][16][RB];
+  __shared__ float p_lds[kWaves][PV16 ? 1 : 16][RB];
+  __shared__ __attribute__((aligned(16))) uint16_t p16_lds[kWaves][PV16 ? RB : 1][16];
   __shared__ float alpha_lds[kWaves][RB];
   __shared__ float m_w[kWaves][RB];
   __shared__ float l_w[kWaves][RB];
@@ -362,10 +369,16 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
       const float m_new = __builtin_fmaxf(m_run[k], mx);
       const float m_use = (m_new == kNegInf) ? 0.f : m_new;
       const float alpha = fast_exp2(m_run[k] - m_use);
-      const float pv = fast_exp2(x - m_use);
+      float pv = fast_exp2(x - m_use);
+      if constexpr (PV16) {
+        const _Float16 ph = (_Float16)pv;
+        p16_lds[wave][qq + 4 * k][n] = __builtin_bit_cast(uint16_t, ph);
+        pv = (float)ph;
+      } else {
+        p_lds[wave][n][qq + 4 * k] = VS ? pv * v_tok : pv;
+      }
       l_run[k] = l_run[k] * alpha + pv;
       m_run[k] = m_new;
-      p_lds[wave][n][qq + 4 * k] = VS ? pv * v_tok : pv;
       if (n == 0) alpha_lds[wave][qq + 4 * k] = alpha;
     }
     wave_lds_sync();
@@ -378,19 +391,52 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
     for (int r = 0; r < RB; ++r)
 #pragma unroll
       for (int c = 0; c < NL; ++c) o[r][c] *= al[r];
+    if constexpr (PV16) {
+      // the lane's chunk is one value row over the page's 16 tokens: word i of
+      // the f16 weights and of the converted values holds tokens 2i, 2i+1
+      uint32_t pw[RB][8];
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) {
-      const int t = tg * EPC + e;
-      float pr[RB];
+      for (int r = 0; r < RB; ++r) {
+        const u32x4 w0 = *reinterpret_cast<const u32x4 *>(&p16_lds[wave][r][0]);
+        const u32x4 w1 = *reinterpret_cast<const u32x4 *>(&p16_lds[wave][r][8]);
 #pragma unroll
-      for (int r = 0; r < RB; ++r) pr[r] = p_lds[wave][t][r];
-      const bool tvalid = page_full || (pg * 16 + t < t1);
+        for (int i = 0; i < 4; ++i) { pw[r][i] = w0[i]; pw[r][4 + i] = w1[i]; }
+      }
+      const int nv = page_full ? 16 : t1 - pg * 16;   // valid tokens of the page
 #pragma unroll
       for (int c = 0; c < NL; ++c) {
-        float vv = chunk_elem<KVDT>(vc[c], e);
-        vv = tvalid ? vv : 0.f;  // slots past the end may hold anything, NaN included
+        uint32_t vh[8];
 #pragma unroll
-        for (int r = 0; r < RB; ++r) o[r][c] = __builtin_fmaf(pr[r], vv, o[r][c]);
+        for (int w = 0; w < 4; ++w) {
+          vh[2 * w] = e8x2_to_f16x2<KVDT, false>(vc[c][w]);
+          vh[2 * w + 1] = e8x2_to_f16x2<KVDT, true>(vc[c][w]);
+        }
+        if (!page_full) {
+          // slots past the end may hold anything, NaN included
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            vh[i] = 2 * i >= nv ? 0u : (2 * i + 1 >= nv ? (vh[i] & 0xffffu) : vh[i]);
+        }
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o[r][c] = dot2_f16(pw[r][i], vh[i], o[r][c]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        const int t = tg * EPC + e;
+        float pr[RB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) pr[r] = p_lds[wave][t][r];
+        const bool tvalid = page_full || (pg * 16 + t < t1);
+#pragma unroll
+        for (int c = 0; c < NL; ++c) {
+          float vv = chunk_elem<KVDT>(vc[c], e);
+          vv = tvalid ? vv : 0.f;  // slots past the end may hold anything, NaN included
+#pragma unroll
+          for (int r = 0; r < RB; ++r) o[r][c] = __builtin_fmaf(pr[r], vv, o[r][c]);
+        }
       }
     }
     wave_lds_sync();
