@@ -204,7 +204,11 @@ void attn_free(void *p);
  * partition count follows the page table's capacity (page_table_stride *
  * page_size), the rows that share each K/V read and the device's CU count
  * (Geramy/LSE releases, v0.4.20: partitions from K/V table capacity, with an
- * LDS check). */
+ * LDS check).  tokens_per_split is the size at full capacity: unless
+ * opts->num_splits forces a split, the kernels apply the same rule to the
+ * longest seq_lens entry of the call and use shorter partitions (never more
+ * than num_splits of them) when every sequence is shorter than the
+ * capacity. */
 attn_status attn_paged_decode_plan(const attn_ctx *ctx, const attn_io *io, const attn_kv *kv,
                                    const attn_opts *opts, int32_t *num_splits,
                                    int32_t *tokens_per_split, size_t *workspace_bytes,
