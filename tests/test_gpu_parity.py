@@ -125,6 +125,29 @@ def test_decode_forced_splits(splits):
     check_full(p, o, l, tol=2e-3, label=f"splits={splits}")
 
 
+SHORT_IN_LONG = [
+    ("valu_r1_bf16", 1, 128, 32, 8, DT_BF16),
+    ("valu_r2_f16_d64", 2, 64, 8, 2, DT_F16),
+    ("valu_r1_fp8", 1, 128, 32, 8, DT_FP8),
+    ("mfma_r4_bf16", 4, 128, 32, 8, DT_BF16),
+    ("mfma_r8_fp8", 8, 128, 16, 4, DT_FP8),
+    ("wide_r4_d256", 4, 256, 16, 4, DT_BF16),
+    ("valu_r1_d256", 1, 256, 8, 2, DT_BF16),
+]
+
+
+@pytest.mark.parametrize("name,R,d,Hq,Hkv,dt", SHORT_IN_LONG, ids=[c[0] for c in SHORT_IN_LONG])
+def test_decode_short_sequences_in_long_tables(name, R, d, Hq, Hkv, dt):
+    """Sequences far shorter than the page table's capacity (65,536 tokens): the
+    kernels size their partitions from the longest sequence of the call, so the
+    partition boundaries differ from the plan's; the result must not."""
+    _say("short in long", name)
+    p = synth.make_decode(231, 4, Hq, Hkv, d, [2500, 100, 7, 1999], R, kv_dtype=dt,
+                          stride=4096, sinks=True)
+    o, l = run(Dev(p))
+    check_full(p, o, l, label=name)
+
+
 def test_decode_page_permutation_bit_identical():
     _say("decode permutation")
     p = synth.make_decode(73, 2, 32, 8, 128, [900, 1333], 4, kv_dtype=DT_BF16, extra_pages=7)
