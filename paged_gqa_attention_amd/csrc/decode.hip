@@ -170,12 +170,14 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
   constexpr int CPR = ELT;           // V chunks per value row (16 tokens * ELT bytes)
   constexpr int MR = RB / 4;         // softmax rows per lane
   constexpr int QW = (KVDT == DT_F32) ? 4 : (is8bit(KVDT) ? 8 : 4);  // Q words per K chunk
-  // 8-bit V without per-vector scales: P.V as f16 dot products.  Every e4m3fn
-  // and e5m2 value is exact in f16 and f16 x f16 products are exact in FP32,
-  // so the only rounding added is that of the weights to f16 (2^-11 relative;
-  // the row sums use the same rounded weights).  It halves the vector
-  // instructions of P.V, which bound this kernel at 8-bit K/V.
-  constexpr bool PV16 = is8bit(KVDT) && !VS;
+  // 8-bit V: P.V as 16-bit dot products, half the vector instructions of
+  // FP32 FMAs, which bound this kernel at 8-bit K/V.  Every e4m3fn and e5m2
+  // value is exact in f16 and in bf16, and the 16-bit products are exact in
+  // FP32, so the only rounding added is that of the weights: to f16 with
+  // per-tensor scales (2^-11 relative; the row sums use the same rounded
+  // weights), to bf16 with per-vector scales, whose weight times V scale can
+  // lie outside the f16 range (2^-9 relative).
+  constexpr bool PV16 = is8bit(KVDT);
 
   // query rows of the workgroup, in the arithmetic's representation:
   // FP32 for FP32 K/V, else the 16-bit Q codes
@@ -370,7 +372,9 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
       const float m_use = (m_new == kNegInf) ? 0.f : m_new;
       const float alpha = fast_exp2(m_run[k] - m_use);
       float pv = fast_exp2(x - m_use);
-      if constexpr (PV16) {
+      if constexpr (PV16 && VS) {
+        p16_lds[wave][qq + 4 * k][n] = __builtin_bit_cast(uint16_t, (__bf16)(pv * v_tok));
+      } else if constexpr (PV16) {
         const _Float16 ph = (_Float16)pv;
         p16_lds[wave][qq + 4 * k][n] = __builtin_bit_cast(uint16_t, ph);
         pv = (float)ph;
@@ -393,7 +397,7 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
       for (int c = 0; c < NL; ++c) o[r][c] *= al[r];
     if constexpr (PV16) {
       // the lane's chunk is one value row over the page's 16 tokens: word i of
-      // the f16 weights and of the converted values holds tokens 2i, 2i+1
+      // the 16-bit weights and of the converted values holds tokens 2i, 2i+1
       uint32_t pw[RB][8];
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
@@ -408,8 +412,8 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
         uint32_t vh[8];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          vh[2 * w] = e8x2_to_f16x2<KVDT, false>(vc[c][w]);
-          vh[2 * w + 1] = e8x2_to_f16x2<KVDT, true>(vc[c][w]);
+          vh[2 * w] = e8x2_to_16<KVDT, !VS, false>(vc[c][w]);
+          vh[2 * w + 1] = e8x2_to_16<KVDT, !VS, true>(vc[c][w]);
         }
         if (!page_full) {
           // slots past the end may hold anything, NaN included
@@ -420,7 +424,8 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
 #pragma unroll
         for (int r = 0; r < RB; ++r)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) o[r][c] = dot2_f16(pw[r][i], vh[i], o[r][c]);
+          for (int i = 0; i < 8; ++i)
+            o[r][c] = VS ? dot2_bf16(pw[r][i], vh[i], o[r][c]) : dot2_f16(pw[r][i], vh[i], o[r][c]);
       }
     } else {
 #pragma unroll

@@ -140,9 +140,11 @@ def test_decode_ragged_rows_per_vector(dt, R, rps):
 def test_uniform_vector_scales_equal_per_tensor_scale():
     """Every per-vector scale = c must give the per-tensor result with scale c, up to
     where the FP32 roundings fall (per token instead of once per call) and the
-    per-tensor single-row path's f16 softmax weights: each weight is rounded to f16
-    (relative error <= 2^-11) and the row sum uses the rounded weights, so the output
-    moves by at most 2^-11 * max|v - o| <= 2^-10 * max|v|."""
+    single-row path's 16-bit softmax weights.  Per-tensor scales: each weight is
+    rounded to f16 (relative error <= 2^-11) and the row sum uses the rounded
+    weights, so the output moves by at most 2^-11 * max|v - o| <= 2^-10 * max|v|.
+    Per-vector scales: each weight times its V scale is rounded to bf16 (<= 2^-9)
+    under an unrounded row sum, so the output moves by at most 2^-9 * max|v|."""
     _say("uniform scales")
     p = synth.make_decode(174, 2, 8, 2, 128, [700, 300], 1, kv_dtype=DT_BF8)
     d = Dev(p)
@@ -155,7 +157,7 @@ def test_uniform_vector_scales_equal_per_tensor_scale():
     torch.cuda.synchronize()
     err = (o1 - o2).abs().max().item()
     vmax = torch.nan_to_num(p.v_pool.float(), nan=0.0, posinf=0.0, neginf=0.0).abs().max().item() * c
-    assert err <= 2.0 ** -10 * vmax + 1e-4, (err, vmax)
+    assert err <= (2.0 ** -10 + 2.0 ** -9) * vmax + 1e-4, (err, vmax)
 
 
 # ------------------------------------------------------------------ prefill
