@@ -77,6 +77,19 @@ def test_append_bit_exact(kv_dtype, src_dtype):
         assert _same_codes(kv_dtype, gt, ex)
 
 
+@pytest.mark.parametrize("kv_dtype", [DT_F32, DT_F16, DT_BF16, DT_FP8])
+@pytest.mark.parametrize("src_dtype", [DT_F32, DT_F16, DT_BF16])
+@pytest.mark.parametrize("n_new,d", [(1, 64), (3, 128), (8, 64), (2, 256)])
+def test_append_few_rows_bit_exact(kv_dtype, src_dtype, n_new, d):
+    """Decode and verify steps (at most 8 new rows per sequence take the one-wave
+    path): mid-page and page-aligned ends, a sequence shorter than n_new, special
+    values."""
+    _, _, got, exp = _append_case(750 + 10 * kv_dtype + src_dtype + 100 * n_new, kv_dtype,
+                                  src_dtype, d, [37, 2, 16, 64, 300], n_new, 20, specials=True)
+    for gt, ex in zip(got, exp):
+        assert _same_codes(kv_dtype, gt, ex)
+
+
 @pytest.mark.parametrize("kv_dtype", [DT_F16, DT_BF16, DT_FP8, DT_F32])
 def test_append_special_values(kv_dtype):
     _, _, got, exp = _append_case(700 + kv_dtype, kv_dtype, DT_F32, 128, [40, 129], 40, 9,
