@@ -352,7 +352,7 @@ def make_blocksparse(seed, batch, num_q_heads, num_kv_heads, head_dim, seq_len,
     return p
 
 
-# --- the five workloads (sizes as stated for the path) -------------
+# --- the five workloads of the path, at their stated sizes ------------------------
 
 def config1(seed=101):
     """Tiny paged decode: 1 sequence, 4 q heads, 1 kv head, d=64, 256 tokens,
