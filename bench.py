@@ -114,8 +114,8 @@ def pmc_summary(fetch_dir: str, write_dir: str):
     w_scale = COPY_BYTES / (copy_mean("WRITE_SIZE") * 1024)
     groups = {
         "decode_bf16_16k": ("decode", ("decode_valu", "decode_merge"),
-                            _src_hash("decode.hip", "common.h")),
-        "prefill_bf16_8k_b16": ("prefill", ("prefill_mfma",), _src_hash("prefill.hip", "common.h")),
+                            _src_hash("decode.hip", "common.h", "attn_internal.h")),
+        "prefill_bf16_8k_b16": ("prefill", ("prefill_mfma",), _src_hash("prefill.hip", "common.h", "attn_internal.h")),
     }
     for key, (run, kernels, h) in groups.items():
         total = 0.0
@@ -386,7 +386,7 @@ def main():
                               synth.DT_BF16, synth.DT_BF16)
     gbs = nbytes / (ms * 1e-3) / 1e9
     dec_pc = None if args.only else per_call_stats(call)
-    dec_hash = _src_hash("decode.hip", "common.h")
+    dec_hash = _src_hash("decode.hip", "common.h", "attn_internal.h")
     traffic = _traffic("decode_bf16_16k", dec_hash)
     roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -410,7 +410,7 @@ def main():
     pre_pc = per_call_stats(pcall, 20)
     flops = acc.attention_flops(acc.causal_pairs(8192, 8192), 64, 64, 16)
     tfs = flops / (pms * 1e-3) / 1e12
-    pre_hash = _src_hash("prefill.hip", "common.h")
+    pre_hash = _src_hash("prefill.hip", "common.h", "attn_internal.h")
     prefill = {
         "metric": "causal prefill attention TFLOP/s (BF16)", "value": round(tfs, 1),
         "unit": "TFLOP/s", "ms_per_step": round(pms, 4), "steps": psteps,

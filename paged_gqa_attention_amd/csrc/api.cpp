@@ -152,6 +152,7 @@ constexpr int kValuWgPerCu = 2;   // decode_valu workgroups per CU the planner c
 constexpr int kMfmaWgPerCu = 1;   // decode_mfma workgroups per CU the planner counts on
 constexpr int kWideWgPerCu = 2;   // head_dim 256 verify workgroups per CU
 constexpr int64_t kValuTAuto = 1024;   // planned partition size limit of the VALU kernel
+constexpr int64_t kValuRounds = 16;    // ... unless it plans more rounds of workgroups than this
 
 attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *kv, const attn_opts *opts,
                         DecodePlan *pl, char **err) {
@@ -227,7 +228,14 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
     // Measured (16 sequences, 32 query / 8 KV heads, d 128): lengths
     // U[8K,16K] +6%, U[4K,32K] +20%, 32 x U[2K,16K] +28%; all 16K equal;
     // 4 x 64K -2.5%.
-    if (!pl->mfma && !pl->wide) T = std::min(T, std::max(tmin, kValuTAuto));
+    // The limit is lifted where it would plan more than kValuRounds rounds
+    // of resident workgroups: with many sequences it only multiplies the
+    // grid, and every launched workgroup costs, even one that exits at once
+    // past its sequence's end (measured, 512 x 1,024 tokens in 1,024-token
+    // tables: 372 us at 1 partition per sequence, 541 us at 2, 940 us at 8).
+    if (!pl->mfma && !pl->wide)
+      T = std::max(std::min(T, std::max(tmin, kValuTAuto)),
+                   round_up(ceil_div(cap, kValuRounds * target), kTGran));
     // the kernels apply the same rule to the batch's longest sequence, so
     // that sequences far shorter than the capacity still fill the CUs
     pl->t_dyn = 1;

@@ -50,19 +50,30 @@ struct DecodeArgs {
 // at most t_cap -- is applied here to the longest sequence of the batch, and T
 // is kept large enough that no sequence needs more than the P partitions the
 // grid has.  With the longest sequence at the capacity this is the plan's T.
+// With more than 64 sequences every lane of the calling wave must be active.
 // Every lane of the calling wave must be active.
 __device__ __forceinline__ int decode_tokens(const DecodeArgs &a) {
   if (!a.t_dyn) return a.T;
-  // the longest sequence: scalar loads of the lengths (wave-uniform), 16 at a time
-  typedef const __attribute__((address_space(4))) int32_t ci32;
-  const ci32 *lens = (const ci32 *)a.lens;
+  // the longest sequence: up to 64 lengths with scalar loads (wave-uniform, 16
+  // at a time), more with vector loads of 64 and a reduction across the wave
   int m = 0;
-  int b = 0;
-  for (; b + 16 <= a.B; b += 16) {
+  if (a.B <= 64) {
+    typedef const __attribute__((address_space(4))) int32_t ci32;
+    const ci32 *lens = (const ci32 *)a.lens;
+    int b = 0;
+    for (; b + 16 <= a.B; b += 16) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) m = max(m, lens[b + k]);
+      for (int k = 0; k < 16; ++k) m = max(m, lens[b + k]);
+    }
+    for (; b < a.B; ++b) m = max(m, lens[b]);
+  } else {
+    typedef const __attribute__((address_space(1))) int32_t gi32;
+    const gi32 *lens = (const gi32 *)a.lens;
+    for (int b = (int)(threadIdx.x & 63); b < a.B; b += 64) m = max(m, lens[b]);
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) m = max(m, __shfl_xor(m, k));
+    m = __builtin_amdgcn_readfirstlane(m);
   }
-  for (; b < a.B; ++b) m = max(m, lens[b]);
   m = min(m, a.capacity);
   const int t = max(a.t_min, ((m + a.t_target - 1) / a.t_target + 127) & ~127);
   return max(min(t, a.t_cap), ((m + a.P - 1) / a.P + 127) & ~127);

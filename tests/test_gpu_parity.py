@@ -148,6 +148,17 @@ def test_decode_short_sequences_in_long_tables(name, R, d, Hq, Hkv, dt):
     check_full(p, o, l, label=name)
 
 
+@pytest.mark.parametrize("R", [1, 4])
+def test_decode_many_sequences_short_in_long_tables(R):
+    """More than 64 sequences (the kernels then find the longest with vector
+    loads and a reduction across the wave), far shorter than the capacity."""
+    _say("many short in long", R)
+    lens = [int(x) for x in (np.arange(80) * 37 % 611 + 1)]
+    p = synth.make_decode(232, 80, 8, 2, 64, lens, R, kv_dtype=DT_BF16, stride=256, sinks=True)
+    o, l = run(Dev(p))
+    check_full(p, o, l, label=f"B=80 R={R}")
+
+
 def test_decode_page_permutation_bit_identical():
     _say("decode permutation")
     p = synth.make_decode(73, 2, 32, 8, 128, [900, 1333], 4, kv_dtype=DT_BF16, extra_pages=7)
