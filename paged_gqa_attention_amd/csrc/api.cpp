@@ -235,7 +235,7 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
     // tables: 372 us at 1 partition per sequence, 541 us at 2, 940 us at 8).
     if (!pl->mfma && !pl->wide)
       T = std::max(std::min(T, std::max(tmin, kValuTAuto)),
-                   round_up(ceil_div(cap, kValuRounds * target), kTGran));
+                   round_up(ceil_div(cap, std::max<int64_t>(1, kValuRounds * slots / groups)), kTGran));
     // the kernels apply the same rule to the batch's longest sequence, so
     // that sequences far shorter than the capacity still fill the CUs
     pl->t_dyn = 1;
@@ -243,8 +243,10 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
     pl->t_cap = (int)std::min<int64_t>(kTMax, (!pl->mfma && !pl->wide) ? std::max(tmin, kValuTAuto)
                                                                          : kTMax);
   }
-  // a wave preloads the page ids of its pages: at most 8192 tokens per partition
-  T = std::min<int64_t>(T, kTMax);
+  // a wave of the MFMA kernels preloads the page ids of its pages: at most
+  // 8192 tokens per partition (the VALU kernel loads them 128 pages at a time)
+  if (pl->mfma || pl->wide) T = std::min<int64_t>(T, kTMax);
+  T = std::min<int64_t>(T, std::min<int64_t>(round_up(cap, kTGran), int64_t(1) << 30));
   const int64_t P = ceil_div(cap, T);
   if (P > 65535) return fail(err, ATTN_ERR_UNSUPPORTED, "too many partitions (%lld)", (long long)P);
   pl->P = (int)P;

@@ -260,16 +260,26 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
   const int pg_first = (t0 >> 4) + wave;
   int pg = pg_first;
 
-  // This wave's page ids (its k-th page is pg_first + 4k, k < 128: partitions
-  // hold at most 8192 tokens), loaded once, coalesced, and broadcast per page.
+  // This wave's page ids (its k-th page is pg_first + 4k), 128 at a time,
+  // loaded coalesced and broadcast per page; the next 128 are loaded when the
+  // walk, which visits the pages in order, reaches them.
   int ids[2];
+  int ids_k0 = 0;
+  auto load_ids = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
-  for (int hlf = 0; hlf < 2; ++hlf) {
-    const int idx = pg_first + (64 * hlf + lane) * kWaves;
-    ids[hlf] = idx < pg_end ? pt[idx] : 0;
-  }
+    for (int hlf = 0; hlf < 2; ++hlf) {
+      const int idx = pg_first + (k0 + 64 * hlf + lane) * kWaves;
+      ids[hlf] = idx < pg_end ? pt[idx] : 0;
+    }
+    ids_k0 = k0;
+  };
+  load_ids(0);
   auto page_id = [&](int page_idx) -> int64_t {
-    const int k = (page_idx - pg_first) / kWaves;
+    int k = (page_idx - pg_first) / kWaves - ids_k0;
+    if (k >= 128) {
+      load_ids(ids_k0 + 128);
+      k -= 128;
+    }
     return k < 64 ? __builtin_amdgcn_readlane(ids[0], k) : __builtin_amdgcn_readlane(ids[1], k - 64);
   };
 

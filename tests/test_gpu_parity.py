@@ -159,6 +159,17 @@ def test_decode_many_sequences_short_in_long_tables(R):
     check_full(p, o, l, label=f"B=80 R={R}")
 
 
+@pytest.mark.parametrize("dt,R", [(DT_BF16, 1), (DT_F16, 2), (DT_FP8, 1)])
+def test_decode_valu_partition_longer_than_8192_tokens(dt, R):
+    """One partition of 20,480 tokens (forced): each wave walks 320 pages, so its
+    page ids are loaded in three blocks of 128."""
+    _say("long partition", dt, R)
+    p = synth.make_decode(233, 2, 8, 2, 64, [20000, 9000], R, kv_dtype=dt, stride=1280,
+                          sinks=True)
+    o, l = run(Dev(p), num_splits=1)
+    check_full(p, o, l, label=f"dt={dt} R={R}")
+
+
 def test_decode_page_permutation_bit_identical():
     _say("decode permutation")
     p = synth.make_decode(73, 2, 32, 8, 128, [900, 1333], 4, kv_dtype=DT_BF16, extra_pages=7)
