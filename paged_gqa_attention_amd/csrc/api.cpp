@@ -243,9 +243,10 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
     pl->t_cap = (int)std::min<int64_t>(kTMax, (!pl->mfma && !pl->wide) ? std::max(tmin, kValuTAuto)
                                                                          : kTMax);
   }
-  // a wave of the MFMA kernels preloads the page ids of its pages: at most
-  // 8192 tokens per partition (the VALU kernel loads them 128 pages at a time)
-  if (pl->mfma || pl->wide) T = std::min<int64_t>(T, kTMax);
+  // a wave of the head_dim 256 verify kernel preloads the page ids of its
+  // pages: at most 8192 tokens per partition (the VALU and MFMA kernels load
+  // them in blocks as their walk reaches them)
+  if (pl->wide) T = std::min<int64_t>(T, kTMax);
   T = std::min<int64_t>(T, std::min<int64_t>(round_up(cap, kTGran), int64_t(1) << 30));
   const int64_t P = ceil_div(cap, T);
   if (P > 65535) return fail(err, ATTN_ERR_UNSUPPORTED, "too many partitions (%lld)", (long long)P);

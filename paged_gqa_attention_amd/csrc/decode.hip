@@ -645,15 +645,19 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
   const int pp_first = (t0 >> 5) + wave;
   int pp = pp_first;
 
-  // Page ids of this wave's page pairs (pair k = pp_first + 4k, k < 64:
-  // partitions hold at most 8192 tokens), loaded once and broadcast per pair.
+  // Page ids of this wave's page pairs (pair k = pp_first + 4k), 64 pairs at
+  // a time, loaded coalesced and broadcast per pair; the next 64 are loaded
+  // when the walk, which visits the pairs in order, reaches them.
   int ids0, ids1;
-  {
-    const int ppi = pp_first + lane * kWaves;
+  int ids_k0 = 0;
+  auto load_ids = [&](int k0) __attribute__((always_inline)) {
+    const int ppi = pp_first + (k0 + lane) * kWaves;
     const int p0 = 2 * ppi, p1 = 2 * ppi + 1;
     ids0 = p0 < pg_end ? pt[p0] : 0;
     ids1 = p1 < pg_end ? pt[p1] : ids0;
-  }
+    ids_k0 = k0;
+  };
+  load_ids(0);
 
   // K rows: A row m = n of MFMA `a` holds token 8*(n/4) + 4a + n%4 (page-pair local)
   // V rows: value row 16*mb + n, tokens 8*j .. 8*j+7 (page j/2, offset 8*(j&1))
@@ -661,7 +665,11 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
   // (sd[0..1] K, sd[2..3] V).
   auto load_pair = [&](auto mode, int ppi, u32x4 (*kd)[KL], u32x4 *vd16, u32x2 *vd8,
                        f32x4 *sd) __attribute__((always_inline)) {
-    const int k = (ppi - pp_first) / kWaves;
+    int k = (ppi - pp_first) / kWaves - ids_k0;
+    if (k >= 64) {
+      load_ids(ids_k0 + 64);
+      k -= 64;
+    }
     const int64_t pid0 = __builtin_amdgcn_readlane(ids0, k);
     const int64_t pid1 = __builtin_amdgcn_readlane(ids1, k);
     // the pair's two page tiles of K and V (page ids are wave-uniform)

@@ -159,10 +159,11 @@ def test_decode_many_sequences_short_in_long_tables(R):
     check_full(p, o, l, label=f"B=80 R={R}")
 
 
-@pytest.mark.parametrize("dt,R", [(DT_BF16, 1), (DT_F16, 2), (DT_FP8, 1)])
-def test_decode_valu_partition_longer_than_8192_tokens(dt, R):
-    """One partition of 20,480 tokens (forced): each wave walks 320 pages, so its
-    page ids are loaded in three blocks of 128."""
+@pytest.mark.parametrize("dt,R", [(DT_BF16, 1), (DT_F16, 2), (DT_FP8, 1), (DT_BF16, 4), (DT_FP8, 8)])
+def test_decode_partition_longer_than_8192_tokens(dt, R):
+    """One partition of 20,480 tokens (forced): a wave of the VALU kernel (R <= 2)
+    walks 320 pages, its page ids loaded in three blocks of 128; a wave of the
+    MFMA kernel (R = 4, 8) walks 160 page pairs, their ids in three blocks of 64."""
     _say("long partition", dt, R)
     p = synth.make_decode(233, 2, 8, 2, 64, [20000, 9000], R, kv_dtype=dt, stride=1280,
                           sinks=True)
