@@ -93,7 +93,8 @@
  *                              implement (head_dim not 64, 128 or 256 --
  *                              256 with 16-bit or 8-bit K/V only --,
  *                              page_size not 16, unsupported dtype
- *                              combination).
+ *                              combination, page_table_stride * 16 above
+ *                              2^30 tokens).
  *   ATTN_ERR_WORKSPACE_TOO_SMALL  decode workspace below the queried size.
  *   ATTN_ERR_DEVICE            no usable gfx950 device, or a HIP error while
  *                              enqueuing (its text in *err).
@@ -186,7 +187,18 @@ typedef struct {
 /* ABI version of the loaded library (ATTN_ABI_VERSION). */
 int attn_abi_version(void);
 
-/* Open device `hip_device` (must be gfx950).  Caches CU count and LDS size. */
+/* Open device `hip_device` (must be gfx950) and return an opaque context in
+ * *ctx (Geramy/LSE README, libLSE C API section: a caller opens the library
+ * once and gets an opaque handle, every later call takes that handle and
+ * returns a status, and a failed open reports its reason through an error
+ * string).  The context caches the device facts the kernels are shaped by
+ * (CU count, LDS per workgroup, architecture), since the pages choose kernel
+ * shapes from device facts (Geramy/LSE summary page, first paragraph) and plan
+ * split attention from the device's limits (Geramy/LSE releases, v0.4.20
+ * "automatic split attention": LDS check).  On failure *ctx is NULL and the
+ * status is ATTN_ERR_DEVICE (no HIP device, index out of range, not gfx950)
+ * or ATTN_ERR_INVALID_ARGUMENT (ctx NULL).  The caller releases the context
+ * with attn_close. */
 attn_status attn_open(int hip_device, attn_ctx **ctx, char **err);
 
 /* A context for planning and argument checking only, describing a device
@@ -194,9 +206,17 @@ attn_status attn_open(int hip_device, attn_ctx **ctx, char **err);
  * then returns ATTN_ERR_DEVICE instead of enqueuing work. */
 attn_status attn_open_host_only(int num_cus, attn_ctx **ctx, char **err);
 
+/* Release a context from attn_open or attn_open_host_only (the close half of
+ * the open/close pair of the libLSE C API section of the Geramy/LSE README).
+ * NULL is ignored.  The caller must not close a context while work enqueued
+ * with it may still use it from another thread; work already on a stream
+ * does not reference the context. */
 void attn_close(attn_ctx *ctx);
 
-/* Release a string returned through an `err` argument. */
+/* Release a string the library returned through an `err` argument (Geramy/LSE
+ * README, libLSE C API section: strings the library hands out are released
+ * with the library's own free function, not the caller's allocator).  NULL is
+ * ignored. */
 void attn_free(void *p);
 
 /* Decode plan: number of KV partitions, tokens per partition and the
@@ -278,7 +298,18 @@ attn_status attn_kv_append(attn_ctx *ctx, const attn_kv *kv, const attn_kv_rows 
  * dequantise them exactly as the attention kernels do, into FP32 arrays
  * k_out, v_out of [num_kv_heads][seq_len][head_dim] (device memory): each
  * value is (code value * per-vector scale) * per-tensor scale, evaluated in
- * FP32 in that order (the per-vector factor only where the cache has one). */
+ * FP32 in that order (the per-vector factor only where the cache has one).
+ * The operation is the read half of the paged cache: K/V kept in pages of a
+ * pool in fp32/fp16/bf16/fp8/bf8 storage, fp8 and bf8 with their scales
+ * (Geramy/LSE README, "K/V storage" paragraph and table), reached through
+ * fragment addresses where the pool is fragmented (Geramy/LSE releases,
+ * v0.4.20 "K/V memory management"); the pages check the cache's contents
+ * against CPU references (v0.4.20, "Correctness"), which is what the hook is
+ * for.  Arguments: b < batch of the page table, 0 <= seq_len <=
+ * page_table_stride * 16 (tokens gathered; seq_lens is not read), k_out and
+ * v_out caller-owned device buffers of num_kv_heads * seq_len * head_dim
+ * floats.  Errors as for the attention calls (ATTN_ERR_INVALID_ARGUMENT for
+ * NULL outputs, negative or out-of-range b / seq_len). */
 attn_status attn_debug_gather_kv(attn_ctx *ctx, const attn_kv *kv, int32_t b, int32_t seq_len,
                                  float *k_out, float *v_out, void *hip_stream, char **err);
 

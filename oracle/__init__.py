@@ -188,7 +188,7 @@ def gather(p, b: int, g: int):
     """Logical (dequantised, scaled) K and V of sequence b, KV head g: [L][d] float64."""
     lib = _load()
     op = p if isinstance(p, OracleProblem) else OracleProblem(p)
-    L = int(op.lens[b])
+    L = min(int(op.lens[b]), op.pt.shape[1] * op.k.shape[2])   # clamped to the capacity
     d = op.p.head_dim
     k = np.zeros((L, d), dtype=np.float64)
     v = np.zeros((L, d), dtype=np.float64)

@@ -35,6 +35,11 @@
  *   block qb (qb from the absolute position), entries outside the mask's
  *   extent count as 0; mh = 0 for one mask head, else the KV head;
  *   a row with no allowed key has o = 0 and lse = sink (or -inf);
+ *   a sequence holds at most as many keys as its page-table row addresses
+ *   (page_table_stride * page_size): a longer seq_lens entry counts as that
+ *   capacity (the partition count of a split follows the K/V table's
+ *   capacity, Geramy/LSE releases v0.4.20 "automatic split attention", so
+ *   no key lies beyond it);
  *   FP8 is OCP e4m3fn (bias 7, no infinities, S.1111.111 is NaN) and BF8
  *   is OCP e5m2 (bias 15, with infinities), each times the per-tensor scale
  *   and, where the cache carries them, the FP32 scale of its (token, head)
@@ -159,9 +164,16 @@ static double value_at(const orc_problem *P, int b, int g, int64_t j, int c) {
          P->v_scale;
 }
 
+/* keys of sequence b: its seq_lens entry, at most the page table's capacity */
+static int64_t len_of(const orc_problem *P, int b) {
+  int64_t L = P->seq_lens[b];
+  int64_t cap = (int64_t)P->page_table_stride * P->page_size;
+  return L < cap ? L : cap;
+}
+
 /* K and V of sequence b, KV head g as logical [L][d] FP64 arrays */
 void orc_gather(const orc_problem *P, int b, int g, double *k_out, double *v_out) {
-  int64_t L = P->seq_lens[b];
+  int64_t L = len_of(P, b);
   int d = P->head_dim;
   for (int64_t j = 0; j < L; ++j)
     for (int c = 0; c < d; ++c) {
@@ -218,7 +230,7 @@ static double score(const orc_problem *P, const double *q, int b, int g, int64_t
 void orc_attend_partial(const orc_problem *P, int b, int i, int h, int64_t j0, int64_t j1,
                         double *o, double *m_out, double *l_out) {
   int G = P->num_q_heads / P->num_kv_heads, g = h / G, d = P->head_dim;
-  int64_t L = P->seq_lens[b], pos = L - rows_of(P, b) + i;
+  int64_t L = len_of(P, b), pos = L - rows_of(P, b) + i;
   if (j1 > L) j1 = L;
   double q[1024];
   load_query(P, b, i, h, q);
@@ -269,7 +281,7 @@ void orc_merge(int n, int d, const double *o_parts, const double *m, const doubl
 static void attend_row(const orc_problem *P, int b, int i, int h, double *o, double *lse,
                        double *s_buf) {
   int G = P->num_q_heads / P->num_kv_heads, g = h / G, d = P->head_dim;
-  int64_t L = P->seq_lens[b], pos = L - rows_of(P, b) + i;
+  int64_t L = len_of(P, b), pos = L - rows_of(P, b) + i;
   double sink = P->sinks ? (double)P->sinks[h] : -INFINITY;
   if (i >= rows_of(P, b)) {            /* no such row: marked NaN (not part of the output) */
     for (int c = 0; c < d; ++c) o[c] = NAN;
@@ -314,7 +326,7 @@ static void *run_job(void *arg) {
   orc_job *J = (orc_job *)arg;
   int64_t maxL = 0;
   for (int b = 0; b < J->P->batch; ++b)
-    if (J->P->seq_lens[b] > maxL) maxL = J->P->seq_lens[b];
+    if (len_of(J->P, b) > maxL) maxL = len_of(J->P, b);
   double *s_buf = (double *)malloc(sizeof(double) * (size_t)(maxL > 0 ? maxL : 1));
   for (int64_t r = J->first; r < J->nrows; r += J->step) {
     const int32_t *t = J->rows + 3 * r;

@@ -353,6 +353,16 @@ def _stream_ptr(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _torch_stream(stream, device) -> torch.cuda.Stream:
+    """The stream a convenience call enqueues on, as a torch stream object (a raw
+    handle is wrapped), so that its temporaries are allocated on that stream."""
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
 # ---- the C ABI calls ----------------------------------------------------------------
 
 def attn_paged_decode_plan(ctx: Context, io: attn_io, kv: attn_kv, opts: attn_opts):
@@ -438,15 +448,23 @@ def paged_decode(ctx: Context, q, k_pages, v_pages, page_table, seq_lens, *, k_s
                  k_vscales=None, v_vscales=None):
     """Decode / verify rows ``q`` [B][R][Hq][d]; returns the output tensor.  With
     ``rows_per_seq`` (int32 [B]) sequence b has only its first rows_per_seq[b] rows;
-    ``k_vscales``/``v_vscales`` are per-vector scale pools of an 8-bit cache."""
-    o = out if out is not None else torch.empty(q.shape, dtype=out_dtype or q.dtype,
-                                                 device=q.device)
-    io = make_io(q, o, lse)
-    kv = make_kv(k_pages, v_pages, page_table, seq_lens, k_scale, v_scale, k_vscales, v_vscales)
-    op = make_opts(softmax_scale, sinks, None, 128, num_splits, rows_per_seq)
-    if workspace is None:
-        workspace = decode_workspace(ctx, io, kv, op, q.device)
-    attn_paged_decode(ctx, io, kv, op, workspace, stream)
+    ``k_vscales``/``v_vscales`` are per-vector scale pools of an 8-bit cache.
+
+    The call is enqueued on ``stream`` (default: the current stream).  The output
+    and a workspace this function allocates are allocated on that stream, so the
+    caching allocator does not hand the workspace to other work before the call's
+    kernels have finished with it."""
+    s = _torch_stream(stream, q.device)
+    with torch.cuda.stream(s):
+        o = out if out is not None else torch.empty(q.shape, dtype=out_dtype or q.dtype,
+                                                     device=q.device)
+        io = make_io(q, o, lse)
+        kv = make_kv(k_pages, v_pages, page_table, seq_lens, k_scale, v_scale, k_vscales,
+                     v_vscales)
+        op = make_opts(softmax_scale, sinks, None, 128, num_splits, rows_per_seq)
+        if workspace is None:
+            workspace = decode_workspace(ctx, io, kv, op, q.device)
+        attn_paged_decode(ctx, io, kv, op, workspace, s)
     return o
 
 
@@ -456,14 +474,19 @@ def prefill(ctx: Context, q, k_pages, v_pages, page_table, seq_lens, *, k_scale=
             v_vscales=None):
     """Causal (optionally block-sparse) prefill of ``q`` [B][S_q][Hq][d]; with
     ``rows_per_seq`` (int32 [B]) sequence b has only its first rows_per_seq[b] rows;
-    ``k_vscales``/``v_vscales`` are per-vector scale pools of an 8-bit cache."""
-    o = out if out is not None else torch.empty(q.shape, dtype=out_dtype or q.dtype,
-                                                 device=q.device)
-    io = make_io(q, o, lse)
-    kv = make_kv(k_pages, v_pages, page_table, seq_lens, k_scale, v_scale, k_vscales, v_vscales)
-    op = make_opts(softmax_scale, sinks, block_mask, mask_block, rows_per_seq=rows_per_seq)
-    if block_mask is None:
-        attn_prefill(ctx, io, kv, op, stream)
-    else:
-        attn_prefill_blocksparse(ctx, io, kv, op, stream)
+    ``k_vscales``/``v_vscales`` are per-vector scale pools of an 8-bit cache.  The
+    call is enqueued on ``stream`` (default: the current stream), where the output
+    is allocated too."""
+    s = _torch_stream(stream, q.device)
+    with torch.cuda.stream(s):
+        o = out if out is not None else torch.empty(q.shape, dtype=out_dtype or q.dtype,
+                                                     device=q.device)
+        io = make_io(q, o, lse)
+        kv = make_kv(k_pages, v_pages, page_table, seq_lens, k_scale, v_scale, k_vscales,
+                     v_vscales)
+        op = make_opts(softmax_scale, sinks, block_mask, mask_block, rows_per_seq=rows_per_seq)
+        if block_mask is None:
+            attn_prefill(ctx, io, kv, op, s)
+        else:
+            attn_prefill_blocksparse(ctx, io, kv, op, s)
     return o

@@ -27,6 +27,7 @@ using pa::DecodeArgs;
 using pa::PrefillArgs;
 
 constexpr int kPage = 16;
+constexpr int64_t kMaxCapacity = int64_t(1) << 30;   // tokens a page-table row may address
 
 int elt_bytes(int dt) {
   switch (dt) {
@@ -70,6 +71,10 @@ attn_status check_kv(const attn_kv *kv, char **err) {
   if (kv->head_dim < 1 || kv->page_size < 1)
     return fail(err, ATTN_ERR_INVALID_ARGUMENT, "head_dim and page_size must be >= 1");
   if (kv->page_size != kPage) return fail(err, ATTN_ERR_UNSUPPORTED, "page_size %d (only 16)", kv->page_size);
+  // token positions, partition bounds and their sums are int32 in the kernels
+  if ((int64_t)kv->page_table_stride * kPage > kMaxCapacity)
+    return fail(err, ATTN_ERR_UNSUPPORTED, "page_table_stride %d: capacity above 2^30 tokens",
+                kv->page_table_stride);
   if (kv->head_dim != 64 && kv->head_dim != 128 && kv->head_dim != 256)
     return fail(err, ATTN_ERR_UNSUPPORTED, "head_dim %d (only 64, 128 or 256)", kv->head_dim);
   if (!aligned16(kv->k_pages) || !aligned16(kv->v_pages))

@@ -50,7 +50,6 @@ struct DecodeArgs {
 // at most t_cap -- is applied here to the longest sequence of the batch, and T
 // is kept large enough that no sequence needs more than the P partitions the
 // grid has.  With the longest sequence at the capacity this is the plan's T.
-// With more than 64 sequences every lane of the calling wave must be active.
 // Every lane of the calling wave must be active.
 __device__ __forceinline__ int decode_tokens(const DecodeArgs &a) {
   if (!a.t_dyn) return a.T;

@@ -159,6 +159,8 @@ def test_host_only_context_never_enqueues(hctx):
     (lambda io, kv, op: setattr(io, "q_dtype", pa.ATTN_F16), pa.ATTN_ERR_UNSUPPORTED),
     (lambda io, kv, op: setattr(op, "block_mask", 0x800000), pa.ATTN_ERR_INVALID_ARGUMENT),
     (lambda io, kv, op: setattr(op, "num_splits", -1), pa.ATTN_ERR_INVALID_ARGUMENT),
+    # rows addressing more than 2^30 tokens (int32 positions in the kernels)
+    (lambda io, kv, op: setattr(kv, "page_table_stride", (1 << 26) + 1), pa.ATTN_ERR_UNSUPPORTED),
 ])
 def test_decode_validation(hctx, mutate, status):
     io, kv, op = _decode_args()
@@ -367,3 +369,9 @@ def test_descriptors_keep_their_tensors_alive():
     del rows
     gc.collect()
     assert wk() is None and wv() is None
+
+
+def test_capacity_at_the_limit_is_planned(hctx):
+    io, kv, op = _decode_args(B=1, R=1, Hq=8, Hkv=2, d=128, stride=1 << 26)
+    P, T, W = pa.attn_paged_decode_plan(hctx, io, kv, op)
+    assert P * T >= 1 << 30 and T <= 1 << 30

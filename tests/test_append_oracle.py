@@ -252,3 +252,32 @@ def test_append_reference_lands_where_the_gather_reads(kv_dtype):
     changed = int((kout != kcodes).any(axis=-1).sum())
     expected = sum(min(L, n_new) for L in lens) * 2
     assert changed <= expected
+
+
+@pytest.mark.parametrize("kv_dtype", [DT_BF16, DT_FP8])
+def test_append_reference_clamps_lengths_to_the_capacity(kv_dtype):
+    """seq_lens above the page table's capacity: the new rows land at the last
+    positions the table addresses, as the (independently pinned) gather reads
+    them back; earlier rows stay as they were."""
+    stride, n_new = 3, 5
+    cap = stride * 16
+    p = synth.make_decode(52, 2, 4, 2, 64, [cap, cap], 1, kv_dtype=kv_dtype, stride=stride)
+    kcodes, vcodes = synth.pool_codes(p.k_pool), synth.pool_codes(p.v_pool)
+    g = np.random.default_rng(5)
+    knew = g.standard_normal((2, n_new, 2, 64)).astype(np.float32)
+    vnew = g.standard_normal((2, n_new, 2, 64)).astype(np.float32)
+    lens_call = np.array([cap + 3, 2 ** 30], dtype=np.int32)
+    kout, vout = oracle.kv_append(kv_dtype, kcodes, vcodes, p.page_table.numpy(), lens_call,
+                                  knew, vnew, p.k_scale, p.v_scale)
+    p2 = synth.with_pool_codes(p, kout, vout)
+    for b in range(2):
+        for gg in range(2):
+            k_old, v_old = oracle.gather(p, b, gg)
+            k_new, v_new = oracle.gather(p2, b, gg)
+            assert np.array_equal(k_new[:cap - n_new], k_old[:cap - n_new])
+            assert np.array_equal(v_new[:cap - n_new], v_old[:cap - n_new])
+            for i in range(n_new):
+                kexp = oracle.decode_codes(kv_dtype, oracle.encode(kv_dtype, knew[b, i, gg], p.k_scale)) * p.k_scale
+                vexp = oracle.decode_codes(kv_dtype, oracle.encode(kv_dtype, vnew[b, i, gg], p.v_scale)) * p.v_scale
+                assert np.array_equal(k_new[cap - n_new + i], kexp)
+                assert np.array_equal(v_new[cap - n_new + i], vexp)

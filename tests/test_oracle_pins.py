@@ -384,3 +384,54 @@ def test_pages_past_the_end_are_ignored():
     p.page_table[0, 3:] = torch.tensor([40, 41, 3, 0, 1], dtype=torch.int32) % p.num_pages
     o1, l1 = oracle.attend_full(p)
     assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+# ---------------------------------------------------------------- corners of the definition
+
+@pytest.mark.parametrize("kind", ["decode", "prefill"])
+def test_lengths_beyond_capacity_count_as_the_capacity(kind):
+    """A seq_lens entry above the page table's capacity (stride * 16) counts as
+    the capacity: the rows sit at the capacity's last positions and see only
+    the keys the table addresses.  Brute force over the first `cap` keys."""
+    stride = 3
+    cap = stride * PAGE
+    if kind == "decode":
+        p = synth.make_decode(71, 2, 4, 2, 8, [cap, cap], 3, kv_dtype=DT_BF16, stride=stride,
+                              sinks=True, softmax_scale=0.4)
+    else:
+        p = synth.make_prefill(72, 2, 4, 2, 8, cap, kv_dtype=DT_BF16, sinks=True,
+                               softmax_scale=0.4)
+    ref = {(b, i, h): _brute(p, b, i, h) for b in range(2) for i in range(p.q_rows)
+           for h in range(4)}
+    p.seq_lens = torch.tensor([cap + 9, 2 ** 30], dtype=torch.int32)
+    o, lse = oracle.attend_full(p)
+    for (b, i, h), (ob, lb) in ref.items():
+        assert np.max(np.abs(o[b, i, h] - ob)) <= 1e-13
+        assert abs(lse[b, h, i] - lb) <= 1e-13
+    # the gather stops at the capacity too
+    k, v = oracle.gather(p, 1, 1)
+    assert k.shape == (cap, 8) and v.shape == (cap, 8)
+
+
+def test_mask_entries_outside_its_extent_count_as_zero():
+    """A block mask with fewer query and key blocks than the sequence has: the
+    missing entries drop their keys, exactly as explicit zeros would.  Brute
+    force on the zero-padded mask (whose extent covers every block)."""
+    S, blk = 40, 8
+    p = synth.make_blocksparse(73, 2, 4, 2, 8, S, mask_block=blk, mask_heads=2, sinks=True)
+    nb = S // blk
+    u = synth.uniform(73, 78, 2 * 2 * nb * nb).view(2, 2, nb, nb)
+    full = (u < 0.7).to(torch.uint8)
+    small = full[:, :, :3, :2].contiguous()           # 3 of 5 query blocks, 2 of 5 key blocks
+    padded = torch.zeros_like(full)
+    padded[:, :, :3, :2] = small
+    p.mask = padded
+    ref = {(b, i, h): _brute(p, b, i, h) for b in range(2) for i in range(S) for h in range(4)}
+    p.mask = small
+    o, lse = oracle.attend_full(p)
+    for (b, i, h), (ob, lb) in ref.items():
+        assert np.max(np.abs(o[b, i, h] - ob)) <= 1e-13
+        assert abs(lse[b, h, i] - lb) <= 1e-13
+    # rows of query blocks past the mask keep no key: o = 0, lse = the sink
+    assert np.all(o[:, 3 * blk:] == 0)
+    assert np.allclose(lse[:, :, 3 * blk:], p.sinks.double().numpy()[None, :, None])
