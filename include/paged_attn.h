@@ -111,7 +111,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 
 typedef enum {
   ATTN_OK = 0,
@@ -247,6 +247,27 @@ size_t attn_paged_decode_workspace_bytes(const attn_ctx *ctx, const attn_io *io,
 attn_status attn_paged_decode(attn_ctx *ctx, const attn_io *io, const attn_kv *kv,
                               const attn_opts *opts, void *workspace, size_t workspace_bytes,
                               void *hip_stream, char **err);
+
+/* Bytes of device-resident scratch behind attn_paged_decode_noalloc, per device. */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* attn_paged_decode without a caller workspace and without any allocation,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Arguments,
+ * semantics, plan and kernels are those of attn_paged_decode; the partition
+ * partials go to a device-resident scratch array of ATTN_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every device it runs on until the process ends
+ * (its address is looked up once per device by attn_open).  The call
+ * allocates and frees nothing.  A decode whose partials need more than
+ * ATTN_NOALLOC_SCRATCH_BYTES (attn_paged_decode_plan's workspace_bytes) is
+ * rejected with ATTN_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.
+ * Every call on a device shares that device's scratch: calls that can run at
+ * the same time on one device (other streams, other threads, other contexts
+ * of the same device) race and must be serialised by the caller; consecutive
+ * calls on one stream are fine.  A host-only context returns ATTN_ERR_DEVICE
+ * after validation and planning. */
+attn_status attn_paged_decode_noalloc(attn_ctx *ctx, const attn_io *io, const attn_kv *kv,
+                                      const attn_opts *opts, void *hip_stream, char **err);
 
 /* Causal prefill (q_rows rows at the end of each sequence, q_rows <= seq_len
  * expected).  K/V F16, BF16, FP8 or BF8; Q F16/BF16 (equal to K/V for 16-bit

@@ -28,11 +28,13 @@ ATTN_F32, ATTN_F16, ATTN_BF16, ATTN_FP8_E4M3, ATTN_BF8_E5M2 = 0, 1, 2, 3, 4
 _DT = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16,
        torch.float8_e4m3fn: ATTN_FP8_E4M3, torch.float8_e5m2: ATTN_BF8_E5M2}
 
-ABI_VERSION = 4   # include/paged_attn.h ATTN_ABI_VERSION
+ABI_VERSION = 5   # include/paged_attn.h ATTN_ABI_VERSION
+NOALLOC_SCRATCH_BYTES = 16 << 20   # ATTN_NOALLOC_SCRATCH_BYTES
 
 EXPORTED = [
     "attn_abi_version", "attn_open", "attn_open_host_only", "attn_close", "attn_free",
     "attn_paged_decode_plan", "attn_paged_decode_workspace_bytes", "attn_paged_decode",
+    "attn_paged_decode_noalloc",
     "attn_prefill", "attn_prefill_blocksparse", "attn_kv_append", "attn_debug_gather_kv",
     "attn_debug_read_probe",
 ]
@@ -131,6 +133,8 @@ def load_library(path: str = LIB_PATH):
     lib.attn_paged_decode.argtypes = [vp, P(attn_io), P(attn_kv), P(attn_opts), vp,
                                       ctypes.c_size_t, vp, cp]
     lib.attn_paged_decode.restype = st
+    lib.attn_paged_decode_noalloc.argtypes = [vp, P(attn_io), P(attn_kv), P(attn_opts), vp, cp]
+    lib.attn_paged_decode_noalloc.restype = st
     for name in ("attn_prefill", "attn_prefill_blocksparse"):
         f = getattr(lib, name)
         f.argtypes = [vp, P(attn_io), P(attn_kv), P(attn_opts), vp, cp]
@@ -390,6 +394,17 @@ def attn_paged_decode(ctx: Context, io: attn_io, kv: attn_kv, opts: attn_opts,
     _check(lib.attn_paged_decode(ctx.handle, ctypes.byref(io), ctypes.byref(kv),
                                  ctypes.byref(opts), workspace.data_ptr(), nbytes,
                                  _stream_ptr(stream), ctypes.byref(err)), err)
+
+
+def attn_paged_decode_noalloc(ctx: Context, io: attn_io, kv: attn_kv, opts: attn_opts,
+                              stream=None):
+    """attn_paged_decode with the library's device-resident scratch (no workspace,
+    no allocation); calls that overlap on one device race."""
+    lib = load_library()
+    err = ctypes.c_char_p()
+    _check(lib.attn_paged_decode_noalloc(ctx.handle, ctypes.byref(io), ctypes.byref(kv),
+                                         ctypes.byref(opts), _stream_ptr(stream),
+                                         ctypes.byref(err)), err)
 
 
 def attn_prefill(ctx: Context, io: attn_io, kv: attn_kv, opts: attn_opts, stream=None):

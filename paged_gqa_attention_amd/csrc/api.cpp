@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "paged_attn.h"
@@ -19,6 +20,7 @@ struct attn_ctx {
   size_t lds_per_block;
   bool host_only;
   char arch[64];
+  void *scratch;   // this device's decode scratch array (attn_paged_decode_noalloc), or null
 };
 
 namespace {
@@ -28,6 +30,7 @@ using pa::PrefillArgs;
 
 constexpr int kPage = 16;
 constexpr int64_t kMaxCapacity = int64_t(1) << 30;   // tokens a page-table row may address
+constexpr int kMaxDevices = 64;
 
 int elt_bytes(int dt) {
   switch (dt) {
@@ -282,6 +285,27 @@ struct DeviceGuard {
   }
 };
 
+// Device address of the decode scratch array on device `dev`, looked up once
+// per device with that device current and kept for every later context.
+attn_status device_scratch(int dev, void **ptr, char **err) {
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  if (dev < 0 || dev >= kMaxDevices) return fail(err, ATTN_ERR_DEVICE, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    DeviceGuard g(dev);
+    if (!g.ok) return fail(err, ATTN_ERR_DEVICE, "cannot select device %d", dev);
+    void *p = nullptr;
+    const hipError_t e = pa::decode_scratch_address(&p);
+    if (e != hipSuccess || !p)
+      return fail(err, ATTN_ERR_DEVICE, "hipGetSymbolAddress(decode scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return ATTN_OK;
+}
+
 attn_status launched(hipError_t e, char **err, const char *what) {
   if (e != hipSuccess) return fail(err, ATTN_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
   return ATTN_OK;
@@ -352,6 +376,50 @@ attn_status prefill_common(attn_ctx *ctx, const attn_io *io, const attn_kv *kv, 
   return launched(pa::launch_prefill(a, (hipStream_t)stream), err, "prefill launch");
 }
 
+// Enqueue a planned decode with its partials in `workspace` (>= pl.ws_bytes).
+attn_status decode_enqueue(attn_ctx *ctx, const attn_io *io, const attn_kv *kv, const attn_opts *opts,
+                           const DecodePlan &pl, void *workspace, void *hip_stream, char **err) {
+  DecodeArgs a{};
+  a.q = io->q;
+  a.q_sb = io->q_stride_b; a.q_sr = io->q_stride_row; a.q_sh = io->q_stride_head;
+  a.k = kv->k_pages; a.v = kv->v_pages;
+  a.k_sp = kv->k_stride_page; a.k_sh = kv->k_stride_head;
+  a.v_sp = kv->v_stride_page; a.v_sh = kv->v_stride_head;
+  a.page_table = kv->page_table;
+  a.pt_stride = kv->page_table_stride;
+  a.capacity = (int32_t)std::min<int64_t>((int64_t)kv->page_table_stride * kPage, INT32_MAX);
+  a.lens = kv->seq_lens;
+  a.B = io->batch; a.R = io->q_rows; a.Hq = io->num_q_heads; a.Hkv = kv->num_kv_heads;
+  a.G = io->num_q_heads / kv->num_kv_heads; a.D = kv->head_dim;
+  a.rows = pl.rows;
+  a.kv_dtype = kv->dtype; a.q_dtype = io->q_dtype; a.o_dtype = io->o_dtype;
+  a.score_scale = score_scale(opts, kv);
+  a.v_scale = kv->v_scale;
+  a.sinks = opts->sinks;
+  a.o = io->o;
+  a.o_sb = io->o_stride_b; a.o_sr = io->o_stride_row; a.o_sh = io->o_stride_head;
+  a.lse = io->lse;
+  a.rows_b = opts->rows_per_seq;
+  a.k_vs = kv->k_vscales; a.v_vs = kv->v_vscales;
+  a.vs_sp = kv->vscale_stride_page; a.vs_sh = kv->vscale_stride_head;
+  a.k_frag = kv->k_fragments; a.v_frag = kv->v_fragments;
+  a.frag_shift = kv->fragment_pages_log2;
+  a.P = pl.P; a.T = pl.T;
+  a.t_dyn = pl.t_dyn; a.t_target = pl.t_target; a.t_min = pl.t_min; a.t_cap = pl.t_cap;
+  a.row_blocks = pl.row_blocks;
+  a.ws_o = reinterpret_cast<float *>(workspace);
+  a.ws_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + pl.ws_o_bytes);
+  if (ctx->host_only) return fail(err, ATTN_ERR_DEVICE, "host-only context: nothing enqueued");
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return fail(err, ATTN_ERR_DEVICE, "cannot select device %d", ctx->device);
+  hipStream_t s = (hipStream_t)hip_stream;
+  attn_status st = launched(pl.wide ? pa::launch_decode_wide(a, s)
+                : pl.mfma ? pa::launch_decode_mfma(a, s) : pa::launch_decode_valu(a, s),
+                err, "decode partial launch");
+  if (st != ATTN_OK) return st;
+  return launched(pa::launch_decode_merge(a, s), err, "decode merge launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -379,6 +447,11 @@ attn_status attn_open(int hip_device, attn_ctx **ctx, char **err) {
   c->lds_per_block = prop.sharedMemPerBlock;
   c->host_only = false;
   snprintf(c->arch, sizeof c->arch, "%s", prop.gcnArchName);
+  attn_status st = device_scratch(hip_device, &c->scratch, err);
+  if (st != ATTN_OK) {
+    free(c);
+    return st;
+  }
   *ctx = c;
   return ATTN_OK;
 }
@@ -428,45 +501,23 @@ attn_status attn_paged_decode(attn_ctx *ctx, const attn_io *io, const attn_kv *k
   if (!aligned16(workspace)) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
   if (workspace_bytes < pl.ws_bytes)
     return fail(err, ATTN_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, pl.ws_bytes);
-  DecodeArgs a{};
-  a.q = io->q;
-  a.q_sb = io->q_stride_b; a.q_sr = io->q_stride_row; a.q_sh = io->q_stride_head;
-  a.k = kv->k_pages; a.v = kv->v_pages;
-  a.k_sp = kv->k_stride_page; a.k_sh = kv->k_stride_head;
-  a.v_sp = kv->v_stride_page; a.v_sh = kv->v_stride_head;
-  a.page_table = kv->page_table;
-  a.pt_stride = kv->page_table_stride;
-  a.capacity = (int32_t)std::min<int64_t>((int64_t)kv->page_table_stride * kPage, INT32_MAX);
-  a.lens = kv->seq_lens;
-  a.B = io->batch; a.R = io->q_rows; a.Hq = io->num_q_heads; a.Hkv = kv->num_kv_heads;
-  a.G = io->num_q_heads / kv->num_kv_heads; a.D = kv->head_dim;
-  a.rows = pl.rows;
-  a.kv_dtype = kv->dtype; a.q_dtype = io->q_dtype; a.o_dtype = io->o_dtype;
-  a.score_scale = score_scale(opts, kv);
-  a.v_scale = kv->v_scale;
-  a.sinks = opts->sinks;
-  a.o = io->o;
-  a.o_sb = io->o_stride_b; a.o_sr = io->o_stride_row; a.o_sh = io->o_stride_head;
-  a.lse = io->lse;
-  a.rows_b = opts->rows_per_seq;
-  a.k_vs = kv->k_vscales; a.v_vs = kv->v_vscales;
-  a.vs_sp = kv->vscale_stride_page; a.vs_sh = kv->vscale_stride_head;
-  a.k_frag = kv->k_fragments; a.v_frag = kv->v_fragments;
-  a.frag_shift = kv->fragment_pages_log2;
-  a.P = pl.P; a.T = pl.T;
-  a.t_dyn = pl.t_dyn; a.t_target = pl.t_target; a.t_min = pl.t_min; a.t_cap = pl.t_cap;
-  a.row_blocks = pl.row_blocks;
-  a.ws_o = reinterpret_cast<float *>(workspace);
-  a.ws_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + pl.ws_o_bytes);
-  if (ctx->host_only) return fail(err, ATTN_ERR_DEVICE, "host-only context: nothing enqueued");
-  DeviceGuard g(ctx->device);
-  if (!g.ok) return fail(err, ATTN_ERR_DEVICE, "cannot select device %d", ctx->device);
-  hipStream_t s = (hipStream_t)hip_stream;
-  st = launched(pl.wide ? pa::launch_decode_wide(a, s)
-                : pl.mfma ? pa::launch_decode_mfma(a, s) : pa::launch_decode_valu(a, s),
-                err, "decode partial launch");
+  return decode_enqueue(ctx, io, kv, opts, pl, workspace, hip_stream, err);
+}
+
+attn_status attn_paged_decode_noalloc(attn_ctx *ctx, const attn_io *io, const attn_kv *kv,
+                                      const attn_opts *opts, void *hip_stream, char **err) {
+  DecodePlan pl;
+  attn_status st = plan_decode(ctx, io, kv, opts, &pl, err);
   if (st != ATTN_OK) return st;
-  return launched(pa::launch_decode_merge(a, s), err, "decode merge launch");
+  static_assert(pa::kDecodeScratchBytes == ATTN_NOALLOC_SCRATCH_BYTES, "scratch size");
+  if (pl.ws_bytes > pa::kDecodeScratchBytes)
+    return fail(err, ATTN_ERR_WORKSPACE_TOO_SMALL,
+                "this decode needs %zu bytes of partials; the library's device-resident scratch "
+                "holds %zu (ATTN_NOALLOC_SCRATCH_BYTES): use attn_paged_decode with a workspace",
+                pl.ws_bytes, (size_t)pa::kDecodeScratchBytes);
+  if (ctx->host_only) return fail(err, ATTN_ERR_DEVICE, "host-only context: nothing enqueued");
+  if (!ctx->scratch) return fail(err, ATTN_ERR_DEVICE, "no device scratch for device %d", ctx->device);
+  return decode_enqueue(ctx, io, kv, opts, pl, ctx->scratch, hip_stream, err);
 }
 
 attn_status attn_prefill(attn_ctx *ctx, const attn_io *io, const attn_kv *kv, const attn_opts *opts,

@@ -142,6 +142,10 @@ hipError_t launch_kv_append(const AppendArgs &a, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t s);
+// Device address of the file-scope decode scratch array of the current device
+// (kDecodeScratchBytes, 256-byte aligned); call with that device current.
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+hipError_t decode_scratch_address(void **ptr);
 bool decode_mfma_supported(int kv_dtype, int q_dtype, int D, int rows);
 bool decode_valu_supported(int kv_dtype, int q_dtype, int D);
 // resident workgroups per CU of the partial kernel selected for these arguments

@@ -1153,6 +1153,23 @@ hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---- device-resident decode workspace -------------------------------------------
+// attn_paged_decode_noalloc keeps its partition partials in this file-scope
+// array instead of a caller workspace, for callers that cannot allocate
+// device memory.  Every device the library runs on holds its own copy until
+// the process ends, and every call on a device shares it: calls that overlap
+// on one device race.  The kernels never read what they did not write in the
+// same call (empty partitions are not merged), so nothing needs clearing.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch_address(void **ptr) {
+  void *p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  *ptr = p;
+  return hipSuccess;
+}
+
 hipError_t launch_debug_gather(const void *k, const void *v, int64_t k_sp, int64_t k_sh,
                                int64_t v_sp, int64_t v_sh, int kv_dtype, int Hkv, int D,
                                float k_scale, float v_scale, const float *k_vs,

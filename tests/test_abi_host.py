@@ -34,7 +34,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.attn_abi_version() == 4
+    assert lib.attn_abi_version() == 5
 
 
 def test_open_without_a_gpu_is_a_device_error(lib):
@@ -375,3 +375,19 @@ def test_capacity_at_the_limit_is_planned(hctx):
     io, kv, op = _decode_args(B=1, R=1, Hq=8, Hkv=2, d=128, stride=1 << 26)
     P, T, W = pa.attn_paged_decode_plan(hctx, io, kv, op)
     assert P * T >= 1 << 30 and T <= 1 << 30
+
+
+def test_noalloc_decode_validates_and_bounds_its_scratch(hctx):
+    io, kv, op = _decode_args()
+    assert _status(lambda: pa.attn_paged_decode_noalloc(hctx, io, kv, op, stream=0)) == \
+        pa.ATTN_ERR_DEVICE
+    io.q_rows = 9
+    assert _status(lambda: pa.attn_paged_decode_noalloc(hctx, io, kv, op, stream=0)) == \
+        pa.ATTN_ERR_INVALID_ARGUMENT
+    # partials beyond the device-resident scratch: rejected before anything else
+    io, kv, op = _decode_args(B=16, R=1, Hq=32, Hkv=8, d=128, stride=1024)
+    op.num_splits = 128
+    _, _, need = pa.attn_paged_decode_plan(hctx, io, kv, op)
+    assert need > pa.NOALLOC_SCRATCH_BYTES
+    assert _status(lambda: pa.attn_paged_decode_noalloc(hctx, io, kv, op, stream=0)) == \
+        pa.ATTN_ERR_WORKSPACE_TOO_SMALL
