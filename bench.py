@@ -1,7 +1,7 @@
 """Benchmark of the paged GQA attention hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--all]
-    python bench.py --only decode|prefill|copy [--steps K] [--warmup W]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
+    python bench.py --only decode|prefill|copy|append|d256|config2|config4|config5
     python bench.py --pmc-summary FETCH_DIR WRITE_DIR
     python bench.py --counter-summary PMC_DIR
 
@@ -17,8 +17,12 @@ Inputs are generated on the GPU with the seeded counter-based generator and
 are resident in HBM before timing.  Each timed region is K calls on one
 stream, bracketed by synchronisation, timed with HIP events on that stream.
 The FP64 CPU oracle is timed on a bounded sample of rows of the same
-workload (``cpu_baseline``).  ``--all`` also prints the other workloads to
-stderr (not part of the JSON line).
+workload (``cpu_baseline``).  The line also carries every other workload:
+``config2`` (decode/verify at R = 1, 4, 8, mixed and uniform lengths),
+``config4`` (all nine causal-prefill points), ``config5`` (block-sparse
+prefill and the dense call at its shape), the 8-bit formats, fragments,
+head_dim 256, the K/V append and one GPU's head-parallel shard, each with
+its roofline.
 
 ``--only`` runs one workload without the CPU baseline, for profiling under
 rocprofv3 (``copy`` is a 1 GiB device-to-device copy whose counter readings
@@ -264,6 +268,29 @@ def prefill_setup(ctx, p, dev="cuda"):
     return (lambda: fn(ctx, io, kv, op)), (io, kv, op)
 
 
+def _host_cpu():
+    """(CPU model, CPUs the host reports) for the CPU-baseline record."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
+def _cpu_record(value, unit, used, sample, single):
+    model, ncpu = _host_cpu()
+    return {"value": value, "unit": unit, "cores": int(used), "kind": "oracle", "sample": sample,
+            "cpu_model": model, "host_cpus": ncpu,
+            "threads_note": f"{CPU_THREADS} threads: the CPU share of one GPU on this host "
+                            f"(it reports {ncpu} CPUs, shared by its GPUs)",
+            "single_thread": single}
+
+
 def cpu_baseline_decode(p, budget_s: float = 12.0):
     """Oracle on a bounded sample of rows, scaled to GB/s of the same workload."""
     import numpy as np
@@ -292,11 +319,11 @@ def cpu_baseline_decode(p, budget_s: float = 12.0):
     oracle.attend(op, sel1, threads=1)
     dt1 = time.perf_counter() - t0
     gbs1 = total * (len(sel1) / len(rows_all)) / dt1 / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(used), "kind": "oracle",
-            "sample": f"{n2} of {len(rows_all)} output rows (random, seed 0), {dt:.1f} s; "
-                      f"bytes scaled by the sampled fraction of rows",
-            "single_thread": {"value": round(gbs1, 4), "unit": "GB/s",
-                              "sample": f"{len(sel1)} rows of the same sample, {dt1:.2f} s"}}
+    return _cpu_record(round(gbs, 4), "GB/s", used,
+                       f"{n2} of {len(rows_all)} output rows (random, seed 0), {dt:.1f} s; "
+                       f"bytes scaled by the sampled fraction of rows",
+                       {"value": round(gbs1, 4), "unit": "GB/s",
+                        "sample": f"{len(sel1)} rows of the same sample, {dt1:.2f} s"})
 
 
 def cpu_baseline_prefill(p, budget_s: float = 8.0):
@@ -321,10 +348,18 @@ def cpu_baseline_prefill(p, budget_s: float = 8.0):
     _, _, used = oracle.attend(op, sel, threads=CPU_THREADS)
     dt = time.perf_counter() - t0
     # flops of the sampled rows: row i of a sequence of length L sees L - S + i + 1 keys
-    keys = sum(int(p.seq_lens[b]) - S + int(i) + 1 for b, i, _ in sel)
-    flops = 4 * p.head_dim * keys
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(used),
-            "kind": "oracle", "sample": f"{n2} random output rows, {dt:.1f} s"}
+    def flops_of(rows):
+        return 4 * p.head_dim * sum(int(p.seq_lens[b]) - S + int(i) + 1 for b, i, _ in rows)
+    flops = flops_of(sel)
+    # one thread on a fixed subset (the first 16 rows of the sample)
+    sel1 = sel[:16]
+    t0 = time.perf_counter()
+    oracle.attend(op, sel1, threads=1)
+    dt1 = time.perf_counter() - t0
+    return _cpu_record(round(flops / dt / 1e12, 6), "TFLOP/s", used,
+                       f"{n2} random output rows, {dt:.1f} s",
+                       {"value": round(flops_of(sel1) / dt1 / 1e12, 7), "unit": "TFLOP/s",
+                        "sample": f"{len(sel1)} rows of the same sample, {dt1:.2f} s"})
 
 
 def main():
@@ -333,8 +368,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--all", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "copy", "append", "d256"])
+    ap.add_argument("--only", choices=["decode", "prefill", "copy", "append", "d256", "config2",
+                                       "config4", "config5"])
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--counter-summary", metavar="DIR")
     args = ap.parse_args()
@@ -376,6 +411,11 @@ def main():
         return
     if args.only == "d256":
         print(json.dumps(wide_summary(ctx, args)), flush=True)
+        return
+    if args.only in ("config2", "config4", "config5"):
+        fn = {"config2": config2_summary, "config4": config4_summary,
+              "config5": config5_summary}[args.only]
+        print(json.dumps(fn(ctx, args)), flush=True)
         return
     t_gen = time.perf_counter()
     p = synth.config2(q_rows=1, lens=[16384] * 16, device=dev)
@@ -442,10 +482,106 @@ def main():
         "fragments": fragments_summary(ctx, args),
         "head_dim_256": wide_summary(ctx, args),
         "shard": shard_summary(ctx, args),
+        "config2": config2_summary(ctx, args),
+        "config4": config4_summary(ctx, args),
+        "config5": config5_summary(ctx, args),
     }
-    if args.all:
-        extra(ctx, args)
     print(json.dumps(line), flush=True)
+
+
+def _kernel_of_decode(rows_per_kv_head, d=128):
+    return "decode_valu + decode_merge" if rows_per_kv_head <= 8 else \
+        ("decode_mfma + decode_merge" if d != 256 else "attn_wide (verify) + decode_merge")
+
+
+def config2_summary(ctx, args):
+    """Decode / verify as specified: 16 sequences, Hq 32 / Hkv 8, d 128, bf16,
+    page-table stride 1,024, R = 1, 4, 8 query rows, lengths U[8192, 16384]
+    (seed 202) and, for comparison, all 16,384.  HBM roofline per call."""
+    import torch
+    import synth
+    from paged_gqa_attention_amd import accounting as acc
+    out = {"workload": "decode/verify B=16, Hq=32, Hkv=8, d=128, bf16 K/V/Q/O, 16-token pages, "
+                       "page-table stride 1024"}
+    for tag, lens in (("mixed", None), ("uniform16k", [16384] * 16)):
+        for R in (1, 4, 8):
+            p = synth.config2(q_rows=R, lens=lens, device="cuda")
+            call, (P, T), keep = decode_setup(ctx, p, "cuda")
+            ms = time_calls(call, args.steps, args.warmup)
+            b = acc.decode_bytes(p.seq_lens.tolist(), R, 32, 8, 128, 2, 2, 2)
+            gbs = b / (ms * 1e-3) / 1e9
+            out[f"{tag}_R{R}"] = {
+                "lengths": "U[8192,16384] seed 202" if lens is None else "16384",
+                "ms": round(ms, 5), "splits": P, "tokens_per_split": T,
+                "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                             "bytes_per_call": b, "kernel": _kernel_of_decode(4 * R)}}
+            del keep, call, p
+    torch.cuda.empty_cache()
+    return out
+
+
+def config4_summary(ctx, args):
+    """Causal prefill with sinks at all nine (S, B) points: Hq 64 / Hkv 8, d 64,
+    bf16, S in {1K, 4K, 8K}, B in {1, 4, 16}.  MFMA roofline per call."""
+    import torch
+    import synth
+    from paged_gqa_attention_amd import accounting as acc
+    out = {"workload": "causal prefill + sinks, Hq=64, Hkv=8, d=64, bf16, 16-token shuffled pages",
+           "kernel": "prefill_mfma<bf16,bf16,64,2,false,false>"}
+    for S in (1024, 4096, 8192):
+        for B in (1, 4, 16):
+            p = synth.config4(seq_len=S, batch=B, device="cuda")
+            call, keep = prefill_setup(ctx, p, "cuda")
+            ms = time_calls(call, max(3, args.steps // 2), max(1, args.warmup // 2))
+            f = acc.attention_flops(acc.causal_pairs(S, S), 64, 64, B)
+            tfs = f / (ms * 1e-3) / 1e12
+            out[f"S{S}_B{B}"] = {"ms": round(ms, 4),
+                                 "roofline": {"bound": "mfma", "achieved": round(tfs, 1),
+                                              "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                              "frac": round(tfs / BF16_PEAK_TFLOPS, 4),
+                                              "flops_per_call": f}}
+            del keep, call, p
+            torch.cuda.empty_cache()
+    return out
+
+
+def config5_summary(ctx, args):
+    """Block-sparse prefill: 1 x 32,768 tokens, Hq 32 / Hkv 8, d 128, bf16, 128-token
+    mask blocks keeping block 0, the diagonal and a Bernoulli(0.1) draw of the
+    rest (seed 505).  TFLOP/s on the kept (query, key) pairs; the dense causal
+    call at the same shape for comparison."""
+    import torch
+    import synth
+    from paged_gqa_attention_amd import accounting as acc
+    p = synth.config5(device="cuda")
+    call, keep = prefill_setup(ctx, p, "cuda")
+    ms = time_calls(call, max(3, args.steps // 2), max(1, args.warmup // 2))
+    m = p.mask[0, 0].cpu()
+    rows = [m[qb].nonzero().flatten().tolist() for qb in range(m.shape[0])]
+    pairs = acc.mask_pairs(rows, 32768, 128)
+    f = acc.attention_flops(pairs, 32, 128, 1)
+    tfs = f / (ms * 1e-3) / 1e12
+    del keep, call
+    p.mask = None
+    dcall, dkeep = prefill_setup(ctx, p, "cuda")
+    dms = time_calls(dcall, 3, 1)
+    df = acc.attention_flops(acc.causal_pairs(32768, 32768), 32, 128, 1)
+    dtfs = df / (dms * 1e-3) / 1e12
+    del dkeep, dcall, p
+    torch.cuda.empty_cache()
+    return {"workload": "block-sparse prefill B=1, S=32768, Hq=32, Hkv=8, d=128, bf16, "
+                        "mask block 128, keep block 0 + diagonal + Bernoulli(0.1)",
+            "kernel": "prefill_mfma<bf16,bf16,128,2,true,false>",
+            "ms": round(ms, 4), "kept_pairs_per_head": pairs,
+            "kept_fraction_of_causal": round(pairs / acc.causal_pairs(32768, 32768), 4),
+            "roofline": {"bound": "mfma", "achieved": round(tfs, 1), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tfs / BF16_PEAK_TFLOPS, 4),
+                         "flops_per_call": f},
+            "dense_same_shape": {"ms": round(dms, 4), "TFLOPs": round(dtfs, 1),
+                                 "frac": round(dtfs / BF16_PEAK_TFLOPS, 4),
+                                 "flops_per_call": df},
+            "sparse_speedup_vs_dense": round(dms / ms, 3)}
 
 
 def shard_summary(ctx, args):
@@ -614,68 +750,6 @@ def only_prefill(ctx, args):
     flops = acc.attention_flops(acc.causal_pairs(8192, 8192), 64, 64, 16)
     print(json.dumps({"workload": "prefill", "ms": round(pms, 4),
                       "TFLOP/s": round(flops / (pms * 1e-3) / 1e12, 1)}), flush=True)
-
-
-def extra(ctx, args):
-    """The other workloads, printed to stderr as one JSON object per line."""
-    import torch
-    import synth
-    from paged_gqa_attention_amd import accounting as acc
-    dev = "cuda"
-    for lens, tag in ((None, "L~U[8K,16K]"), ([16384] * 16, "L=16384")):
-        for R in (1, 4, 8):
-            p = synth.config2(q_rows=R, lens=lens, device=dev)
-            call, (P, T), keep = decode_setup(ctx, p, dev)
-            ms = time_calls(call, args.steps, args.warmup)
-            b = acc.decode_bytes(p.seq_lens.tolist(), R, 32, 8, 128, 2, 2, 2)
-            print(json.dumps({"workload": f"decode/verify B=16 {tag} R={R}", "ms": round(ms, 4),
-                              "GB/s": round(b / ms / 1e6, 1), "splits": P}), file=sys.stderr,
-                  flush=True)
-            del keep, call, p
-    # sequences far shorter than the page table's capacity (16 x 4,096 tokens in
-    # 65,536-token tables): the kernels size partitions from the longest one
-    for R in (1, 4):
-        p = synth.make_decode(208, 16, 32, 8, 128, [4096] * 16, R, kv_dtype=synth.DT_BF16,
-                              stride=4096, device=dev)
-        call, (P, T), keep = decode_setup(ctx, p, dev)
-        ms = time_calls(call, args.steps, args.warmup)
-        b = acc.decode_bytes(p.seq_lens.tolist(), R, 32, 8, 128, 2, 2, 2)
-        print(json.dumps({"workload": f"decode/verify B=16 L=4096 in 64K tables R={R}",
-                          "ms": round(ms, 4), "GB/s": round(b / ms / 1e6, 1),
-                          "planned_splits": P}), file=sys.stderr, flush=True)
-        del keep, call, p
-    p = synth.config3(device=dev)
-    call, (P, T), keep = decode_setup(ctx, p, dev)
-    ms = time_calls(call, args.steps, args.warmup)
-    b = acc.decode_bytes(p.seq_lens.tolist(), 4, 32, 8, 128, 3, 2, 2)
-    print(json.dumps({"workload": "fp8 decode B=4 L=65536 R=4", "ms": round(ms, 4),
-                      "GB/s": round(b / ms / 1e6, 1), "splits": P}), file=sys.stderr, flush=True)
-    del keep, call, p
-    torch.cuda.empty_cache()
-    for S in (1024, 4096, 8192):
-        for B in (1, 4, 16):
-            p = synth.config4(seq_len=S, batch=B, device=dev)
-            call, keep = prefill_setup(ctx, p, dev)
-            ms = time_calls(call, max(3, args.steps // 2), 2)
-            f = acc.attention_flops(acc.causal_pairs(S, S), 64, 64, B)
-            print(json.dumps({"workload": f"prefill+sinks S={S} B={B}", "ms": round(ms, 4),
-                              "TFLOP/s": round(f / ms / 1e9, 1)}), file=sys.stderr, flush=True)
-            del keep, call, p
-            torch.cuda.empty_cache()
-    p = synth.config5(device=dev)
-    call, keep = prefill_setup(ctx, p, dev)
-    ms = time_calls(call, max(3, args.steps // 2), 2)
-    m = p.mask[0, 0].cpu()
-    rows = [m[qb].nonzero().flatten().tolist() for qb in range(m.shape[0])]
-    pairs = acc.mask_pairs(rows, 32768, 128)
-    f = acc.attention_flops(pairs, 32, 128, 1)
-    p.mask = None
-    dcall, dkeep = prefill_setup(ctx, p, dev)
-    dms = time_calls(dcall, 3, 1)
-    print(json.dumps({"workload": "blocksparse prefill S=32768 (kept pairs)", "ms": round(ms, 4),
-                      "TFLOP/s": round(f / ms / 1e9, 1), "dense_ms": round(dms, 4),
-                      "kept_fraction_of_causal": round(pairs / acc.causal_pairs(32768, 32768), 4)}),
-          file=sys.stderr, flush=True)
 
 
 if __name__ == "__main__":

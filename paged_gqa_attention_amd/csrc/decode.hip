@@ -855,6 +855,13 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
           if (pp + 5 * S < pp_end) load_pair(mode, pp + 5 * S, kC, vC16, vC8, sC);
         }
       }
+    } else if constexpr (NB == 4 && D == 128) {
+      // 64 rows at d 128: the accumulators and Q fragments leave room for one
+      // pair in flight (a second register set spills to scratch)
+      for (; pp < pp_end; pp += kWaves) {
+        load_pair(mode, pp, kA, vA16, vA8, sA);
+        process_pair(pp, kA, vA16, vA8, sA);
+      }
     } else {
       if (pp < pp_end) load_pair(mode, pp, kA, vA16, vA8, sA);
       if (pp + kWaves < pp_end) load_pair(mode, pp + kWaves, kB, vB16, vB8, sB);

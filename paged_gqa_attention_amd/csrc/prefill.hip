@@ -169,6 +169,13 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
   const uint8_t *mrow = MASK ? a.mask + ((int64_t)b * a.mask_heads + mh) *
                                           (int64_t)a.mask_nqb * a.mask_nkb
                              : nullptr;
+  // block mask: the rows of the tile span query blocks qb_lo .. qb_lo + 2 at
+  // most (128 rows, blocks of at least 64); each listed K/V tile carries one
+  // bit per such block (kept for that block), and a row reads the bit of its
+  // own block
+  const int qb_lo = MASK ? max(0, off + qt * kTileQ) / a.mask_block : 0;
+  const int qb_hi = MASK ? max(0, off + tile_last) / a.mask_block : 0;
+  const int rel_qb = (MASK && pos_row >= 0) ? pos_row / a.mask_block - qb_lo : 0;
 
   // ---- staging: global -> registers -> LDS.  The 4 page ids of a tile are
   // workgroup-uniform scalar loads.  Each wave's 64 consecutive 16-byte chunks
@@ -318,16 +325,12 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
 
   // ---- per-tile work of one wave ----
   const float sc = a.score_scale;
-  auto compute = [&](int t, int buf) {
+  auto compute = [&](int t, int buf, int bits) {
     const int kt0 = t * kTileK;
     if (!wave_has_rows || kt0 >= wave_key_end) return;
     bool keep = true;
     if constexpr (MASK) {
-      keep = false;
-      if (pos_row >= 0) {
-        const int qb = pos_row / a.mask_block, kb = kt0 / a.mask_block;
-        keep = qb < a.mask_nqb && kb < a.mask_nkb && mrow[(int64_t)qb * a.mask_nkb + kb] != 0;
-      }
+      keep = pos_row >= 0 && ((bits >> rel_qb) & 1);
       if (!__builtin_amdgcn_ballot_w64(keep)) return;
     }
     const uint16_t *kl = k_lds[buf];
@@ -436,38 +439,37 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
       for (int t = 0; t < nt; t += 2) {
         const int pb = t & 2;
         if (t + 2 < nt) gload(t + 2);
-        compute(t, pb);
+        compute(t, pb, 0);
         if (t + 2 < nt) lstore(t + 2, pb ^ 2);
         if (t + 3 < nt) gload(t + 3);
-        if (t + 1 < nt) compute(t + 1, pb + 1);
+        if (t + 1 < nt) compute(t + 1, pb + 1, 0);
         if (t + 3 < nt) lstore(t + 3, (pb ^ 2) + 1);
         __syncthreads();
       }
     } else {
-      // rows of the tile span query blocks [qb_lo, qb_hi]
-      const int first_row = qt * kTileQ;
-      const int qb_lo = max(0, off + first_row) / a.mask_block;
-      const int qb_hi = max(0, off + tile_last) / a.mask_block;
       for (int w0 = 0; w0 < nt; w0 += LIST) {
         const int wn = min(LIST, nt - w0);
-        // compact list of tiles in [w0, w0 + wn) that some row of the tile keeps
+        // compact list of tiles in [w0, w0 + wn) that some row of the tile
+        // keeps, each entry t | (bits << 24), bit j: kept for block qb_lo + j
         int base = 0;
         for (int c0 = 0; c0 < wn; c0 += NT) {
           const int t = w0 + c0 + tid;
-          bool kept = false;
+          int bits = 0;
           if (c0 + tid < wn) {
             const int kb = (t * kTileK) / a.mask_block;
-            for (int qb = qb_lo; qb <= qb_hi && !kept; ++qb)
-              kept = qb < a.mask_nqb && kb < a.mask_nkb && kb <= qb &&
-                     mrow[(int64_t)qb * a.mask_nkb + kb] != 0;
+            for (int qb = qb_lo; qb <= qb_hi; ++qb)
+              if (qb < a.mask_nqb && kb < a.mask_nkb && kb <= qb &&
+                  mrow[(int64_t)qb * a.mask_nkb + kb] != 0)
+                bits |= 1 << (qb - qb_lo);
           }
+          const bool kept = bits != 0;
           const uint64_t bal = __builtin_amdgcn_ballot_w64(kept);
           const int below = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
           if (lane == 0) list_count[wave] = __builtin_popcountll(bal);
           __syncthreads();
           int wbase = base;
           for (int w = 0; w < wave; ++w) wbase += list_count[w];
-          if (kept) tile_list[wbase + below] = t;
+          if (kept) tile_list[wbase + below] = t | (bits << 24);
           int tot = 0;
           for (int w = 0; w < NW; ++w) tot += list_count[w];
           __syncthreads();
@@ -476,7 +478,8 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
         const int cnt = base;
         if (cnt == 0) continue;
         // the listed tiles, two per barrier as in the unmasked loop
-        auto tl = [&](int i) { return __builtin_amdgcn_readfirstlane(tile_list[i]); };
+        auto tl = [&](int i) { return __builtin_amdgcn_readfirstlane(tile_list[i]) & 0xffffff; };
+        auto tb = [&](int i) { return __builtin_amdgcn_readfirstlane(tile_list[i]) >> 24; };
         gload(tl(0));
         lstore(tl(0), 0);
         if (cnt > 1) {
@@ -487,10 +490,10 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
         for (int idx = 0; idx < cnt; idx += 2) {
           const int pb = idx & 2;
           if (idx + 2 < cnt) gload(tl(idx + 2));
-          compute(tl(idx), pb);
+          compute(tl(idx), pb, tb(idx));
           if (idx + 2 < cnt) lstore(tl(idx + 2), pb ^ 2);
           if (idx + 3 < cnt) gload(tl(idx + 3));
-          if (idx + 1 < cnt) compute(tl(idx + 1), pb + 1);
+          if (idx + 1 < cnt) compute(tl(idx + 1), pb + 1, tb(idx + 1));
           if (idx + 3 < cnt) lstore(tl(idx + 3), (pb ^ 2) + 1);
           __syncthreads();
         }
