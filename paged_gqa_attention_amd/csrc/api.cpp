@@ -31,6 +31,8 @@ using pa::PrefillArgs;
 constexpr int kPage = 16;
 constexpr int64_t kMaxCapacity = int64_t(1) << 30;   // tokens a page-table row may address
 constexpr int kMaxDevices = 64;
+constexpr int64_t kLdsPerCu = 160 * 1024;   // gfx950 LDS per compute unit
+constexpr int64_t kSkRounds = 2;            // balanced partitions: rounds of resident workgroups
 
 int elt_bytes(int dt) {
   switch (dt) {
@@ -151,7 +153,8 @@ struct DecodePlan {
   bool wide;              // head_dim 256 with more than 8 rows per KV head
   int rows, rb, row_blocks, P, T;
   int t_dyn, t_target, t_min, t_cap;   // the device-side partition rule (DecodeArgs)
-  size_t ws_bytes, ws_o_bytes, ws_ml_bytes;
+  int sk, sk_wgs, sk_cmin, sk_unit, sk_rbw, sk_lds;   // balanced split (DecodeArgs)
+  size_t ws_bytes, ws_o_bytes, ws_ml_bytes, ws_tab_bytes;
 };
 
 constexpr int kTGran = 128;   // partition granularity (tokens)
@@ -256,14 +259,51 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
   // them in blocks as their walk reaches them)
   if (pl->wide) T = std::min<int64_t>(T, kTMax);
   T = std::min<int64_t>(T, std::min<int64_t>(round_up(cap, kTGran), int64_t(1) << 30));
-  const int64_t P = ceil_div(cap, T);
+  int64_t P = ceil_div(cap, T);
+  pl->sk = 0;
+  pl->sk_wgs = pl->sk_cmin = pl->sk_unit = pl->sk_rbw = pl->sk_lds = 0;
+  int64_t slots = (int64_t)io->batch * kv->num_kv_heads * rows * P;
+  if (opts->num_splits == 0 && !pl->wide && io->batch <= 64 && pl->row_blocks == 1) {
+    // Balanced partitions (up to 64 sequences, one row block): per KV head,
+    // each sequence is cut into partitions of at most lam units (pages, or
+    // page pairs for the MFMA kernel), lam the smallest size that needs one
+    // round of resident workgroups, or two if one round leaves the partitions
+    // unequal; the kernels compute lam from seq_lens on the device, so
+    // sequences of different lengths cost their length (with one partition
+    // size for all, set by the longest, short sequences leave workgroups idle
+    // or empty).
+    const int cap_cu = pl->mfma ? kMfmaWgPerCu : kValuWgPerCu;
+    int per_cu = ctx->host_only ? cap_cu
+                                : pa::decode_blocks_per_cu(pl->mfma, kv->dtype, io->q_dtype, D, rows,
+                                                           kv->k_vscales != nullptr);
+    per_cu = std::max(1, std::min(per_cu, cap_cu));
+    const int64_t wgs = (int64_t)ctx->num_cus * per_cu;
+    const int unit = pl->mfma ? 32 : kPage;
+    pl->sk = 1;
+    // partitions per KV head: kSkRounds rounds of the resident workgroups
+    const int64_t rph = std::max<int64_t>(io->batch, kSkRounds * ceil_div(wgs, kv->num_kv_heads));
+    pl->sk_wgs = (int)std::min<int64_t>(rph, INT32_MAX);
+    pl->sk_unit = unit;
+    pl->sk_cmin = (int)ceil_div(tmin, unit);
+    pl->sk_rbw = rows_per_wg;
+    // dynamic LDS that keeps per_cu + 1 workgroups from sharing a CU (the
+    // kernels' own LDS is far below what that leaves for per_cu of them)
+    pl->sk_lds = (int)(kLdsPerCu / (per_cu + 1) + 256);
+    if ((size_t)pl->sk_lds + lds > ctx->lds_per_block) pl->sk_lds = 0;
+    // the partition size at full capacity (one round), reported as the plan's
+    const int64_t c_full = std::max<int64_t>(
+        pl->sk_cmin, ceil_div(ceil_div(cap, unit), std::max<int64_t>(1, rph / 2 / io->batch)));
+    T = std::min<int64_t>(c_full * unit, int64_t(1) << 30);
+    P = ceil_div(cap, T);
+    slots = rph * kv->num_kv_heads * rows_per_wg;
+  }
   if (P > 65535) return fail(err, ATTN_ERR_UNSUPPORTED, "too many partitions (%lld)", (long long)P);
   pl->P = (int)P;
   pl->T = (int)T;
-  const int64_t slots = (int64_t)io->batch * kv->num_kv_heads * rows * P;
   pl->ws_o_bytes = (size_t)round_up(slots * D * 4, 256);
   pl->ws_ml_bytes = (size_t)round_up(slots * 2 * 4, 256);
-  pl->ws_bytes = pl->ws_o_bytes + pl->ws_ml_bytes;
+  pl->ws_tab_bytes = pl->sk ? (size_t)round_up((int64_t)kv->num_kv_heads * io->batch * 2 * 4, 256) : 0;
+  pl->ws_bytes = pl->ws_o_bytes + pl->ws_ml_bytes + pl->ws_tab_bytes;
   return ATTN_OK;
 }
 
@@ -407,8 +447,12 @@ attn_status decode_enqueue(attn_ctx *ctx, const attn_io *io, const attn_kv *kv, 
   a.P = pl.P; a.T = pl.T;
   a.t_dyn = pl.t_dyn; a.t_target = pl.t_target; a.t_min = pl.t_min; a.t_cap = pl.t_cap;
   a.row_blocks = pl.row_blocks;
+  a.sk = pl.sk; a.sk_wgs = pl.sk_wgs; a.sk_cmin = pl.sk_cmin; a.sk_unit = pl.sk_unit;
+  a.sk_rbw = pl.sk_rbw; a.sk_lds = pl.sk_lds;
   a.ws_o = reinterpret_cast<float *>(workspace);
   a.ws_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + pl.ws_o_bytes);
+  a.sk_tab = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(workspace) + pl.ws_o_bytes +
+                                         pl.ws_ml_bytes);
   if (ctx->host_only) return fail(err, ATTN_ERR_DEVICE, "host-only context: nothing enqueued");
   DeviceGuard g(ctx->device);
   if (!g.ok) return fail(err, ATTN_ERR_DEVICE, "cannot select device %d", ctx->device);

@@ -43,6 +43,26 @@ struct DecodeArgs {
   // partition size from the batch's longest sequence (t_dyn = 1): the plan's
   // rule with that length in place of the capacity (see decode_tokens)
   int32_t t_dyn, t_target, t_min, t_cap;
+  // Balanced partitions (sk = 1: at most 64 sequences, one row block; see
+  // sk_plan): per KV head, sequence b of u_b units (pages for the VALU
+  // kernel, page pairs for the MFMA kernel) is cut into q_b = ceil(u_b / lam)
+  // equal partitions, so every partition of every sequence is at most lam
+  // units.  Partition p of sequence b is the head's partial slot
+  // qe_b + p, qe_b = sum_{b'<b} q_b'.  The one-dimensional grid has
+  // Hkv * sk_wgs workgroups; workgroup q takes slot q / Hkv of KV head
+  // q % Hkv (consecutive workgroups, dealt round-robin to the XCDs, take
+  // different heads of the same pages, as in the partition grid, and the
+  // empty slots come last).  Partial row r of head h's slot j is at index
+  // (h * sk_wgs + j) * sk_rbw + r of ws_o (times D) and ws_ml (times 2);
+  // partition 0 of each sequence also leaves (qe_b, q_b) in sk_tab[h][b] for
+  // the merge.
+  int32_t sk, sk_wgs, sk_cmin, sk_unit;
+  int32_t *sk_tab;        // [Hkv][B][2]
+  int32_t sk_rbw;         // rows per block (row block size, or all rows)
+  // dynamic LDS bytes of a balanced-split launch: sized so that no more than
+  // the planned workgroups per CU are resident (the grid carries empty slots,
+  // and a CU running two ranges at once would finish last)
+  int32_t sk_lds;
 };
 
 // Tokens per partition of this call.  The plan sees only the page table's
@@ -86,6 +106,115 @@ __device__ __forceinline__ int decode_tokens_lo(const DecodeArgs &a, int L) {
   if (!a.t_dyn) return a.T;
   const int l = max(L, 0);
   return min(a.t_cap, max(a.t_min, ((l + a.t_target - 1) / a.t_target + 127) & ~127));
+}
+
+// Balanced partitions over at most 64 sequences, one per lane: lane b holds
+// sequence b's units u (pages or page pairs; 0 past the batch), its partition
+// count q = ceil(u / lam) and the exclusive prefix qe of the counts, where lam
+// is the smallest partition size >= sk_cmin with sum q <= N.  N is sk_wgs / 2
+// (one round of resident workgroups) when the non-empty sequences are equally
+// long, else sk_wgs (two rounds: unequal sequences cut into partitions for
+// one round leave some workgroups a partition well above the mean).
+struct SkPlan {
+  int u, q, qe;
+  int total;   // sum q: the non-empty slots of each KV head
+};
+
+// Reductions over the 64 lanes with DPP within rows of 16 (quad_perm
+// [1,0,3,2], [2,3,0,1], row_ror 4, 8) and permlane swaps across rows; every
+// lane receives the result.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <bool MAX>
+__device__ __forceinline__ int wave_ext(int v) {
+  auto op = [](int x, int y) { return MAX ? max(x, y) : min(x, y); };
+  v = op(v, dpp_i<0xB1>(v));
+  v = op(v, dpp_i<0x4E>(v));
+  v = op(v, dpp_i<0x124>(v));
+  v = op(v, dpp_i<0x128>(v));
+  auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  v = op((int)r[0], (int)r[1]);
+  r = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  return op((int)r[0], (int)r[1]);
+}
+// sum of values below 2^26 per lane: rows of 16 in 32 bits, the rows in 64
+__device__ __forceinline__ int64_t wave_sum64(int v) {
+  v += dpp_i<0xB1>(v);
+  v += dpp_i<0x4E>(v);
+  v += dpp_i<0x124>(v);
+  v += dpp_i<0x128>(v);
+  return (int64_t)__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
+// smallest lam in [cmin, umax] with sum ceil(u / lam) <= N (lam = umax gives
+// one partition per non-empty sequence, nonempty <= N)
+__device__ __forceinline__ int sk_lam(int u, int64_t W, int umax, int nonempty, int N, int cmin) {
+  const int64_t w_lo = (W + N - 1) / N;                       // sum q >= W / lam
+  int lo = max(cmin, (int)(w_lo < umax ? w_lo : umax));
+  int hi = umax;
+  if (N > nonempty) {                                         // sum q <= W / lam + nonempty
+    const int64_t w_hi = (W + (N - nonempty) - 1) / (N - nonempty);
+    if (w_hi < hi) hi = (int)w_hi;
+  }
+  hi = max(lo, hi);
+  while (lo < hi) {
+    const int mid = lo + (hi - lo) / 2;
+    if (wave_sum64(u > 0 ? (u + mid - 1) / mid : 0) <= N) hi = mid;
+    else lo = mid + 1;
+  }
+  return lo;
+}
+
+// Every lane of the wave must be active; B <= 64.  Returns false if slot
+// `slot` is empty, as soon as it can tell.
+__device__ __forceinline__ bool sk_plan(const DecodeArgs &a, int slot, SkPlan &s) {
+  const int lane = threadIdx.x & 63;
+  const int L = lane < a.B ? min(max(a.lens[lane], 0), a.capacity) : 0;
+  s.u = (L + a.sk_unit - 1) / a.sk_unit;
+  const uint64_t live = __builtin_amdgcn_ballot_w64(s.u > 0);
+  const int nonempty = __builtin_popcountll(live);
+  if (nonempty == 0) return false;
+  const int umax = wave_ext<true>(s.u);
+  const int umin = wave_ext<false>(s.u > 0 ? s.u : INT32_MAX);
+  if (umax == umin) {
+    // equal lengths: one round, the same number of partitions for each
+    const int n = max(nonempty, a.sk_wgs / 2);
+    if (slot >= n) return false;
+    const int q0 = n / nonempty;
+    const int lam = max(a.sk_cmin, (umax + q0 - 1) / q0);
+    const int qq = (umax + lam - 1) / lam;
+    s.q = s.u > 0 ? qq : 0;
+    s.qe = qq * __builtin_popcountll(live & ((uint64_t(1) << lane) - 1));
+    s.total = qq * nonempty;
+    return slot < s.total;
+  }
+  // unequal lengths: two rounds of finer partitions
+  const int64_t W = wave_sum64(s.u);
+  const int lam = sk_lam(s.u, W, umax, nonempty, a.sk_wgs, a.sk_cmin);
+  s.q = s.u > 0 ? (s.u + lam - 1) / lam : 0;
+  int incl = s.q;
+#pragma unroll
+  for (int k = 1; k < 64; k <<= 1) {
+    const int y = __shfl_up(incl, k);
+    if (lane >= k) incl += y;
+  }
+  s.qe = incl - s.q;
+  s.total = __builtin_amdgcn_readlane(incl, 63);
+  return slot < s.total;
+}
+
+// Slot i < total of a KV head: sequence b, its partition p of q, units [x0, x1).
+__device__ __forceinline__ void sk_part(const SkPlan &s, int i, int &b, int &p, int &q, int &x0,
+                                        int &x1) {
+  b = __builtin_popcountll(__builtin_amdgcn_ballot_w64(s.qe + s.q <= i));
+  p = i - __builtin_amdgcn_readlane(s.qe, b);
+  q = __builtin_amdgcn_readlane(s.q, b);
+  const int64_t u = __builtin_amdgcn_readlane(s.u, b);
+  x0 = (int)(p * u / q);
+  x1 = (int)((p + 1) * u / q);
 }
 
 struct PrefillArgs {

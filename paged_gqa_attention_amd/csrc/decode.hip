@@ -65,15 +65,14 @@ __device__ __forceinline__ void wave_scales(const float (*m_w)[NR], int wave, in
 // ==================================================================================
 // Log-sum-exp merge of the partitions + sink, one wave per output row
 // ==================================================================================
+// Row rr of (sequence b, KV head kvh) from its Pl partials, partial k at
+// workspace index base + k * stride.
 template <int D>
-__device__ __forceinline__ void merge_row(const DecodeArgs &a, int T, int b, int kvh, int rr,
-                                          int lane) {
+__device__ __forceinline__ void merge_row(const DecodeArgs &a, int b, int kvh, int rr, int Pl,
+                                          int64_t base, int64_t stride, int lane) {
   constexpr int DPL = D / 64;
   constexpr int CH = 8;                  // partitions whose outputs are loaded at once
-  const int L = min(a.lens[b], a.capacity);
-  const int Pl = (L + T - 1) / T;        // live partitions
   const int h = kvh * a.G + rr / a.R, i = rr % a.R;
-  const int64_t base = (((int64_t)b * a.Hkv + kvh) * a.rows + rr) * a.P;
   const float sink = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
 
   float o[DPL];
@@ -84,8 +83,8 @@ __device__ __forceinline__ void merge_row(const DecodeArgs &a, int T, int b, int
   // loads of a chunk are issued before any of them is used
   for (int p0 = 0; p0 < Pl; p0 += 64) {
     const int pm = p0 + lane;
-    const float mp = pm < Pl ? a.ws_ml[(base + pm) * 2] : kNegInf;
-    const float lp = pm < Pl ? a.ws_ml[(base + pm) * 2 + 1] : 0.f;
+    const float mp = pm < Pl ? a.ws_ml[(base + pm * stride) * 2] : kNegInf;
+    const float lp = pm < Pl ? a.ws_ml[(base + pm * stride) * 2 + 1] : 0.f;
     float Mc = mp;
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) Mc = __builtin_fmaxf(Mc, shfl_xor(Mc, m));
@@ -104,7 +103,7 @@ __device__ __forceinline__ void merge_row(const DecodeArgs &a, int T, int b, int
 #pragma unroll
       for (int q = 0; q < CH; ++q) {
         const int qq = q0 + q < cnt ? q0 + q : cnt - 1;
-        const float *op = a.ws_o + (base + p0 + qq) * D;
+        const float *op = a.ws_o + (base + (p0 + qq) * stride) * D;
 #pragma unroll
         for (int e = 0; e < DPL; ++e) ov[q][e] = op[lane + 64 * e];
       }
@@ -145,9 +144,26 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rr = blockIdx.x * kWaves + wave, kvh = blockIdx.y, b = blockIdx.z;
+  int Pl;
+  int64_t base, stride;
+  if (!a.sk) {
+    const int T = decode_tokens(a);
+    const int L = min(a.lens[b], a.capacity);
+    Pl = (L + T - 1) / T;                     // live partitions
+    base = (((int64_t)b * a.Hkv + kvh) * a.rows + rr) * a.P;
+    stride = 1;
+  } else {
+    // sequence b's partitions are the head's slots qe_b .. qe_b + q_b - 1, as
+    // its partition 0 recorded them (an empty sequence has none)
+    const int L = min(a.lens[b], a.capacity);
+    const int qe = L > 0 ? a.sk_tab[((int64_t)kvh * a.B + b) * 2] : 0;
+    Pl = L > 0 ? a.sk_tab[((int64_t)kvh * a.B + b) * 2 + 1] : 0;
+    base = ((int64_t)kvh * a.sk_wgs + qe) * a.sk_rbw + rr;
+    stride = a.sk_rbw;
+  }
   // rows past a sequence's own row count are not part of the output
-  const int T = decode_tokens(a);
-  if (rr < a.rows && rr % a.R < seq_rows(a.rows_b, b, a.R)) merge_row<D>(a, T, b, kvh, rr, lane);
+  if (rr < a.rows && rr % a.R < seq_rows(a.rows_b, b, a.R))
+    merge_row<D>(a, b, kvh, rr, Pl, base, stride, lane);
 }
 
 // ==================================================================================
@@ -192,14 +208,44 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform_int(threadIdx.x >> 6);
-  const int kvh = blockIdx.x / a.row_blocks, rb = blockIdx.x % a.row_blocks;
-  const int p = blockIdx.y, b = blockIdx.z;
+  // this workgroup's tokens [t0, t1) of row block rb of (sequence b, KV head
+  // kvh); partial row r of the block goes to workspace index pbase + r * pstride
+  int b, kvh, rb, t0, t1;
+  int64_t pbase, pstride;
+  if (!a.sk) {
+    // partition p: blockIdx (KV head * row blocks + row block, p, sequence)
+    kvh = blockIdx.x / a.row_blocks;
+    rb = blockIdx.x % a.row_blocks;
+    const int p = blockIdx.y;
+    b = blockIdx.z;
+    const int Lb = min(a.lens[b], a.capacity);
+    if (p * decode_tokens_lo(a, Lb) >= Lb) return;   // empty partition: the merge never reads it
+    const int T = decode_tokens(a);
+    t0 = p * T;
+    if (t0 >= Lb) return;
+    t1 = min(Lb, t0 + T);
+    pbase = (((int64_t)b * a.Hkv + kvh) * a.rows + rb * RB) * a.P + p;
+    pstride = a.P;
+  } else {
+    // balanced partitions (one row block): slot q / Hkv of KV head q % Hkv, in pages
+    kvh = blockIdx.x % a.Hkv;
+    rb = 0;
+    const int slot = blockIdx.x / a.Hkv;
+    SkPlan sp;
+    if (!sk_plan(a, slot, sp)) return;
+    int x0, x1, pp, qq;
+    sk_part(sp, slot, b, pp, qq, x0, x1);
+    if (pp == 0 && threadIdx.x == 0) {
+      a.sk_tab[((int64_t)kvh * a.B + b) * 2] = slot;
+      a.sk_tab[((int64_t)kvh * a.B + b) * 2 + 1] = qq;
+    }
+    const int Lb = min(a.lens[b], a.capacity);
+    t0 = x0 * kPage;
+    t1 = min(Lb, x1 * kPage);
+    pbase = ((int64_t)kvh * a.sk_wgs + slot) * a.sk_rbw;
+    pstride = 1;
+  }
   const int L = min(a.lens[b], a.capacity);
-  if (p * decode_tokens_lo(a, L) >= L) return;   // empty partition: the merge never reads it
-  const int T = decode_tokens(a);
-  const int t0 = p * T;
-  if (t0 >= L) return;
-  const int t1 = min(L, t0 + T);
   const int n = lane >> 2, qq = lane & 3;
   const int tg = lane % CPR;
 
@@ -527,14 +573,10 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
   }
 
   // ---- partial write: rows of this block ----
-  const int64_t P = a.P;
   for (int idx = threadIdx.x; idx < RB * D; idx += 256) {
     const int r = idx / D, d = idx % D;
     const int rr = rb * RB + r;
-    if (rr < a.rows) {
-      const int64_t slot = (((int64_t)b * a.Hkv + kvh) * a.rows + rr) * P + p;
-      a.ws_o[slot * D + d] = acc_lds[r][d];
-    }
+    if (rr < a.rows) a.ws_o[(pbase + r * pstride) * D + d] = acc_lds[r][d];
   }
   if (threadIdx.x < RB) {
     const int r = threadIdx.x;
@@ -545,7 +587,7 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
       const float Mu = (M == kNegInf) ? 0.f : M;
       float l = 0.f;
       for (int w = 0; w < kWaves; ++w) l += fast_exp2(m_w[w][r] - Mu) * l_w[w][r];
-      const int64_t slot = (((int64_t)b * a.Hkv + kvh) * a.rows + rr) * P + p;
+      const int64_t slot = pbase + r * pstride;
       a.ws_ml[slot * 2 + 0] = M;
       a.ws_ml[slot * 2 + 1] = l;
     }
@@ -599,13 +641,42 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform_int(threadIdx.x >> 6);
-  const int kvh = blockIdx.x, p = blockIdx.y, b = blockIdx.z;
+  // this workgroup's tokens [t0, t1) of (sequence b, KV head kvh), t0 a
+  // multiple of 32; partial row r goes to workspace index pbase + r * pstride
+  int b, kvh, t0, t1;
+  int64_t pbase, pstride;
+  if (!a.sk) {
+    // partition p: blockIdx (KV head, p, sequence)
+    kvh = blockIdx.x;
+    const int p = blockIdx.y;
+    b = blockIdx.z;
+    const int Lb = min(a.lens[b], a.capacity);
+    if (p * decode_tokens_lo(a, Lb) >= Lb) return;   // empty partition
+    const int T = decode_tokens(a);
+    t0 = p * T;
+    if (t0 >= Lb) return;
+    t1 = min(Lb, t0 + T);
+    pbase = (((int64_t)b * a.Hkv + kvh) * a.rows) * a.P + p;
+    pstride = a.P;
+  } else {
+    // balanced partitions: slot q / Hkv of KV head q % Hkv, in page pairs
+    kvh = blockIdx.x % a.Hkv;
+    const int slot = blockIdx.x / a.Hkv;
+    SkPlan sp;
+    if (!sk_plan(a, slot, sp)) return;
+    int x0, x1, pp, qq;
+    sk_part(sp, slot, b, pp, qq, x0, x1);
+    if (pp == 0 && threadIdx.x == 0) {
+      a.sk_tab[((int64_t)kvh * a.B + b) * 2] = slot;
+      a.sk_tab[((int64_t)kvh * a.B + b) * 2 + 1] = qq;
+    }
+    const int Lb = min(a.lens[b], a.capacity);
+    t0 = x0 * 32;
+    t1 = min(Lb, x1 * 32);
+    pbase = ((int64_t)kvh * a.sk_wgs + slot) * a.sk_rbw;
+    pstride = 1;
+  }
   const int L = min(a.lens[b], a.capacity);
-  if (p * decode_tokens_lo(a, L) >= L) return;   // empty partition
-  const int T = decode_tokens(a);
-  const int t0 = p * T;
-  if (t0 >= L) return;
-  const int t1 = min(L, t0 + T);
   const int n = lane & 15, j = lane >> 4;
 
   // ---- Q^T fragments: B[k = d][n = row] ----
@@ -916,13 +987,9 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
     __syncthreads();
   }
 
-  const int64_t P = a.P;
   for (int idx = threadIdx.x; idx < NR * D; idx += 256) {
     const int r = idx / D, d = idx % D;
-    if (r < a.rows) {
-      const int64_t slot = (((int64_t)b * a.Hkv + kvh) * a.rows + r) * P + p;
-      a.ws_o[slot * D + d] = acc_lds[r][d];
-    }
+    if (r < a.rows) a.ws_o[(pbase + r * pstride) * D + d] = acc_lds[r][d];
   }
   for (int r = threadIdx.x; r < NR; r += 256) {
     if (r < a.rows) {
@@ -931,7 +998,7 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
       const float Mu = (M == kNegInf) ? 0.f : M;
       float l = 0.f;
       for (int w = 0; w < kWaves; ++w) l += fast_exp2(m_w[w][r] - Mu) * l_w[w][r];
-      const int64_t slot = (((int64_t)b * a.Hkv + kvh) * a.rows + r) * P + p;
+      const int64_t slot = pbase + r * pstride;
       a.ws_ml[slot * 2 + 0] = M;
       a.ws_ml[slot * 2 + 1] = l;
     }
@@ -1023,10 +1090,13 @@ bool decode_mfma_supported(int kv, int qd, int D, int rows) {
 
 template <int KV, int QD, int D, bool VS>
 static hipError_t valu_rb(const DecodeArgs &a, hipStream_t s) {
-  dim3 grid(a.Hkv * a.row_blocks, a.P, a.B);   // KV heads of one page run side by side
+  // KV heads of one page run side by side; the balanced split has one
+  // workgroup per partial slot
+  const dim3 grid = a.sk ? dim3(a.Hkv * a.sk_wgs) : dim3(a.Hkv * a.row_blocks, a.P, a.B);
   const int rb = (a.rows + a.row_blocks - 1) / a.row_blocks;
-  if (rb <= 4) hipLaunchKernelGGL((decode_valu<KV, QD, D, 4, VS>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((decode_valu<KV, QD, D, 8, VS>), grid, dim3(256), 0, s, a);
+  const unsigned lds = a.sk ? (unsigned)a.sk_lds : 0u;
+  if (rb <= 4) hipLaunchKernelGGL((decode_valu<KV, QD, D, 4, VS>), grid, dim3(256), lds, s, a);
+  else hipLaunchKernelGGL((decode_valu<KV, QD, D, 8, VS>), grid, dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
@@ -1062,12 +1132,13 @@ hipError_t launch_decode_valu(const DecodeArgs &a, hipStream_t s) {
 
 template <int KV, int QD, int D, bool VS>
 static hipError_t mfma_nb(const DecodeArgs &a, hipStream_t s) {
-  dim3 grid(a.Hkv, a.P, a.B);
+  const dim3 grid = a.sk ? dim3(a.Hkv * a.sk_wgs) : dim3(a.Hkv, a.P, a.B);
   const int nb = (a.rows + 15) / 16;
+  const unsigned lds = a.sk ? (unsigned)a.sk_lds : 0u;
   switch (nb) {
-    case 1: hipLaunchKernelGGL((decode_mfma<KV, QD, D, 1, VS>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_mfma<KV, QD, D, 2, VS>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((decode_mfma<KV, QD, D, 4, VS>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((decode_mfma<KV, QD, D, 1, VS>), grid, dim3(256), lds, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_mfma<KV, QD, D, 2, VS>), grid, dim3(256), lds, s, a); break;
+    default: hipLaunchKernelGGL((decode_mfma<KV, QD, D, 4, VS>), grid, dim3(256), lds, s, a); break;
   }
   return hipGetLastError();
 }

@@ -101,17 +101,18 @@ def hctx(lib):
 def test_plan_headline_decode(hctx):
     io, kv, op = _decode_args(B=16, R=1, Hq=32, Hkv=8, d=128, stride=1024)
     P, T, W = pa.attn_paged_decode_plan(hctx, io, kv, op)
-    assert P * T >= 1024 * 16 and T % 128 == 0
-    # the VALU path: at least one round of two partial workgroups per CU, and
-    # partitions of at most 1,024 tokens (16 per sequence at a 16K capacity)
-    assert 16 * 8 * P >= 2 * 256 and T <= 1024 and P == 16
-    assert W >= 16 * 8 * 4 * P * (128 + 2) * 4
+    # the VALU path with balanced partitions: one round of 512 workgroups (two
+    # per CU), 64 per KV head, i.e. 4 partitions of 256 pages (4,096 tokens)
+    # per sequence at full capacity
+    assert (P, T) == (4, 4096)
+    # partial slots for up to two rounds (finer partitions for unequal lengths), 4 rows each
+    assert W >= 1024 * 4 * (128 + 2) * 4
 
 
 def test_plan_few_groups_fill_the_cus(hctx):
     # one KV head of the headline at R=8: 16 groups of 32 rows (the MFMA path at
-    # one workgroup per CU) -> 16 partitions of 1,024 tokens (32 per row), so
-    # 256 partial workgroups; a floor of 64 tokens per row would give 128
+    # one workgroup per CU) -> ranges of 1,024 tokens (32 per row), so 256
+    # partial workgroups; a floor of 64 tokens per row would leave half idle
     io, kv, op = _decode_args(B=16, R=8, Hq=4, Hkv=1, d=128, stride=1024)
     P, T, W = pa.attn_paged_decode_plan(hctx, io, kv, op)
     assert (P, T) == (16, 1024) and 16 * P == 256
@@ -391,3 +392,11 @@ def test_noalloc_decode_validates_and_bounds_its_scratch(hctx):
     assert need > pa.NOALLOC_SCRATCH_BYTES
     assert _status(lambda: pa.attn_paged_decode_noalloc(hctx, io, kv, op, stream=0)) == \
         pa.ATTN_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_plan_forced_splits_keep_partitions_per_sequence(hctx):
+    # a forced split count keeps fixed partitions per (sequence, KV head)
+    io, kv, op = _decode_args(B=16, R=1, Hq=32, Hkv=8, d=128, stride=1024)
+    op.num_splits = 16
+    P, T, W = pa.attn_paged_decode_plan(hctx, io, kv, op)
+    assert (P, T) == (16, 1024) and W >= 16 * 8 * 4 * 16 * (128 + 2) * 4
