@@ -7,11 +7,17 @@
 // into one pair of buffers while the other pair is read) and shared by all
 // waves.  Per wave and tile:
 //     S^T = K Q^T        (32x32x16 MFMA, FP32 accumulators)
-//     online softmax     (FP32, one row per lane column, lazy rescaling)
+//     online softmax     (FP32, one row per lane column; the reference
+//                         maximum is refreshed only when a tile's
+//                         exponentials leave their bound)
 //     O^T += V^T P^T     (P rounded to the MFMA operand type)
 // The K rows of each 32-key block are stored in LDS in the order that makes
 // every lane's 16 scores of a row exactly the 16 keys it then supplies to
 // the P.V products, and V pages are token-minor, so no transposes are needed.
+// 16-bit K/V at head_dim 64 (dense, two heads per workgroup) skip the
+// staging registers: each wave copies its share of a tile from global memory
+// straight into LDS (K rows with XOR-swizzled 16-byte chunks, V pages as
+// stored), one pair of tiles ahead of the pair being computed.
 //
 // Tiles wholly above a wave's diagonal are skipped (Geramy/LSE releases,
 // v0.4.14: fully masked key windows skipped, the rest keep their arithmetic);
@@ -40,7 +46,6 @@ constexpr int kXcds = 8;
 constexpr int kTileK = 64;     // keys per tile
 constexpr int kTileQ = 128;    // query rows per workgroup
 constexpr float kNegInf = -__builtin_inff();
-constexpr float kLazy = 8.0f;  // rescale only when the max grows by more than 2^8
 
 __device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f32x16 &c,
                                          bool f16) {
@@ -91,6 +96,9 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
   constexpr int KPT = (KCH + NT - 1) / NT;
   constexpr int EPC = 16 / ELT;         // stored elements per chunk
   constexpr int LIST = 1024;            // tiles per mask window
+  // 16-bit K/V at d 64, eight waves, dense: tiles are copied from global
+  // memory straight into LDS (no staging registers), one pair of tiles ahead
+  constexpr bool DL = !is8bit(KVDT) && !VS && D == 64 && NW == 8 && !MASK;
 
   // LDS buffers: the loop stages two tiles per barrier (two pairs of buffers)
   constexpr int NBUF = 4;
@@ -158,9 +166,11 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m_run = kNegInf, l_run = 0.f;
-  // derived from m_run, updated only when it changes: the exponent offset
-  // (0 while no score was seen) and the raw-score threshold of the next rescale
-  float neg_m = 0.f, grow_at = kNegInf;
+  float neg_m = 0.f;   // exponent offset: -m_run (0 while the row has no maximum)
+  bool unset = wave_has_rows;   // some row of the wave has no maximum yet (wave-uniform)
+  // bound on a lane's sum of one tile's exponentials (32 of them) before the
+  // reference maximum is refreshed: every P stays below 2^16 (2^14 as FP16)
+  constexpr float kTrig = F16 ? 16384.0f : 65536.0f;
 
   const int32_t *pt = a.page_table + (int64_t)b * a.pt_stride;
   const char *kbase = reinterpret_cast<const char *>(a.k) + (int64_t)kvh * a.k_sh * ELT;
@@ -323,6 +333,57 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
     }
   };
 
+  // direct copies (DL): K rows of 128 bytes, 16-byte chunk c of LDS row R at
+  // slot c ^ (R & 7); one wave copies LDS rows 8w .. 8w + 7 (keys of page
+  // w / 2) and half w % 2 of V page w / 2, stored as in memory (d-major,
+  // 16 tokens per row)
+  uint32_t dl_koff = 0, dl_voff = 0;
+  if constexpr (DL) {
+    const int R = 8 * wave + (lane >> 3), slot = lane & 7;
+    const int c = slot ^ (R & 7);
+    const int key = (R & ~31) | kperm(R & 31);
+    dl_koff = (uint32_t)((key & 15) * D * 2 + c * 16);
+    dl_voff = (uint32_t)((wave & 1) * 1024 + lane * 16);
+  }
+  auto gload_dl = [&](int t, int buf) {
+    if constexpr (DL) {
+      t = __builtin_amdgcn_readfirstlane(t);
+      const int pg = wave >> 1;
+      typedef const __attribute__((address_space(4))) int32_t ci32;   // scalar load: the table is read-only here
+      const int pid = ((ci32 *)pt)[min(4 * t + pg, npages - 1)];
+      const char *kpage = page_addr(kbase, a.k_frag, a.frag_shift, pid, k_page_bytes,
+                                    (int64_t)kvh * a.k_sh * ELT);
+      const char *vpage = page_addr(vbase, a.v_frag, a.frag_shift, pid, v_page_bytes,
+                                    (int64_t)kvh * a.v_sh * ELT);
+      // issued as instructions the compiler does not track: it would otherwise
+      // wait for these copies before every LDS read of the other buffers
+      const uint32_t kl = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&k_lds[buf][8 * wave * D]);
+      const uint32_t vl = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&v_lds[buf][pg * 16 * D + (wave & 1) * 512]);
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(kpage + dl_koff), "s"(kl) : "memory", "m0");
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(vpage + dl_voff), "s"(vl) : "memory", "m0");
+    }
+  };
+  // after this wave's copies landed: V slots at or past the end are zeroed
+  auto fix_tail = [&](int t, int buf) {
+    if constexpr (DL) {
+      const int kb0 = t * kTileK;
+      if (kb0 + kTileK <= L) return;
+      const int pg = wave >> 1;
+      uint16_t *vp = &v_lds[buf][pg * 16 * D + (wave & 1) * 512 + lane * 8];
+      u32x4 v = *reinterpret_cast<u32x4 *>(vp);
+      const int tok0 = kb0 + 16 * pg + 8 * (lane & 1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t w = v[e];
+        if (tok0 + 2 * e >= L) w &= 0xffff0000u;
+        if (tok0 + 2 * e + 1 >= L) w &= 0x0000ffffu;
+        v[e] = w;
+      }
+      *reinterpret_cast<u32x4 *>(vp) = v;
+    }
+  };
+  auto vm_wait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
+
   // ---- per-tile work of one wave ----
   const float sc = a.score_scale;
   auto compute = [&](int t, int buf, int bits) {
@@ -346,7 +407,9 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const u32x4 ka = *reinterpret_cast<const u32x4 *>(kl + (32 * mb + nl) * KSTR + 16 * ks + 8 * hh);
+        const int R = 32 * mb + nl, c = 2 * ks + hh;
+        const u32x4 ka = DL ? *reinterpret_cast<const u32x4 *>(kl + R * D + ((c ^ (R & 7)) * 8))
+                            : *reinterpret_cast<const u32x4 *>(kl + R * KSTR + 16 * ks + 8 * hh);
         s[mb] = mfma32(ka, qf[ks], s[mb], F16);
       }
     }
@@ -366,50 +429,59 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
         }
     }
 
-    // online softmax (lazy rescaling) for row nl; the two lane halves hold
-    // keys 16g' + 8hh + ... of each 32-key block
-    // row max as a tree of 3-input maxima (32 values -> 10 + 2 -> 4 -> 1)
-    float t1[10];
+    // online softmax for row nl (the two lane halves hold keys 16g' + 8hh + ...
+    // of each 32-key block).  The exponentials use the current reference
+    // maximum; it is refreshed only when this lane's sum of the tile's
+    // exponentials leaves its bound (kTrig) or a row of the wave has no
+    // maximum yet: then the row maxima are taken, the accumulators rescaled
+    // and the tile's exponentials recomputed.  Any reference works for the
+    // result (the sum and the output carry the same factor); the bound keeps
+    // P and the FP32 accumulators in range.
+    u32x4 pf[2][2];   // [mb][kk]: P^T fragment, keys 32mb + 16kk + 8hh .. +8
+    auto expo = [&]() {
+      float la = 0.f, lb = 0.f;
 #pragma unroll
-    for (int k = 0; k < 10; ++k) {
-      const int a0 = 3 * k, a1 = 3 * k + 1, a2 = 3 * k + 2;
-      t1[k] = max3(s[a0 >> 4][a0 & 15], s[a1 >> 4][a1 & 15], s[a2 >> 4][a2 & 15]);
-    }
-    float mx = max2(max3(max3(t1[0], t1[1], t1[2]), max3(t1[3], t1[4], t1[5]),
-                         max3(t1[6], t1[7], t1[8])),
-                    max3(t1[9], s[1][14], s[1][15]));
-    {
-      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
-    }
-    // rescale when the scaled max exceeds m_run by more than kLazy (sc > 0)
-    const bool grow = mx > grow_at;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float m_new = grow ? mx * sc : m_run;
-      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = fast_exp2(__builtin_fmaf(s[mb][8 * kk + 2 * e], sc, neg_m));
+            const float p1 = fast_exp2(__builtin_fmaf(s[mb][8 * kk + 2 * e + 1], sc, neg_m));
+            const uint32_t w = F16 ? pack_f16x2(p0, p1) : pack_bf16x2(p0, p1);
+            pf[mb][kk][e] = w;
+            if (e & 1) lb = F16 ? dot2_f16(w, 0x3C003C00u, lb) : dot2_bf16(w, 0x3F803F80u, lb);
+            else la = F16 ? dot2_f16(w, 0x3C003C00u, la) : dot2_bf16(w, 0x3F803F80u, la);
+          }
+      return la + lb;
+    };
+    float ts = expo();
+    if (unset || __builtin_amdgcn_ballot_w64(ts > kTrig)) {
+      float t1[10];
+#pragma unroll
+      for (int k = 0; k < 10; ++k) {
+        const int a0 = 3 * k, a1 = 3 * k + 1, a2 = 3 * k + 2;
+        t1[k] = max3(s[a0 >> 4][a0 & 15], s[a1 >> 4][a1 & 15], s[a2 >> 4][a2 & 15]);
+      }
+      float mx = max2(max3(max3(t1[0], t1[1], t1[2]), max3(t1[3], t1[4], t1[5]),
+                           max3(t1[6], t1[7], t1[8])),
+                      max3(t1[9], s[1][14], s[1][15]));
+      {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+      }
+      const float m_new = __builtin_fmaxf(m_run, mx * sc);
+      const float alpha = m_new == m_run ? 1.0f : fast_exp2(m_run - m_new);
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
       l_run *= alpha;
+      const bool moved = __builtin_amdgcn_ballot_w64(m_new != m_run) != 0;
       m_run = m_new;
-      neg_m = (m_run == kNegInf) ? 0.f : -m_run;
-      grow_at = (m_run + kLazy) / sc;
+      neg_m = m_run == kNegInf ? 0.f : -m_run;
+      if (moved) ts = expo();
+      unset = __builtin_amdgcn_ballot_w64(pos_row >= 0 && m_run == kNegInf) != 0;
     }
-    float la = l_run, lb = 0.f;   // two chains of the row sum
-    u32x4 pf[2][2];   // [mb][kk]: P^T fragment, keys 32mb + 16kk + 8hh .. +8
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(__builtin_fmaf(s[mb][8 * kk + 2 * e], sc, neg_m));
-          const float p1 = fast_exp2(__builtin_fmaf(s[mb][8 * kk + 2 * e + 1], sc, neg_m));
-          const uint32_t w = F16 ? pack_f16x2(p0, p1) : pack_bf16x2(p0, p1);
-          pf[mb][kk][e] = w;
-          if (e & 1) lb = F16 ? dot2_f16(w, 0x3C003C00u, lb) : dot2_bf16(w, 0x3F803F80u, lb);
-          else la = F16 ? dot2_f16(w, 0x3C003C00u, la) : dot2_bf16(w, 0x3F803F80u, la);
-        }
-    l_run = la + lb;
+    l_run += ts;
 
     // O^T[db] += V^T[32 rows, 16 keys] P^T[16 keys, 32 rows]
 #pragma unroll
@@ -418,14 +490,35 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const u32x4 va = *reinterpret_cast<const u32x4 *>(vl + (32 * db + nl) * VSTR + 32 * mb + 16 * kk + 8 * hh);
+          const u32x4 va = DL ? *reinterpret_cast<const u32x4 *>(vl + (2 * mb + kk) * 16 * D + (32 * db + nl) * 16 + 8 * hh)
+                              : *reinterpret_cast<const u32x4 *>(vl + (32 * db + nl) * VSTR + 32 * mb + 16 * kk + 8 * hh);
           oacc[db] = mfma32(va, pf[mb][kk], oacc[db], F16);
         }
   };
 
   // ---- tile loop (LDS buffers as above; one barrier per two tiles) ----
   if (nt > 0) {
-    if constexpr (!MASK) {
+    if constexpr (DL) {
+      // the next pair of tiles is copied into the other pair of buffers while
+      // this pair is computed; their copies have two tiles' time to land
+      gload_dl(0, 0);
+      if (nt > 1) gload_dl(1, 1);
+      vm_wait();
+      fix_tail(0, 0);
+      if (nt > 1) fix_tail(1, 1);
+      __syncthreads();
+      for (int t = 0; t < nt; t += 2) {
+        const int pb = t & 2;
+        if (t + 2 < nt) gload_dl(t + 2, pb ^ 2);
+        if (t + 3 < nt) gload_dl(t + 3, (pb ^ 2) + 1);
+        compute(t, pb, 0);
+        if (t + 1 < nt) compute(t + 1, pb + 1, 0);
+        vm_wait();
+        if (t + 2 < nt) fix_tail(t + 2, pb ^ 2);
+        if (t + 3 < nt) fix_tail(t + 3, (pb ^ 2) + 1);
+        __syncthreads();
+      }
+    } else if constexpr (!MASK) {
       // two tiles per barrier: tiles t, t + 1 in buffer pair (t & 2), while
       // t + 2, t + 3 are staged into the other pair, whose last readers
       // passed the previous barrier (about 2% over one tile per barrier)
