@@ -14,7 +14,7 @@
 // The K rows of each 32-key block are stored in LDS in the order that makes
 // every lane's 16 scores of a row exactly the 16 keys it then supplies to
 // the P.V products, and V pages are token-minor, so no transposes are needed.
-// 16-bit K/V at head_dim 64 (dense, two heads per workgroup) skip the
+// 16-bit K/V at head_dim 64 and 128 (two heads per workgroup) skip the
 // staging registers: each wave copies its share of a tile from global memory
 // straight into LDS (K rows with XOR-swizzled 16-byte chunks, V pages as
 // stored), one pair of tiles ahead of the pair being computed.
@@ -46,6 +46,7 @@ constexpr int kXcds = 8;
 constexpr int kTileK = 64;     // keys per tile
 constexpr int kTileQ = 128;    // query rows per workgroup
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kLazy = 8.0f;  // block-mask variants: rescale when the max grows by more than 2^8
 
 __device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f32x16 &c,
                                          bool f16) {
@@ -96,9 +97,12 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
   constexpr int KPT = (KCH + NT - 1) / NT;
   constexpr int EPC = 16 / ELT;         // stored elements per chunk
   constexpr int LIST = 1024;            // tiles per mask window
-  // 16-bit K/V at d 64, eight waves, dense: tiles are copied from global
+  // 16-bit K/V at d 64 / 128 with eight waves: tiles are copied from global
   // memory straight into LDS (no staging registers), one pair of tiles ahead
-  constexpr bool DL = !is8bit(KVDT) && !VS && D == 64 && NW == 8 && !MASK;
+  constexpr bool DL = !is8bit(KVDT) && !VS && (D == 64 || D == 128) && NW == 8;
+  constexpr int DL_RPI = 1024 / (D * 2);       // K rows per wave-wide copy (1 KiB)
+  constexpr int DL_IK = 8 / DL_RPI;            // K copies per wave and tile (8 rows)
+  constexpr int DL_IV = (16 * D * 2 / 2) / 1024;   // V copies per wave (half a page)
 
   // LDS buffers: the loop stages two tiles per barrier (two pairs of buffers)
   constexpr int NBUF = 4;
@@ -167,6 +171,7 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m_run = kNegInf, l_run = 0.f;
   float neg_m = 0.f;   // exponent offset: -m_run (0 while the row has no maximum)
+  float grow_at = kNegInf;   // block-mask variants: raw score above which the reference moves
   bool unset = wave_has_rows;   // some row of the wave has no maximum yet (wave-uniform)
   // bound on a lane's sum of one tile's exponentials (32 of them) before the
   // reference maximum is refreshed: every P stays below 2^16 (2^14 as FP16)
@@ -333,17 +338,21 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
     }
   };
 
-  // direct copies (DL): K rows of 128 bytes, 16-byte chunk c of LDS row R at
-  // slot c ^ (R & 7); one wave copies LDS rows 8w .. 8w + 7 (keys of page
-  // w / 2) and half w % 2 of V page w / 2, stored as in memory (d-major,
-  // 16 tokens per row)
-  uint32_t dl_koff = 0, dl_voff = 0;
+  // direct copies (DL): K rows of D elements, 16-byte chunk c of LDS row R at
+  // slot c ^ (R & 7); wave w copies LDS rows 8w .. 8w + 7 (keys of page w / 2)
+  // and half w % 2 of V page w / 2, stored as in memory (d-major, 16 tokens
+  // per row).  One copy instruction writes 1 KiB of LDS, lane by lane.
+  uint32_t dl_koff[DL ? DL_IK : 1], dl_voff[DL ? DL_IV : 1];
   if constexpr (DL) {
-    const int R = 8 * wave + (lane >> 3), slot = lane & 7;
-    const int c = slot ^ (R & 7);
-    const int key = (R & ~31) | kperm(R & 31);
-    dl_koff = (uint32_t)((key & 15) * D * 2 + c * 16);
-    dl_voff = (uint32_t)((wave & 1) * 1024 + lane * 16);
+#pragma unroll
+    for (int j = 0; j < DL_IK; ++j) {
+      const int R = 8 * wave + j * DL_RPI + lane / (D / 8), slot = lane % (D / 8);
+      const int c = slot ^ (R & 7);
+      const int key = (R & ~31) | kperm(R & 31);
+      dl_koff[j] = (uint32_t)((key & 15) * D * 2 + c * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < DL_IV; ++j) dl_voff[j] = (uint32_t)((wave & 1) * 16 * D + j * 1024 + lane * 16);
   }
   auto gload_dl = [&](int t, int buf) {
     if constexpr (DL) {
@@ -356,11 +365,20 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
       const char *vpage = page_addr(vbase, a.v_frag, a.frag_shift, pid, v_page_bytes,
                                     (int64_t)kvh * a.v_sh * ELT);
       // issued as instructions the compiler does not track: it would otherwise
-      // wait for these copies before every LDS read of the other buffers
-      const uint32_t kl = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&k_lds[buf][8 * wave * D]);
-      const uint32_t vl = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&v_lds[buf][pg * 16 * D + (wave & 1) * 512]);
-      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(kpage + dl_koff), "s"(kl) : "memory", "m0");
-      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(vpage + dl_voff), "s"(vl) : "memory", "m0");
+      // wait for these copies before every LDS read of the other buffers; the
+      // loop waits for them itself before the barrier that publishes them
+#pragma unroll
+      for (int j = 0; j < DL_IK; ++j) {
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(
+            (uint32_t)(uintptr_t)&k_lds[buf][(8 * wave + j * DL_RPI) * D]);
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(kpage + dl_koff[j]), "s"(dst) : "memory", "m0");
+      }
+#pragma unroll
+      for (int j = 0; j < DL_IV; ++j) {
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(
+            (uint32_t)(uintptr_t)&v_lds[buf][pg * 16 * D + (wave & 1) * 8 * D + j * 512]);
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(vpage + dl_voff[j]), "s"(dst) : "memory", "m0");
+      }
     }
   };
   // after this wave's copies landed: V slots at or past the end are zeroed
@@ -369,17 +387,20 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
       const int kb0 = t * kTileK;
       if (kb0 + kTileK <= L) return;
       const int pg = wave >> 1;
-      uint16_t *vp = &v_lds[buf][pg * 16 * D + (wave & 1) * 512 + lane * 8];
-      u32x4 v = *reinterpret_cast<u32x4 *>(vp);
       const int tok0 = kb0 + 16 * pg + 8 * (lane & 1);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        uint32_t w = v[e];
-        if (tok0 + 2 * e >= L) w &= 0xffff0000u;
-        if (tok0 + 2 * e + 1 >= L) w &= 0x0000ffffu;
-        v[e] = w;
+      for (int j = 0; j < DL_IV; ++j) {
+        uint16_t *vp = &v_lds[buf][pg * 16 * D + (wave & 1) * 8 * D + j * 512 + lane * 8];
+        u32x4 v = *reinterpret_cast<u32x4 *>(vp);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t w = v[e];
+          if (tok0 + 2 * e >= L) w &= 0xffff0000u;
+          if (tok0 + 2 * e + 1 >= L) w &= 0x0000ffffu;
+          v[e] = w;
+        }
+        *reinterpret_cast<u32x4 *>(vp) = v;
       }
-      *reinterpret_cast<u32x4 *>(vp) = v;
     }
   };
   auto vm_wait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
@@ -455,6 +476,36 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
           }
       return la + lb;
     };
+    if constexpr (MASK) {
+      // block-mask variants keep the maximum of every tile (fewer live
+      // registers across the exponentials): the accumulators are rescaled
+      // when the scaled maximum exceeds the reference by more than 2^kLazy
+      float t1[10];
+#pragma unroll
+      for (int k = 0; k < 10; ++k) {
+        const int a0 = 3 * k, a1 = 3 * k + 1, a2 = 3 * k + 2;
+        t1[k] = max3(s[a0 >> 4][a0 & 15], s[a1 >> 4][a1 & 15], s[a2 >> 4][a2 & 15]);
+      }
+      float mx = max2(max3(max3(t1[0], t1[1], t1[2]), max3(t1[3], t1[4], t1[5]),
+                           max3(t1[6], t1[7], t1[8])),
+                      max3(t1[9], s[1][14], s[1][15]));
+      {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+      }
+      const bool grow = mx > grow_at;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mx * sc : m_run;
+        const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+        neg_m = (m_run == kNegInf) ? 0.f : -m_run;
+        grow_at = (m_run + kLazy) / sc;
+      }
+      l_run += expo();
+    } else {
     float ts = expo();
     if (unset || __builtin_amdgcn_ballot_w64(ts > kTrig)) {
       float t1[10];
@@ -482,6 +533,7 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
       unset = __builtin_amdgcn_ballot_w64(pos_row >= 0 && m_run == kNegInf) != 0;
     }
     l_run += ts;
+    }
 
     // O^T[db] += V^T[32 rows, 16 keys] P^T[16 keys, 32 rows]
 #pragma unroll
@@ -498,7 +550,7 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
 
   // ---- tile loop (LDS buffers as above; one barrier per two tiles) ----
   if (nt > 0) {
-    if constexpr (DL) {
+    if constexpr (DL && !MASK) {
       // the next pair of tiles is copied into the other pair of buffers while
       // this pair is computed; their copies have two tiles' time to land
       gload_dl(0, 0);
@@ -573,6 +625,26 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
         // the listed tiles, two per barrier as in the unmasked loop
         auto tl = [&](int i) { return __builtin_amdgcn_readfirstlane(tile_list[i]) & 0xffffff; };
         auto tb = [&](int i) { return __builtin_amdgcn_readfirstlane(tile_list[i]) >> 24; };
+        if constexpr (DL) {
+          gload_dl(tl(0), 0);
+          if (cnt > 1) gload_dl(tl(1), 1);
+          vm_wait();
+          fix_tail(tl(0), 0);
+          if (cnt > 1) fix_tail(tl(1), 1);
+          __syncthreads();
+          for (int idx = 0; idx < cnt; idx += 2) {
+            const int pb = idx & 2;
+            if (idx + 2 < cnt) gload_dl(tl(idx + 2), pb ^ 2);
+            if (idx + 3 < cnt) gload_dl(tl(idx + 3), (pb ^ 2) + 1);
+            compute(tl(idx), pb, tb(idx));
+            if (idx + 1 < cnt) compute(tl(idx + 1), pb + 1, tb(idx + 1));
+            vm_wait();
+            if (idx + 2 < cnt) fix_tail(tl(idx + 2), pb ^ 2);
+            if (idx + 3 < cnt) fix_tail(tl(idx + 3), (pb ^ 2) + 1);
+            __syncthreads();
+          }
+          continue;
+        }
         gload(tl(0));
         lstore(tl(0), 0);
         if (cnt > 1) {
