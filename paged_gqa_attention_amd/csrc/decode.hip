@@ -422,8 +422,7 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
       float mx = x;
       mx = __builtin_fmaxf(mx, dpp<kDppRowRor4>(mx));
       mx = __builtin_fmaxf(mx, dpp<kDppRowRor8>(mx));
-      mx = __builtin_fmaxf(mx, shfl_xor(mx, 16));
-      mx = __builtin_fmaxf(mx, shfl_xor(mx, 32));
+      mx = max_xor32(max_xor16(mx));
       const float m_new = __builtin_fmaxf(m_run[k], mx);
       const float m_use = (m_new == kNegInf) ? 0.f : m_new;
       const float alpha = fast_exp2(m_run[k] - m_use);
@@ -847,21 +846,25 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
       mx = max3(mx, x[3], x[4]);
       mx = max3(mx, x[5], x[6]);
       mx = __builtin_fmaxf(mx, x[7]);
-      mx = __builtin_fmaxf(mx, shfl_xor(mx, 16));
-      mx = __builtin_fmaxf(mx, shfl_xor(mx, 32));
+      mx = max_xor32(max_xor16(mx));   // the row's 32 tokens: lanes n, n + 16, n + 32, n + 48
       const float m_new = __builtin_fmaxf(m_run[nb], mx);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[nb] - m_use);
-      m_run[nb] = m_new;
+      // rescale only when some row's maximum moved (otherwise the factor is 1)
+      if (__builtin_amdgcn_ballot_w64(m_new > m_run[nb])) {
+        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run[nb] - m_use);
+        l_run[nb] *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) oacc[mb][nb] *= alpha;
+        m_run[nb] = m_new;
+      }
+      const float m_use = (m_run[nb] == kNegInf) ? 0.f : m_run[nb];
       float pv[8], ps = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         pv[e] = fast_exp2(x[e] - m_use);
         ps += pv[e];
       }
-      l_run[nb] = l_run[nb] * alpha + ps;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) oacc[mb][nb] *= alpha;
+      l_run[nb] += ps;
       if constexpr (VS) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) pv[e] *= vw[e];
