@@ -46,7 +46,7 @@ constexpr int kXcds = 8;
 constexpr int kTileK = 64;     // keys per tile
 constexpr int kTileQ = 128;    // query rows per workgroup
 constexpr float kNegInf = -__builtin_inff();
-constexpr float kLazy = 8.0f;  // block-mask variants: rescale when the max grows by more than 2^8
+constexpr float kLazy = 8.0f;  // per-tile rule: rescale when the max grows by more than 2^8
 
 __device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f32x16 &c,
                                          bool f16) {
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m_run = kNegInf, l_run = 0.f;
   float neg_m = 0.f;   // exponent offset: -m_run (0 while the row has no maximum)
-  float grow_at = kNegInf;   // block-mask variants: raw score above which the reference moves
+  float grow_at = kNegInf;   // per-tile rule: raw score above which the reference moves
   bool unset = wave_has_rows;   // some row of the wave has no maximum yet (wave-uniform)
   // bound on a lane's sum of one tile's exponentials (32 of them) before the
   // reference maximum is refreshed: every P stays below 2^16 (2^14 as FP16)
@@ -451,13 +451,13 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
     }
 
     // online softmax for row nl (the two lane halves hold keys 16g' + 8hh + ...
-    // of each 32-key block).  The exponentials use the current reference
-    // maximum; it is refreshed only when this lane's sum of the tile's
-    // exponentials leaves its bound (kTrig) or a row of the wave has no
-    // maximum yet: then the row maxima are taken, the accumulators rescaled
-    // and the tile's exponentials recomputed.  Any reference works for the
-    // result (the sum and the output carry the same factor); the bound keeps
-    // P and the FP32 accumulators in range.
+    // of each 32-key block).  Dense tiles copied straight into LDS: the
+    // exponentials use the current reference maximum; it is refreshed only
+    // when this lane's sum of the tile's exponentials leaves its bound (kTrig)
+    // or a row of the wave has no maximum yet: then the row maxima are taken,
+    // the accumulators rescaled and the tile's exponentials recomputed.  Any
+    // reference works for the result (the sum and the output carry the same
+    // factor); the bound keeps P and the FP32 accumulators in range.
     u32x4 pf[2][2];   // [mb][kk]: P^T fragment, keys 32mb + 16kk + 8hh .. +8
     auto expo = [&]() {
       float la = 0.f, lb = 0.f;
@@ -476,10 +476,11 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
           }
       return la + lb;
     };
-    if constexpr (MASK) {
-      // block-mask variants keep the maximum of every tile (fewer live
-      // registers across the exponentials): the accumulators are rescaled
-      // when the scaled maximum exceeds the reference by more than 2^kLazy
+    if constexpr (MASK || !DL) {
+      // block-mask variants and those with register staging keep the maximum
+      // of every tile (fewer live registers across the exponentials): the
+      // accumulators are rescaled when the scaled maximum exceeds the
+      // reference by more than 2^kLazy
       float t1[10];
 #pragma unroll
       for (int k = 0; k < 10; ++k) {

@@ -24,6 +24,12 @@ HEADLINE = {
     "_ZN2pa12prefill_mfmaILi2ELi2ELi64ELi2ELb0ELb0EEEvNS_11PrefillArgsE":
         dict(max_vgprs=128, occupancy=4, max_lds=80 * 1024),
     "_ZN2pa12decode_mergeILi128EEEvNS_10DecodeArgsE": dict(max_vgprs=64),
+    # the 8-bit prefill variants of the headline shape (e4m3fn K/V, bf16 Q; with
+    # and without per-vector scales) keep four waves per SIMD as well
+    "_ZN2pa12prefill_mfmaILi3ELi2ELi64ELi2ELb0ELb0EEEvNS_11PrefillArgsE":
+        dict(max_vgprs=128, occupancy=4, max_lds=80 * 1024),
+    "_ZN2pa12prefill_mfmaILi3ELi2ELi64ELi2ELb0ELb1EEEvNS_11PrefillArgsE":
+        dict(max_vgprs=128, occupancy=4, max_lds=80 * 1024),
 }
 
 
