@@ -153,7 +153,7 @@ struct DecodePlan {
   bool wide;              // head_dim 256 with more than 8 rows per KV head
   int rows, rb, row_blocks, P, T;
   int t_dyn, t_target, t_min, t_cap;   // the device-side partition rule (DecodeArgs)
-  int sk, sk_wgs, sk_cmin, sk_unit, sk_rbw, sk_lds;   // balanced split (DecodeArgs)
+  int sk, sk_wgs, sk_cmin, sk_unit, sk_rbw, sk_lds, sk_round;   // balanced split (DecodeArgs)
   size_t ws_bytes, ws_o_bytes, ws_ml_bytes, ws_tab_bytes;
 };
 
@@ -261,7 +261,7 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
   T = std::min<int64_t>(T, std::min<int64_t>(round_up(cap, kTGran), int64_t(1) << 30));
   int64_t P = ceil_div(cap, T);
   pl->sk = 0;
-  pl->sk_wgs = pl->sk_cmin = pl->sk_unit = pl->sk_rbw = pl->sk_lds = 0;
+  pl->sk_wgs = pl->sk_cmin = pl->sk_unit = pl->sk_rbw = pl->sk_lds = pl->sk_round = 0;
   int64_t slots = (int64_t)io->batch * kv->num_kv_heads * rows * P;
   if (opts->num_splits == 0 && !pl->wide && io->batch <= 64 && pl->row_blocks == 1) {
     // Balanced partitions (up to 64 sequences, one row block): per KV head,
@@ -281,8 +281,10 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
     const int unit = pl->mfma ? 32 : kPage;
     pl->sk = 1;
     // partitions per KV head: kSkRounds rounds of the resident workgroups
-    const int64_t rph = std::max<int64_t>(io->batch, kSkRounds * ceil_div(wgs, kv->num_kv_heads));
+    const int64_t round = ceil_div(wgs, kv->num_kv_heads);
+    const int64_t rph = std::max<int64_t>(io->batch, kSkRounds * round);
     pl->sk_wgs = (int)std::min<int64_t>(rph, INT32_MAX);
+    pl->sk_round = (int)std::min<int64_t>(rph / kSkRounds, INT32_MAX);
     pl->sk_unit = unit;
     pl->sk_cmin = (int)ceil_div(tmin, unit);
     pl->sk_rbw = rows_per_wg;
@@ -292,7 +294,7 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
     if ((size_t)pl->sk_lds + lds > ctx->lds_per_block) pl->sk_lds = 0;
     // the partition size at full capacity (one round), reported as the plan's
     const int64_t c_full = std::max<int64_t>(
-        pl->sk_cmin, ceil_div(ceil_div(cap, unit), std::max<int64_t>(1, rph / 2 / io->batch)));
+        pl->sk_cmin, ceil_div(ceil_div(cap, unit), std::max<int64_t>(1, rph / kSkRounds / io->batch)));
     T = std::min<int64_t>(c_full * unit, int64_t(1) << 30);
     P = ceil_div(cap, T);
     slots = rph * kv->num_kv_heads * rows_per_wg;
@@ -448,7 +450,7 @@ attn_status decode_enqueue(attn_ctx *ctx, const attn_io *io, const attn_kv *kv, 
   a.t_dyn = pl.t_dyn; a.t_target = pl.t_target; a.t_min = pl.t_min; a.t_cap = pl.t_cap;
   a.row_blocks = pl.row_blocks;
   a.sk = pl.sk; a.sk_wgs = pl.sk_wgs; a.sk_cmin = pl.sk_cmin; a.sk_unit = pl.sk_unit;
-  a.sk_rbw = pl.sk_rbw; a.sk_lds = pl.sk_lds;
+  a.sk_rbw = pl.sk_rbw; a.sk_lds = pl.sk_lds; a.sk_round = pl.sk_round;
   a.ws_o = reinterpret_cast<float *>(workspace);
   a.ws_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + pl.ws_o_bytes);
   a.sk_tab = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(workspace) + pl.ws_o_bytes +

@@ -57,6 +57,7 @@ struct DecodeArgs {
   // partition 0 of each sequence also leaves (qe_b, q_b) in sk_tab[h][b] for
   // the merge.
   int32_t sk, sk_wgs, sk_cmin, sk_unit;
+  int32_t sk_round;       // slots of one round of resident workgroups (per KV head)
   int32_t *sk_tab;        // [Hkv][B][2]
   int32_t sk_rbw;         // rows per block (row block size, or all rows)
   // dynamic LDS bytes of a balanced-split launch: sized so that no more than
@@ -111,10 +112,11 @@ __device__ __forceinline__ int decode_tokens_lo(const DecodeArgs &a, int L) {
 // Balanced partitions over at most 64 sequences, one per lane: lane b holds
 // sequence b's units u (pages or page pairs; 0 past the batch), its partition
 // count q = ceil(u / lam) and the exclusive prefix qe of the counts, where lam
-// is the smallest partition size >= sk_cmin with sum q <= N.  N is sk_wgs / 2
+// is the smallest partition size >= sk_cmin with sum q <= N.  N is sk_round
 // (one round of resident workgroups) when the non-empty sequences are equally
-// long, else sk_wgs (two rounds: unequal sequences cut into partitions for
-// one round leave some workgroups a partition well above the mean).
+// long, else sk_wgs (all the planned rounds: unequal sequences cut into
+// partitions for one round leave some workgroups a partition well above the
+// mean).
 struct SkPlan {
   int u, q, qe;
   int total;   // sum q: the non-empty slots of each KV head
@@ -181,7 +183,7 @@ __device__ __forceinline__ bool sk_plan(const DecodeArgs &a, int slot, SkPlan &s
   const int umin = wave_ext<false>(s.u > 0 ? s.u : INT32_MAX);
   if (umax == umin) {
     // equal lengths: one round, the same number of partitions for each
-    const int n = max(nonempty, a.sk_wgs / 2);
+    const int n = max(nonempty, a.sk_round);
     if (slot >= n) return false;
     const int q0 = n / nonempty;
     const int lam = max(a.sk_cmin, (umax + q0 - 1) / q0);
@@ -191,7 +193,7 @@ __device__ __forceinline__ bool sk_plan(const DecodeArgs &a, int slot, SkPlan &s
     s.total = qq * nonempty;
     return slot < s.total;
   }
-  // unequal lengths: two rounds of finer partitions
+  // unequal lengths: every planned round, finer partitions
   const int64_t W = wave_sum64(s.u);
   const int lam = sk_lam(s.u, W, umax, nonempty, a.sk_wgs, a.sk_cmin);
   s.q = s.u > 0 ? (s.u + lam - 1) / lam : 0;
