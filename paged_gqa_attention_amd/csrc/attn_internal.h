@@ -197,21 +197,27 @@ __device__ __forceinline__ bool sk_plan(const DecodeArgs &a, int slot, SkPlan &s
   const int64_t W = wave_sum64(s.u);
   const int lam = sk_lam(s.u, W, umax, nonempty, a.sk_wgs, a.sk_cmin);
   s.q = s.u > 0 ? (s.u + lam - 1) / lam : 0;
-  int incl = s.q;
-#pragma unroll
-  for (int k = 1; k < 64; k <<= 1) {
-    const int y = __shfl_up(incl, k);
-    if (lane >= k) incl += y;
+  // Slots are dispatched in order, so the sequences are laid out largest
+  // partition first (longest-processing-time order): the last workgroups to
+  // start are the shortest, and the round ends evenly.  A sequence's
+  // partitions stay consecutive; ties keep the sequence order.
+  const int sz = s.q > 0 ? (s.u + s.q - 1) / s.q : 0;
+  int qe = 0, total = 0;
+  for (int k = 0; k < a.B; ++k) {
+    const int szk = __builtin_amdgcn_readlane(sz, k);
+    const int qk = __builtin_amdgcn_readlane(s.q, k);
+    qe += (szk > sz || (szk == sz && k < lane)) ? qk : 0;
+    total += qk;
   }
-  s.qe = incl - s.q;
-  s.total = __builtin_amdgcn_readlane(incl, 63);
+  s.qe = qe;
+  s.total = total;
   return slot < s.total;
 }
 
 // Slot i < total of a KV head: sequence b, its partition p of q, units [x0, x1).
 __device__ __forceinline__ void sk_part(const SkPlan &s, int i, int &b, int &p, int &q, int &x0,
                                         int &x1) {
-  b = __builtin_popcountll(__builtin_amdgcn_ballot_w64(s.qe + s.q <= i));
+  b = __builtin_ctzll(__builtin_amdgcn_ballot_w64(s.q > 0 && s.qe <= i && i < s.qe + s.q));
   p = i - __builtin_amdgcn_readlane(s.qe, b);
   q = __builtin_amdgcn_readlane(s.q, b);
   const int64_t u = __builtin_amdgcn_readlane(s.u, b);
