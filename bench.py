@@ -194,16 +194,19 @@ def per_call_stats(fn, n: int = 50):
 
 
 def read_ceiling(ctx, steps: int = 10):
-    """Read-only probe rates over 1 GiB: contiguous, and 4 KiB tiles in a shuffled order."""
+    """Read-only probe rates over 1 GiB: contiguous, and 4 KiB (a bf16 K or V
+    page tile at head_dim 128) or 2 KiB (8-bit) tiles in a shuffled order."""
     import torch
     import paged_gqa_attention_amd as pa
     nbytes = 1 << 30
     buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     g = torch.Generator().manual_seed(7)
     order = torch.randperm(nbytes // 4096, generator=g).to(torch.int32).cuda()
+    order2 = torch.randperm(nbytes // 2048, generator=g).to(torch.int32).cuda()
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     out = {}
-    for name, pat, o in (("contiguous", 0, None), ("paged_4k_tiles", 1, order)):
+    for name, pat, o in (("contiguous", 0, None), ("paged_4k_tiles", 1, order),
+                         ("paged_2k_tiles", 2, order2)):
         ms = time_calls(lambda: pa.attn_debug_read_probe(ctx, buf, pat, o, sink), steps, 2)
         out[name] = round(nbytes / (ms * 1e-3) / 1e9, 1)
     out["unit"] = "GB/s"

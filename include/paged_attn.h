@@ -339,7 +339,10 @@ attn_status attn_debug_gather_kv(attn_ctx *ctx, const attn_kv *kv, int32_t b, in
  * contiguously; pattern 1 reads the 4 KiB tiles buf + 4096 * tile_order[i],
  * i < bytes / 4096, in that order (tile_order: device int32 array whose
  * entries lie in [0, bytes / 4096), trusted), the access pattern of a paged
- * pool.  buf must be 16-byte aligned and bytes a positive multiple of 4096.
+ * pool; pattern 2 does the same with 2 KiB tiles (buf + 2048 * tile_order[i],
+ * i < bytes / 2048, entries in [0, bytes / 2048)), the size of one (page, KV
+ * head) tile of 8-bit K or V at head_dim 128.  buf must be 16-byte aligned
+ * and bytes a positive multiple of 4096.
  * `sink` (device, one word) is written only if the data XOR to a fixed
  * constant: it exists so that no load can be optimised away. */
 attn_status attn_debug_read_probe(attn_ctx *ctx, const void *buf, size_t bytes, int32_t pattern,

@@ -440,8 +440,8 @@ def attn_debug_gather_kv(ctx: Context, kv: attn_kv, b: int, seq_len: int, k_out:
 
 def attn_debug_read_probe(ctx: Context, buf: torch.Tensor, pattern: int,
                           tile_order: Optional[torch.Tensor], sink: torch.Tensor, stream=None):
-    """Read-only HBM probe over ``buf`` (pattern 0 contiguous, 1 4 KiB tiles in
-    ``tile_order``); a measurement hook."""
+    """Read-only HBM probe over ``buf`` (pattern 0 contiguous, 1 4 KiB tiles and
+    2 2 KiB tiles in ``tile_order``); a measurement hook."""
     lib = load_library()
     err = ctypes.c_char_p()
     _check(lib.attn_debug_read_probe(ctx.handle, _ptr(buf), buf.numel() * buf.element_size(),

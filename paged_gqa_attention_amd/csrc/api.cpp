@@ -669,9 +669,10 @@ attn_status attn_debug_read_probe(attn_ctx *ctx, const void *buf, size_t bytes, 
     return fail(err, ATTN_ERR_INVALID_ARGUMENT, "buf is not 16-byte aligned");
   if (bytes == 0 || bytes % 4096 != 0)
     return fail(err, ATTN_ERR_INVALID_ARGUMENT, "bytes must be a positive multiple of 4096");
-  if (pattern != 0 && pattern != 1) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "pattern must be 0 or 1");
-  if (pattern == 1 && !tile_order) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "tile_order is NULL");
-  if (pattern == 1 && bytes / 4096 > (size_t)INT32_MAX)
+  if (pattern < 0 || pattern > 2)
+    return fail(err, ATTN_ERR_INVALID_ARGUMENT, "pattern must be 0, 1 or 2");
+  if (pattern != 0 && !tile_order) return fail(err, ATTN_ERR_INVALID_ARGUMENT, "tile_order is NULL");
+  if (pattern != 0 && bytes / (pattern == 1 ? 4096 : 2048) > (size_t)INT32_MAX)
     return fail(err, ATTN_ERR_INVALID_ARGUMENT, "too many tiles");
   if (ctx->host_only) return fail(err, ATTN_ERR_DEVICE, "host-only context: nothing enqueued");
   DeviceGuard g(ctx->device);

@@ -210,8 +210,11 @@ def test_read_probe_validation(hctx):
     # valid requests validate, then a planning-only context enqueues nothing
     assert probe(buf, 0, None, sink) == pa.ATTN_ERR_DEVICE
     assert probe(buf, 1, order, sink) == pa.ATTN_ERR_DEVICE
-    assert probe(buf, 2, order, sink) == pa.ATTN_ERR_INVALID_ARGUMENT           # no such pattern
+    assert probe(buf, 2, order, sink) == pa.ATTN_ERR_DEVICE
+    assert probe(buf, 3, order, sink) == pa.ATTN_ERR_INVALID_ARGUMENT           # no such pattern
+    assert probe(buf, -1, order, sink) == pa.ATTN_ERR_INVALID_ARGUMENT
     assert probe(buf, 1, None, sink) == pa.ATTN_ERR_INVALID_ARGUMENT            # tiles need an order
+    assert probe(buf, 2, None, sink) == pa.ATTN_ERR_INVALID_ARGUMENT
     assert probe(buf, 0, None, None) == pa.ATTN_ERR_INVALID_ARGUMENT            # no sink
     assert probe(FakeTensor((1000,), torch.uint8, 0x100000), 0, None, sink) == pa.ATTN_ERR_INVALID_ARGUMENT
     assert probe(FakeTensor((4096,), torch.uint8, 0x100004), 0, None, sink) == pa.ATTN_ERR_INVALID_ARGUMENT

@@ -411,14 +411,17 @@ def test_decode_workspace_reuse():
 
 
 def test_read_probe_runs_and_keeps_its_sink():
-    """The read-only probe is a measurement hook: it must run over both patterns
+    """The read-only probe is a measurement hook: it must run over every pattern
     and leave the sink alone (the data never XOR to its fixed constant)."""
     _say("read probe")
-    buf = torch.zeros(1 << 22, dtype=torch.uint8, device="cuda")           # 4 MiB = 1024 tiles
-    order = torch.randperm(1024, generator=torch.Generator().manual_seed(3)).to(torch.int32).cuda()
+    buf = torch.zeros(1 << 22, dtype=torch.uint8, device="cuda")   # 4 MiB = 1024 4 KiB tiles
+    g = torch.Generator().manual_seed(3)
+    order = torch.randperm(1024, generator=g).to(torch.int32).cuda()
+    order2 = torch.randperm(2048, generator=g).to(torch.int32).cuda()   # 2 KiB tiles
     sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
     pa.attn_debug_read_probe(ctx(), buf, 0, None, sink)
     pa.attn_debug_read_probe(ctx(), buf, 1, order, sink)
+    pa.attn_debug_read_probe(ctx(), buf, 2, order2, sink)
     torch.cuda.synchronize()
     assert int(sink.item()) == 7
 
