@@ -476,11 +476,11 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
           }
       return la + lb;
     };
-    if constexpr (MASK || !DL) {
-      // block-mask variants and those with register staging keep the maximum
-      // of every tile (fewer live registers across the exponentials): the
-      // accumulators are rescaled when the scaled maximum exceeds the
-      // reference by more than 2^kLazy
+    if constexpr ((MASK && D == 64) || !DL) {
+      // the head_dim 64 block-mask variant and those with register staging
+      // keep the maximum of every tile (fewer live registers across the
+      // exponentials): the accumulators are rescaled when the scaled maximum
+      // exceeds the reference by more than 2^kLazy
       float t1[10];
 #pragma unroll
       for (int k = 0; k < 10; ++k) {
