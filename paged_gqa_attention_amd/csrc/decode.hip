@@ -311,13 +311,18 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
   // walk, which visits the pages in order, reaches them.
   int ids[2];
   int ids_k0 = 0;
+  // The id loads are unconditional (indices clamped to the last page) and
+  // waited for at once: a load under a branch, or one still in flight where
+  // the walk's paths join, makes the compiler wait for every K/V load in
+  // flight at the join (once per 128 pages here is all it costs).
   auto load_ids = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int hlf = 0; hlf < 2; ++hlf) {
       const int idx = pg_first + (k0 + 64 * hlf + lane) * kWaves;
-      ids[hlf] = idx < pg_end ? pt[idx] : 0;
+      ids[hlf] = pt[min(idx, pg_end - 1)];
     }
     ids_k0 = k0;
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   };
   load_ids(0);
   auto page_id = [&](int page_idx) -> int64_t {
@@ -720,12 +725,17 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
   // when the walk, which visits the pairs in order, reaches them.
   int ids0, ids1;
   int ids_k0 = 0;
+  // The id loads are unconditional (indices clamped to the last page) and
+  // waited for at once: a load under a branch, or one still in flight where
+  // the walk's paths join, makes the compiler wait for every K/V load in
+  // flight at the join (once per 64 pairs here is all it costs).
   auto load_ids = [&](int k0) __attribute__((always_inline)) {
     const int ppi = pp_first + (k0 + lane) * kWaves;
-    const int p0 = 2 * ppi, p1 = 2 * ppi + 1;
-    ids0 = p0 < pg_end ? pt[p0] : 0;
-    ids1 = p1 < pg_end ? pt[p1] : ids0;
+    const int p0 = min(2 * ppi, pg_end - 1), p1 = min(2 * ppi + 1, pg_end - 1);
+    ids0 = pt[p0];
+    ids1 = pt[p1];
     ids_k0 = k0;
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   };
   load_ids(0);
 
@@ -908,27 +918,48 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
   u32x4 vA16[MB], vB16[MB], vC16[MB];
   u32x2 vA8[MB], vB8[MB], vC8[MB];
   f32x4 sA[4], sB[4], sC[4];
+  // The steady-state loops issue every load unconditionally (the loop runs
+  // only while all its pairs exist) so that the compiler can count the loads
+  // in flight exactly: processing a pair waits for that pair's loads only,
+  // while the later pairs' loads stay in flight.  The last pairs are handled
+  // after the loop.
+  constexpr int S = kWaves;
   auto pairs = [&](auto mode) __attribute__((always_inline)) {
     if constexpr (is8bit(KVDT) && NB == 2) {
       // 8-bit pairs carry half the bytes of 16-bit ones for the same
-      // arithmetic: three pairs in flight per wave at 32 rows (measured
-      // +3-5%; no gain at 16 rows, and at 64 rows the third set would spill)
-      constexpr int S = kWaves;
-      if (pp < pp_end) load_pair(mode, pp, kA, vA16, vA8, sA);
-      if (pp + S < pp_end) load_pair(mode, pp + S, kB, vB16, vB8, sB);
-      if (pp + 2 * S < pp_end) load_pair(mode, pp + 2 * S, kC, vC16, vC8, sC);
-      for (; pp < pp_end; pp += 3 * S) {
+      // arithmetic: three pairs in flight per wave at 32 rows (at 64 rows
+      // the third set would spill)
+      if (pp + 5 * S < pp_end) {
+        load_pair(mode, pp, kA, vA16, vA8, sA);
+        load_pair(mode, pp + S, kB, vB16, vB8, sB);
+        load_pair(mode, pp + 2 * S, kC, vC16, vC8, sC);
+        do {
+          process_pair(pp, kA, vA16, vA8, sA);
+          load_pair(mode, pp + 3 * S, kA, vA16, vA8, sA);
+          process_pair(pp + S, kB, vB16, vB8, sB);
+          load_pair(mode, pp + 4 * S, kB, vB16, vB8, sB);
+          process_pair(pp + 2 * S, kC, vC16, vC8, sC);
+          load_pair(mode, pp + 5 * S, kC, vC16, vC8, sC);
+          pp += 3 * S;
+        } while (pp + 5 * S < pp_end);
+      } else {
+        if (pp < pp_end) load_pair(mode, pp, kA, vA16, vA8, sA);
+        if (pp + S < pp_end) load_pair(mode, pp + S, kB, vB16, vB8, sB);
+        if (pp + 2 * S < pp_end) load_pair(mode, pp + 2 * S, kC, vC16, vC8, sC);
+      }
+      // A, B, C hold pairs pp, pp + S, pp + 2S (those that exist); pairs up
+      // to pp + 4S remain
+      if (pp < pp_end) {
         process_pair(pp, kA, vA16, vA8, sA);
         if (pp + 3 * S < pp_end) load_pair(mode, pp + 3 * S, kA, vA16, vA8, sA);
-        if (pp + S < pp_end) {
-          process_pair(pp + S, kB, vB16, vB8, sB);
-          if (pp + 4 * S < pp_end) load_pair(mode, pp + 4 * S, kB, vB16, vB8, sB);
-        }
-        if (pp + 2 * S < pp_end) {
-          process_pair(pp + 2 * S, kC, vC16, vC8, sC);
-          if (pp + 5 * S < pp_end) load_pair(mode, pp + 5 * S, kC, vC16, vC8, sC);
-        }
       }
+      if (pp + S < pp_end) {
+        process_pair(pp + S, kB, vB16, vB8, sB);
+        if (pp + 4 * S < pp_end) load_pair(mode, pp + 4 * S, kB, vB16, vB8, sB);
+      }
+      if (pp + 2 * S < pp_end) process_pair(pp + 2 * S, kC, vC16, vC8, sC);
+      if (pp + 3 * S < pp_end) process_pair(pp + 3 * S, kA, vA16, vA8, sA);
+      if (pp + 4 * S < pp_end) process_pair(pp + 4 * S, kB, vB16, vB8, sB);
     } else if constexpr (NB == 4 && D == 128) {
       // 64 rows at d 128: the accumulators and Q fragments leave room for one
       // pair in flight (a second register set spills to scratch)
@@ -937,16 +968,27 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
         process_pair(pp, kA, vA16, vA8, sA);
       }
     } else {
-      if (pp < pp_end) load_pair(mode, pp, kA, vA16, vA8, sA);
-      if (pp + kWaves < pp_end) load_pair(mode, pp + kWaves, kB, vB16, vB8, sB);
-      for (; pp < pp_end; pp += 2 * kWaves) {
-        process_pair(pp, kA, vA16, vA8, sA);
-        if (pp + 2 * kWaves < pp_end) load_pair(mode, pp + 2 * kWaves, kA, vA16, vA8, sA);
-        if (pp + kWaves < pp_end) {
-          process_pair(pp + kWaves, kB, vB16, vB8, sB);
-          if (pp + 3 * kWaves < pp_end) load_pair(mode, pp + 3 * kWaves, kB, vB16, vB8, sB);
-        }
+      if (pp + 3 * S < pp_end) {
+        load_pair(mode, pp, kA, vA16, vA8, sA);
+        load_pair(mode, pp + S, kB, vB16, vB8, sB);
+        do {
+          process_pair(pp, kA, vA16, vA8, sA);
+          load_pair(mode, pp + 2 * S, kA, vA16, vA8, sA);
+          process_pair(pp + S, kB, vB16, vB8, sB);
+          load_pair(mode, pp + 3 * S, kB, vB16, vB8, sB);
+          pp += 2 * S;
+        } while (pp + 3 * S < pp_end);
+      } else {
+        if (pp < pp_end) load_pair(mode, pp, kA, vA16, vA8, sA);
+        if (pp + S < pp_end) load_pair(mode, pp + S, kB, vB16, vB8, sB);
       }
+      // A, B hold pairs pp, pp + S (those that exist); pairs up to pp + 2S remain
+      if (pp < pp_end) {
+        process_pair(pp, kA, vA16, vA8, sA);
+        if (pp + 2 * S < pp_end) load_pair(mode, pp + 2 * S, kA, vA16, vA8, sA);
+      }
+      if (pp + S < pp_end) process_pair(pp + S, kB, vB16, vB8, sB);
+      if (pp + 2 * S < pp_end) process_pair(pp + 2 * S, kA, vA16, vA8, sA);
     }
   };
   if (a.k_frag || a.v_frag) pairs(Fragmented{});
