@@ -62,6 +62,20 @@ __device__ __forceinline__ u32x4 ld16_nt(const void *p) {
 __device__ __forceinline__ u32x2 ld8_nt(const void *p) {
   return __builtin_nontemporal_load((gu32x2 *)p);
 }
+// A non-temporal 16-byte load at base + off through a buffer resource of
+// `bytes` bytes (base wave-uniform): with bytes = 0 it returns zeros without
+// a memory access, so a load that may be past the end needs no branch (the
+// compiler then counts the loads in flight exactly).  Data format 32 bits in
+// the resource's fourth word, as raw buffer loads require.
+__device__ __forceinline__ u32x4 ld16_nt_buf(const void *base, uint32_t off, uint32_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  void *ub = (void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));
+}
 
 // ---- page addressing ---------------------------------------------------------------
 

@@ -337,8 +337,12 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
   // per-vector scales: lane n's token (the quad shares it)
   const float *ksbase = VS ? a.k_vs + (int64_t)kvh * a.vs_sh + n : nullptr;
   const float *vsbase = VS ? a.v_vs + (int64_t)kvh * a.vs_sh + n : nullptr;
+  // A page past the walk's end is "loaded" through an empty buffer resource
+  // (zeros, no memory access), so that the loop issues its loads
+  // unconditionally and every page waits for its own loads only.
   auto load_page = [&](auto mode, int page_idx, u32x4 *kd, u32x4 *vd, float &ksd,
                        float &vsd) __attribute__((always_inline)) {
+    const bool live = page_idx < pg_end;
     const int64_t pid = page_id(page_idx);
     const char *kp, *vp;
     if constexpr (decltype(mode)::value) {
@@ -348,12 +352,12 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
       kp = kbase + pid * a.k_sp * ELT;
       vp = vbase + pid * a.v_sp * ELT;
     }
-    kp += n * (D * ELT) + qq * 16;
-    vp += lane * 16;
+    const uint32_t tile = live ? 16 * D * ELT : 0;   // bytes of a (page, head) tile
 #pragma unroll
     for (int c = 0; c < NL; ++c) {
-      kd[c] = ld16_nt(kp + c * 64);       // streamed once: non-temporal
-      vd[c] = ld16_nt(vp + c * 1024);
+      // streamed once: non-temporal
+      kd[c] = ld16_nt_buf(kp, n * (D * ELT) + qq * 16 + c * 64, tile);
+      vd[c] = ld16_nt_buf(vp, lane * 16 + c * 1024, tile);
     }
     if constexpr (VS) {
       ksd = ksbase[pid * a.vs_sp];
@@ -513,15 +517,14 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs a) {
   u32x4 kA[NL], vA[NL], kB[NL], vB[NL];
   float ksA = 1.f, vsA = 1.f, ksB = 1.f, vsB = 1.f;
   auto pages = [&](auto mode) __attribute__((always_inline)) {
-    if (pg < pg_end) load_page(mode, pg, kA, vA, ksA, vsA);
-    if (pg + kWaves < pg_end) load_page(mode, pg + kWaves, kB, vB, ksB, vsB);
+    if (pg >= pg_end) return;
+    load_page(mode, pg, kA, vA, ksA, vsA);
+    load_page(mode, pg + kWaves, kB, vB, ksB, vsB);
     for (; pg < pg_end; pg += 2 * kWaves) {
       process_page(pg, kA, vA, ksA, vsA);
-      if (pg + 2 * kWaves < pg_end) load_page(mode, pg + 2 * kWaves, kA, vA, ksA, vsA);
-      if (pg + kWaves < pg_end) {
-        process_page(pg + kWaves, kB, vB, ksB, vsB);
-        if (pg + 3 * kWaves < pg_end) load_page(mode, pg + 3 * kWaves, kB, vB, ksB, vsB);
-      }
+      load_page(mode, pg + 2 * kWaves, kA, vA, ksA, vsA);
+      if (pg + kWaves < pg_end) process_page(pg + kWaves, kB, vB, ksB, vsB);
+      load_page(mode, pg + 3 * kWaves, kB, vB, ksB, vsB);
     }
   };
   if (a.k_frag || a.v_frag) pages(Fragmented{});
