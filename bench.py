@@ -635,7 +635,8 @@ def kv_append_summary(ctx, args):
 def formats_summary(ctx, args):
     """The 8-bit cache formats on their own workloads: decode B=4 x 65,536 keys,
     R=4 (MFMA verify path, HBM roofline) and prefill 16 x 8K (MFMA roofline),
-    with per-tensor e4m3fn, per-vector-scaled e4m3fn and per-vector-scaled e5m2."""
+    with per-tensor e4m3fn, per-vector-scaled e4m3fn and per-vector-scaled e5m2;
+    plus e4m3fn verify at R=8 over 16 x 16,384 keys."""
     import torch
     import synth
     from paged_gqa_attention_amd import accounting as acc
@@ -662,6 +663,20 @@ def formats_summary(ctx, args):
                      "prefill_TFLOPs": round(tfs, 1),
                      "prefill_mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 4),
                      "prefill_ms": round(pms, 3)}
+    # 8-bit speculative verify: 16 x 16,384 keys, R = 8 (32 rows per KV head,
+    # MFMA path with three page pairs in flight per wave), per-tensor e4m3fn
+    p = synth.make_decode(202, 16, 32, 8, 128, [16384] * 16, 8, kv_dtype=synth.DT_FP8,
+                          q_dtype=synth.DT_BF16, o_dtype=synth.DT_BF16, stride=1024, device="cuda")
+    call, (P, T), keep = decode_setup(ctx, p, "cuda")
+    ms = time_calls(call, args.steps, args.warmup)
+    b = acc.decode_bytes(p.seq_lens.tolist(), 8, 32, 8, 128, synth.DT_FP8, 2, 2)
+    gbs = b / (ms * 1e-3) / 1e9
+    del keep, call, p
+    torch.cuda.empty_cache()
+    out["fp8_verify_r8"] = {"workload": "B=16, Hq=32, Hkv=8, d=128, 16,384 keys, R=8, e4m3fn K/V, bf16 Q/O",
+                            "kernel": "decode_mfma + decode_merge",
+                            "decode_GBs": round(gbs, 1), "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                            "decode_ms": round(ms, 4), "decode_bytes": b, "splits": P}
     return out
 
 
