@@ -1,7 +1,7 @@
 """Benchmark of the paged GQA attention hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
-    python bench.py --only decode|prefill|copy|append|d256|config2|config4|config5
+    python bench.py --only decode|prefill|copy|append|d256|config2|config4|config5|fp8
     python bench.py --pmc-summary FETCH_DIR WRITE_DIR
     python bench.py --counter-summary PMC_DIR
 
@@ -372,7 +372,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["decode", "prefill", "copy", "append", "d256", "config2",
-                                       "config4", "config5"])
+                                       "config4", "config5", "fp8"])
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--counter-summary", metavar="DIR")
     args = ap.parse_args()
@@ -414,6 +414,16 @@ def main():
         return
     if args.only == "d256":
         print(json.dumps(wide_summary(ctx, args)), flush=True)
+        return
+    if args.only == "fp8":
+        # the FP8 long-context decode workload alone (B=4 x 65,536 keys, R=4)
+        p = synth.config3(device=dev)
+        call, (P, T), keep = decode_setup(ctx, p, dev)
+        ms = time_calls(call, args.steps, args.warmup)
+        b = acc.decode_bytes(p.seq_lens.tolist(), 4, 32, 8, 128, synth.DT_FP8, 2, 2)
+        print(json.dumps({"workload": "fp8 decode B=4, 65,536 keys, R=4", "ms": round(ms, 5),
+                          "GB/s": round(b / (ms * 1e-3) / 1e9, 1), "splits": P,
+                          "bytes_per_call": b}), flush=True)
         return
     if args.only in ("config2", "config4", "config5"):
         fn = {"config2": config2_summary, "config4": config4_summary,
