@@ -101,12 +101,20 @@ def hctx(lib):
 def test_plan_headline_decode(hctx):
     io, kv, op = _decode_args(B=16, R=1, Hq=32, Hkv=8, d=128, stride=1024)
     P, T, W = pa.attn_paged_decode_plan(hctx, io, kv, op)
-    # the VALU path with balanced partitions: one round of 512 workgroups (two
-    # per CU), 64 per KV head, i.e. 4 partitions of 256 pages (4,096 tokens)
-    # per sequence at full capacity
-    assert (P, T) == (4, 4096)
+    # the VALU path with balanced partitions: equal lengths take one round of
+    # 256 workgroups (one per CU: page tiles of 4 KiB), 32 per KV head, i.e. 2
+    # partitions of 512 pages (8,192 tokens) per sequence at full capacity
+    assert (P, T) == (2, 8192)
     # partial slots for up to two rounds (finer partitions for unequal lengths), 4 rows each
     assert W >= 1024 * 4 * (128 + 2) * 4
+
+
+def test_plan_small_page_tiles_keep_two_workgroups_per_cu(hctx):
+    # 8-bit K/V at d 128 (2 KiB page tiles): two workgroups per CU for equal
+    # lengths, 64 per KV head -> 4 x 65,536 tokens in 16 partitions of 4,096
+    io, kv, op = _decode_args(B=4, R=1, Hq=32, Hkv=8, d=128, stride=4096, dtype=torch.float8_e4m3fn)
+    P, T, W = pa.attn_paged_decode_plan(hctx, io, kv, op)
+    assert (P, T) == (16, 4096)
 
 
 def test_plan_few_groups_fill_the_cus(hctx):
