@@ -118,7 +118,7 @@ def pmc_summary(fetch_dir: str, write_dir: str):
     w_scale = COPY_BYTES / (copy_mean("WRITE_SIZE") * 1024)
     groups = {
         "decode_bf16_16k": ("decode", ("decode_valu", "decode_merge"),
-                            _src_hash("decode.hip", "common.h", "attn_internal.h")),
+                            _src_hash("decode.hip", "common.h", "attn_internal.h", "api.cpp")),
         "prefill_bf16_8k_b16": ("prefill", ("prefill_mfma",), _src_hash("prefill.hip", "common.h", "attn_internal.h")),
     }
     for key, (run, kernels, h) in groups.items():
@@ -439,7 +439,7 @@ def main():
                               synth.DT_BF16, synth.DT_BF16)
     gbs = nbytes / (ms * 1e-3) / 1e9
     dec_pc = None if args.only else per_call_stats(call)
-    dec_hash = _src_hash("decode.hip", "common.h", "attn_internal.h")
+    dec_hash = _src_hash("decode.hip", "common.h", "attn_internal.h", "api.cpp")   # api.cpp: the plan
     traffic = _traffic("decode_bf16_16k", dec_hash)
     roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
