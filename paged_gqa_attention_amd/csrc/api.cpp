@@ -291,8 +291,13 @@ attn_status plan_decode(const attn_ctx *ctx, const attn_io *io, const attn_kv *k
     // With smaller tiles (8-bit K/V, head_dim 64 at 16 bits) one workgroup
     // per CU cannot keep enough bytes in flight (e4m3fn 4 x 65,536: -20%),
     // and unequal lengths keep the finer partitions of two rounds (-4%).
+    // Fragment-addressed pools keep two as well: each page's fragment-table
+    // lookup is a dependent load that half the waves hide poorly (the
+    // headline in 256 KiB fragments: 19% over the contiguous call at one
+    // workgroup per CU, 3% at two).
     const bool big_tiles = (int64_t)kPage * D * elt_bytes(kv->dtype) >= 4096;
-    const int64_t round_eq = (!pl->mfma && big_tiles && per_cu > 1)
+    const bool fragmented = kv->k_fragments || kv->v_fragments;
+    const int64_t round_eq = (!pl->mfma && big_tiles && !fragmented && per_cu > 1)
                                  ? ceil_div((int64_t)ctx->num_cus, kv->num_kv_heads)
                                  : rph / kSkRounds;
     pl->sk_round = (int)std::min<int64_t>(round_eq, INT32_MAX);
