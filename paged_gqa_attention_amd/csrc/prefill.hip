@@ -440,13 +440,15 @@ __global__ __launch_bounds__(HPW * 256) void prefill_mfma(PrefillArgs a) {
     bool need_mask = diag;
     if constexpr (MASK) need_mask = need_mask || __builtin_amdgcn_ballot_w64(!keep) != 0;
     if (need_mask) {
-      const int lim = keep ? min(pos_row, L - 1) : -1;
+      // key kt0 + 8hh + c of this lane is visible when c <= rel: one compare
+      // with a small constant per score
+      const int rel = (keep ? min(pos_row, L - 1) : -1) - (kt0 + 8 * hh);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = kt0 + 32 * mb + 16 * (i >> 3) + 8 * hh + 4 * ((i >> 2) & 1) + (i & 3);
-          s[mb][i] = key <= lim ? s[mb][i] : kNegInf;
+          const int c = 32 * mb + 16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3);
+          s[mb][i] = c <= rel ? s[mb][i] : kNegInf;
         }
     }
 
